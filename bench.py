@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Throughput of the hot path on one MI355X: FP32 C = A x B through the C ABI's sgemm_f32.
+
+One step is one call of sgemm_f32 over the whole workload (the default is the square
+8192^3 product with A, B ~ U[-1, 1], packed row-major). Inputs are drawn on the host from
+fixed seeds, copied to HBM, and are resident before timing starts. W untimed steps, then
+exactly K timed steps between two device synchronisations, timed with HIP events recorded
+on the stream the kernels are launched on (torch's current stream).
+
+Prints one JSON line on stdout:
+  value        whole-job GFLOP/s = 2 M N K * steps / elapsed
+  roofline     the kernel's achieved TFLOP/s (algorithmic 2MNK per launch / average
+               launch time) against the MI355X FP32 matrix peak; for a workload whose
+               HBM floor is the larger one, GB/s of compulsory bytes against 8 TB/s.
+               traffic = measured HBM bytes per launch from the committed rocprofv3
+               counter summary, or null if the kernel sources changed since then.
+  cpu_baseline the CPU oracle (fp64 triple loop) timed on this host on a bounded sample
+               of rows of the same product; the same rows of the GPU result are checked
+               against it.
+Everything else goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_FP32_MFMA_TFLOPS = 157.3     # MI355X dense FP32 matrix peak
+PEAK_HBM_GBS = 8000.0             # MI355X HBM3E
+KERNEL_SOURCES = ["fp32_gemm_f32_amd/csrc/kernel_mfma.hpp", "fp32_gemm_f32_amd/csrc/plan.hpp",
+                  "fp32_gemm_f32_amd/csrc/sgemm_f32.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sources_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, if it is current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = data.get(workload)
+    if not entry or entry.get("kernel_sources_sha") != kernel_sources_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def copy_calibration(mib: int, steps: int) -> None:
+    """A plain device copy of a known size, for scaling the HBM byte counters."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4,
+                      "launches": steps}))
+
+
+def cpu_baseline(A, B, C_dev, M, N, K, seconds: float):
+    """Time the oracle on a bounded sample of rows and check the GPU's rows against it."""
+    import numpy as np
+
+    import oracle
+    lib = oracle.load()
+    rows_all = np.linspace(0, M - 1, num=min(M, 4096)).astype(np.int64)
+    C_host = C_dev.cpu().numpy()
+    # calibrate on a few rows, then size the sample to the time budget
+    probe = rows_all[:: max(1, len(rows_all) // 8)][:8]
+    t0 = time.perf_counter()
+    oracle.check(A, B, C_host, rows=probe, lib=lib)
+    t_probe = time.perf_counter() - t0
+    per_row = max(t_probe / len(probe), 1e-6)
+    n_rows = int(min(len(rows_all), max(len(probe), seconds / per_row)))
+    rows = rows_all[np.linspace(0, len(rows_all) - 1, num=n_rows).astype(np.int64)]
+    t0 = time.perf_counter()
+    rep = oracle.check(A, B, C_host, rows=rows, lib=lib)
+    t = time.perf_counter() - t0
+    flop = 2.0 * len(rows) * N * K
+    return {"value": round(flop / t / 1e9, 3), "unit": "GFLOP/s", "cores": oracle.threads(lib),
+            "kind": "oracle",
+            "sample": f"{len(rows)} of {M} rows of C (all {N} columns, K={K}), fp64 oracle, "
+                      f"OpenMP over rows, {t:.1f} s",
+            "check_max_err": rep["max_err"], "check_nonfinite": rep["n_nonfinite"]}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--variant", type=int, default=-1, help="force a hot-kernel tile variant")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run a plain device copy of this size instead (counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        log("bench.py: this build measures one GPU only; multi-GPU runs are not supported "
+            "(the product shards by output tiles, see the design notes)")
+        return 2
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib, max(args.steps, 1))
+        return 0
+
+    import torch
+
+    import fp32_gemm_f32_amd as g
+    import workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    M, N, K = w.M, w.N, w.K
+    log(f"bench: workload {w.describe()}, steps {args.steps}, warmup {args.warmup}")
+    A, B = wl.operands(args.workload)
+    dev = torch.device("cuda:0")
+    dA = torch.from_numpy(A).to(dev)
+    dB = torch.from_numpy(B).to(dev)
+    dC = torch.empty((M, N), dtype=torch.float32, device=dev)
+    plan = g.sgemm_f32_plan_describe(M, N, K, dA.data_ptr(), K, dB.data_ptr(), N,
+                                     dC.data_ptr(), N)
+    if args.variant >= 0:
+        plan["name"] = g.variant_names()[args.variant]
+    log(f"bench: plan {plan}")
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    lib = g.library()
+    call_args = (M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, dC.data_ptr(), N, sp)
+
+    def step():
+        rc = (lib.sgemm_f32(*call_args) if args.variant < 0
+              else lib.sgemm_f32_variant(args.variant, *call_args))
+        if rc != 0:
+            raise g.SgemmError(rc, "sgemm_f32")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t_wall0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t_wall0
+    elapsed_ms = start.elapsed_time(end)
+    ms = elapsed_ms / args.steps
+    flop = 2.0 * M * N * K
+    gflops = flop * args.steps / (elapsed_ms / 1e3) / 1e9
+    log(f"bench: {ms:.4f} ms/step (events), wall {wall:.3f} s, {gflops:.1f} GFLOP/s")
+
+    # roofline of the one kernel a step launches
+    compulsory = 4.0 * (M * K + K * N + M * N)
+    t_mfma = flop / (PEAK_FP32_MFMA_TFLOPS * 1e12)
+    t_hbm = compulsory / (PEAK_HBM_GBS * 1e9)
+    if t_mfma >= t_hbm:
+        achieved = flop / (ms / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_FP32_MFMA_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4)}
+    else:
+        achieved = compulsory / (ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = measured_traffic(args.workload)
+    roof["kernel"] = plan["name"]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(A, B, dC, M, N, K, args.cpu_seconds)
+        log(f"bench: cpu baseline {cpu}")
+        if cpu["check_nonfinite"] or cpu["check_max_err"] > 1e-5:
+            log("bench: PARITY FAILURE on the sampled rows")
+            return 1
+
+    out = {
+        "metric": "SGEMM GFLOP/s (2MNK/t) and % of FP32 matrix peak at 8192^3, 1 MI355X",
+        "value": round(gflops, 1), "unit": "GFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+        "config": {"workload": f"{w.label} ({w.name}): FP32 row-major C=AxB, "
+                               f"{w.dist} operands from fixed seeds",
+                   "M": M, "N": N, "K": K, "lda": K, "ldb": N, "ldc": N,
+                   "kernel": plan["name"], "tile": [plan["BM"], plan["BN"], plan["BK"]],
+                   "grid": plan["grid"], "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

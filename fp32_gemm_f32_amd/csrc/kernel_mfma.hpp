@@ -1,0 +1,363 @@
+// kernel_mfma.hpp -- the hot kernel: LDS-tiled, register-tiled FP32 GEMM on the gfx950
+// matrix cores.
+//
+// What it computes is the row-by-column product of "Shared Memory Tiling", "The naive
+// kernel". How it gets there follows the ladder of the pages, carried onto CDNA4:
+//
+//  * Block tiling ("SGEMM: Shared Memory Tiling Visualizer", code panel; "Shared Memory
+//    Tiling", "The tiled kernel"): a workgroup owns a BM x BN tile of C and walks K in
+//    panels of BK, staging a BM x BK panel of A and a BK x BN panel of B in LDS once and
+//    reusing every staged element BN (resp. BM) times. Elements past M, N or K are
+//    staged as zeros, so ragged shapes need no special cases in the inner loop.
+//  * Register tiling ("SGEMM: 2D Register Tiling Visualizer", "Why 2D Register Tiling
+//    Dominates"): each wavefront owns a WM x WN sub-tile and forms outer products of a
+//    column of A-values and a row of B-values. On gfx950 the outer product is one
+//    instruction: v_mfma_f32_32x32x2_f32 adds a 32 x 2 by 2 x 32 product into a 32 x 32
+//    FP32 accumulator block spread over 16 registers per lane. A wave holds
+//    (WM/32) x (WN/32) such blocks; per k-pair it reads WM/32 A-registers and WN/32
+//    B-registers from LDS and issues (WM/32)(WN/32) MFMAs, the hardware form of the
+//    pages' (TM + TN) reads per TM * TN multiply-adds.
+//  * Software pipelining ("Shared Memory Tiling", "What tiling does not fix"): two LDS
+//    stages; the global loads of panel p+1 are in flight while the MFMAs consume panel
+//    p, so each panel costs one barrier instead of two.
+//
+// gfx950 specifics:
+//  * Loads use buffer resources. A lane whose element lies outside the matrix gets the
+//    voffset kOob, past the resource's size, and the hardware returns zero without
+//    touching memory: that is the zero-fill of the pages' masked loads, and it also
+//    keeps the last rows of B from reading past the end of the allocation. Resources
+//    are rebased per workgroup (A) and per panel (B), keeping offsets in 31 bits.
+//  * VEC = true loads 16 bytes per lane (rows 16-byte aligned, K % 4 == 0); VEC = false
+//    loads one dword per element with a per-element mask (any alignment, any K).
+//  * MFMA operand layout (32x32x2): lane l supplies A[l % 32][l / 32] and
+//    B[l / 32][l % 32]; accumulator register v of lane l holds
+//    D[8 (v / 4) + 4 (l / 32) + v % 4][l % 32].
+//  * K permutation: lanes 0-31 read 4 consecutive k of a row of A with one ds_read_b128
+//    and lanes 32-63 the next 4, so four MFMAs consume 8 k values; the B operand of step
+//    s is read from LDS row 8 kb + s + 4 (l / 32), which pairs the same k on both sides.
+//  * Column interleave: a lane reads CI consecutive columns of a B row with one LDS load
+//    and feeds them to CI different MFMA blocks, so MFMA column c of block j is column
+//    CI c + j of the wave tile. In the epilogue each lane then owns CI consecutive
+//    columns of a row and writes them with one vector store.
+//  * LDS layout: B rows are stored as they are (each read is a contiguous row segment,
+//    conflict-free). A rows are BK words; a 16-byte chunk q of row r is stored at chunk
+//    position q ^ swz(r), which spreads the 8 (or 16) rows read by one ds_read_b128
+//    phase over distinct banks.
+//  * Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2; the
+//    tile order gives each XCD a contiguous range of tiles, walked in groups of
+//    kGroupM tile rows, so concurrently running tiles share A and B panels in L2.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <type_traits>
+
+namespace sgemm {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+template <int W> struct fvec;
+template <> struct fvec<1> { typedef float type; };
+template <> struct fvec<2> { typedef f32x2 type; };
+template <> struct fvec<4> { typedef f32x4 type; };
+
+// Word 3 of a raw buffer resource on the gfx9 family: 32-bit data format, no swizzle.
+constexpr int kBufferWord3 = 0x00020000;
+// A voffset beyond every resource size built below: loads from it return zero.
+constexpr uint32_t kOob = 0x80000000u;
+constexpr int kXcds = 8;
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+constexpr int kGroupM = 8;
+
+struct GemmArgs {
+    const float *A;
+    const float *B;
+    float *C;
+    int64_t a_bytes;   // bytes from A to the end of its last row
+    int64_t b_bytes;   // bytes from B to the end of its last row
+    int M, N, K, lda, ldb, ldc;
+    int tiles_m, tiles_n;
+    int store_vec;     // C rows and base allow 16-byte stores
+};
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const float *base, int64_t bytes)
+{
+    int32_t n = 0;
+    if (bytes > 0) n = bytes >= int64_t(kOob) ? int32_t(kOob - 64) : int32_t(bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0, n,
+                                             kBufferWord3);
+}
+
+__device__ inline f32x4 load_b128(__amdgpu_buffer_rsrc_t r, uint32_t voff)
+{
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
+__device__ inline float load_b32(__amdgpu_buffer_rsrc_t r, uint32_t voff)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
+}
+
+// Calls f(std::integral_constant<int, I>) for I = BEGIN .. END-1, so I is a constant
+// expression inside f (needed by the scheduling builtins).
+template <int BEGIN, int END, typename F>
+__device__ inline void static_for(F &&f)
+{
+    if constexpr (BEGIN < END) {
+        f(std::integral_constant<int, BEGIN>{});
+        static_for<BEGIN + 1, END>(f);
+    }
+}
+
+// Physical 16-byte chunk slot of logical chunk q in A-tile row r (CPR chunks per row).
+template <int CPR>
+__host__ __device__ constexpr int a_swizzle(int r)
+{
+    static_assert(CPR == 8 || CPR == 4 || CPR == 2, "A row must hold 2, 4 or 8 chunks");
+    return CPR == 8 ? ((r & 7) ^ ((r >> 3) & 1))
+         : CPR == 4 ? (((r >> 1) ^ (r >> 3)) & 3)
+                    : (((r >> 2) ^ (r >> 3)) & 1);
+}
+
+// Tile coordinates of workgroup bid: a contiguous range of tiles per XCD, then groups of
+// kGroupM tile rows walked column by column.
+__device__ inline void tile_coords(int bid, int tiles_m, int tiles_n, int &tm, int &tn)
+{
+    const int total = tiles_m * tiles_n;
+    const int q = total / kXcds, r = total % kXcds;
+    const int x = bid % kXcds, l = bid / kXcds;
+    const int t = x < r ? x * (q + 1) + l : r * (q + 1) + (x - r) * q + l;
+    const int per_group = kGroupM * tiles_n;
+    const int g = t / per_group;
+    const int first = g * kGroupM;
+    const int rows = min(tiles_m - first, kGroupM);
+    const int w = t - g * per_group;
+    tm = first + w % rows;
+    tn = w / rows;
+}
+
+template <int BM, int BN, int BK, int WGM, int WGN, bool VEC>
+struct MfmaTile {
+    static constexpr int kThreads = 64 * WGM * WGN;
+    static constexpr int WM = BM / WGM;          // wave tile rows
+    static constexpr int WN = BN / WGN;          // wave tile columns
+    static constexpr int RB = WM / 32;           // 32-row MFMA blocks per wave
+    static constexpr int CI = WN >= 128 ? 4 : WN / 32;   // column interleave
+    static constexpr int CG = WN / (32 * CI);    // interleaved column groups
+    static constexpr int CPR = BK / 4;           // 16-byte chunks per A-tile row
+    static constexpr int A_CH = BM * BK / 4 / kThreads;  // A chunks per thread per panel
+    static constexpr int B_CH = BK * BN / 4 / kThreads;  // B chunks per thread per panel
+    static constexpr int A_TILE = BM * BK;       // floats per A stage
+    static constexpr int B_TILE = BK * BN;       // floats per B stage
+    static constexpr int STAGE = A_TILE + B_TILE;
+    static constexpr int LDS_BYTES = 2 * STAGE * 4;
+    static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile is made of 32 x 32 blocks");
+    static_assert(WN % (32 * CI) == 0, "column groups");
+    static_assert(BK % 8 == 0, "four MFMA k-steps consume 8 k values");
+    static_assert((BM * BK / 4) % kThreads == 0 && (BK * BN / 4) % kThreads == 0,
+                  "panel chunks divide evenly over the workgroup");
+    static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS holds 160 KiB per workgroup");
+};
+
+template <int BM, int BN, int BK, int WGM, int WGN, bool VEC>
+__global__ __launch_bounds__(64 * WGM * WGN) void k_sgemm_mfma(GemmArgs p)
+{
+    using T = MfmaTile<BM, BN, BK, WGM, WGN, VEC>;
+    constexpr int NT = T::kThreads, WM = T::WM, WN = T::WN, RB = T::RB, CI = T::CI,
+                  CG = T::CG, CPR = T::CPR, A_CH = T::A_CH, B_CH = T::B_CH;
+    typedef typename fvec<CI>::type bvec;
+
+    __shared__ __attribute__((aligned(16))) float smem[2 * T::STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int lo = lane & 31, hi = lane >> 5;
+    const int wave = tid >> 6;
+    const int wm = wave / WGN, wn = wave % WGN;
+
+    int tm, tn;
+    tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
+
+    // ---- per-thread load assignment (fixed for the whole K loop) ----
+    // A chunk c = tid + i*NT covers row c / CPR, k columns 4 (c % CPR) .. +3 of a panel.
+    uint32_t a_off[A_CH];
+    int a_k[A_CH];
+    int a_lds[A_CH];
+    bool a_ok[A_CH];
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+        const int c = tid + i * NT;
+        const int r = c / CPR, q = c % CPR;
+        a_off[i] = uint32_t(r) * uint32_t(lda) * 4u + uint32_t(q) * 16u;
+        a_k[i] = 4 * q;
+        a_lds[i] = r * BK + 4 * (q ^ a_swizzle<CPR>(r));
+        a_ok[i] = m0 + r < M;
+    }
+    // B chunk c = tid + i*NT covers panel row c / (BN/4), columns 4 (c % (BN/4)) .. +3.
+    uint32_t b_off[B_CH];
+    int b_k[B_CH];
+    int b_n[B_CH];
+    int b_lds[B_CH];
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+        const int c = tid + i * NT;
+        const int kk = c / (BN / 4), cc = c % (BN / 4);
+        b_off[i] = uint32_t(kk) * uint32_t(ldb) * 4u + uint32_t(cc) * 16u;
+        b_k[i] = kk;
+        b_n[i] = n0 + 4 * cc;
+        b_lds[i] = kk * BN + 4 * cc;
+    }
+
+    f32x4 ra[A_CH], rb[B_CH];
+
+    auto load_panel = [&](int k0) {
+        const __amdgpu_buffer_rsrc_t rsa =
+            make_rsrc(p.A + (int64_t(m0) * lda + k0), p.a_bytes - (int64_t(m0) * lda + k0) * 4);
+        const __amdgpu_buffer_rsrc_t rsb =
+            make_rsrc(p.B + (int64_t(k0) * ldb + n0), p.b_bytes - (int64_t(k0) * ldb + n0) * 4);
+#pragma unroll
+        for (int i = 0; i < A_CH; ++i) {
+            const int kc = k0 + a_k[i];
+            if constexpr (VEC) {
+                ra[i] = load_b128(rsa, (a_ok[i] && kc < K) ? a_off[i] : kOob);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    ra[i][e] = load_b32(rsa, (a_ok[i] && kc + e < K) ? a_off[i] + 4u * e : kOob);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < B_CH; ++i) {
+            const bool kok = k0 + b_k[i] < K;
+            if constexpr (VEC) {
+                rb[i] = load_b128(rsb, (kok && b_n[i] < N) ? b_off[i] : kOob);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    rb[i][e] = load_b32(rsb, (kok && b_n[i] + e < N) ? b_off[i] + 4u * e : kOob);
+            }
+        }
+    };
+
+    auto store_panel = [&](int stage) {
+        float *As = smem + stage * T::STAGE;
+        float *Bs = As + T::A_TILE;
+#pragma unroll
+        for (int i = 0; i < A_CH; ++i) *reinterpret_cast<f32x4 *>(As + a_lds[i]) = ra[i];
+#pragma unroll
+        for (int i = 0; i < B_CH; ++i) *reinterpret_cast<f32x4 *>(Bs + b_lds[i]) = rb[i];
+    };
+
+    f32x16 acc[RB][CI * CG];
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int j = 0; j < CI * CG; ++j) acc[i][j] = f32x16{};
+
+    // A-operand LDS rows of this lane: row wm*WM + rb*32 + lo, whose swizzle depends on
+    // lo only (wm*WM + rb*32 is a multiple of 32).
+    const int a_sw = a_swizzle<CPR>(lo);
+    const int a_row0 = (wm * WM + lo) * BK;
+    const int b_col0 = wn * WN + CI * lo;
+
+    // One panel: BK/2 MFMA k-steps. Operands of step t+1 (and the A registers of the
+    // next group of 8 k) are read from LDS before the MFMAs of step t are issued, so the
+    // LDS latency is hidden behind matrix-core work instead of stalling the wave.
+    auto read_a = [&](const float *As, int kb, f32x4 (&a)[RB]) {
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+            a[r] = *reinterpret_cast<const f32x4 *>(As + a_row0 + r * 32 * BK +
+                                                    4 * ((2 * kb + hi) ^ a_sw));
+    };
+    auto read_b = [&](const float *Bs, int t, bvec (&b)[CG]) {
+        const float *brow = Bs + (8 * (t >> 2) + (t & 3) + 4 * hi) * BN + b_col0;
+#pragma unroll
+        for (int g = 0; g < CG; ++g) b[g] = *reinterpret_cast<const bvec *>(brow + g * 32 * CI);
+    };
+    auto compute = [&](int stage) {
+        constexpr int STEPS = BK / 2;
+        const float *As = smem + stage * T::STAGE;
+        const float *Bs = As + T::A_TILE;
+        f32x4 a[2][RB];
+        bvec b[2][CG];
+        read_a(As, 0, a[0]);
+        read_b(Bs, 0, b[0]);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, RB + CG, 0);
+        static_for<0, STEPS>([&](auto tc) {
+            constexpr int t = decltype(tc)::value;
+            constexpr int kb = t >> 2, s = t & 3;
+            constexpr bool next_b = t + 1 < STEPS;
+            constexpr bool next_a = s == 0 && kb + 1 < BK / 8;
+            if constexpr (next_b) read_b(Bs, t + 1, b[(t + 1) & 1]);
+            if constexpr (next_a) read_a(As, kb + 1, a[(kb + 1) & 1]);
+            // the scheduler would otherwise sink these reads next to their first use
+            if constexpr (next_b || next_a)
+                __builtin_amdgcn_sched_group_barrier(
+                    kSchedDsRead, (next_b ? CG : 0) + (next_a ? RB : 0), 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, RB * CG * CI, 0);
+#pragma unroll
+            for (int r = 0; r < RB; ++r)
+#pragma unroll
+                for (int g = 0; g < CG; ++g)
+#pragma unroll
+                    for (int j = 0; j < CI; ++j) {
+                        float bj;
+                        if constexpr (CI == 1) bj = b[t & 1][g]; else bj = b[t & 1][g][j];
+                        acc[r][g * CI + j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                            a[kb & 1][r][s], bj, acc[r][g * CI + j], 0, 0, 0);
+                    }
+        });
+    };
+
+    // ---- K loop: two LDS stages, loads of panel p+1 in flight during panel p ----
+    const int panels = (K + BK - 1) / BK;
+    load_panel(0);
+    store_panel(0);
+    __syncthreads();
+    for (int pnl = 0; pnl < panels; ++pnl) {
+        const int cur = pnl & 1;
+        const bool more = pnl + 1 < panels;
+        if (more) load_panel((pnl + 1) * BK);
+        compute(cur);
+        if (more) store_panel(cur ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: accumulators to C, masked at the M and N edges ----
+    const int ldc = p.ldc;
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int row = m0 + wm * WM + r * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
+            if (row >= M) continue;
+            float *crow = p.C + int64_t(row) * ldc;
+#pragma unroll
+            for (int g = 0; g < CG; ++g) {
+                const int col = n0 + wn * WN + g * 32 * CI + CI * lo;
+                if (CI > 1 && p.store_vec && col + CI <= N) {
+                    bvec out;
+#pragma unroll
+                    for (int j = 0; j < CI; ++j) {
+                        if constexpr (CI == 1) out = acc[r][g * CI + j][v];
+                        else out[j] = acc[r][g * CI + j][v];
+                    }
+                    *reinterpret_cast<bvec *>(crow + col) = out;
+                } else {
+#pragma unroll
+                    for (int j = 0; j < CI; ++j)
+                        if (col + j < N) crow[col + j] = acc[r][g * CI + j][v];
+                }
+            }
+        }
+    }
+}
+
+}  // namespace sgemm

@@ -1,0 +1,253 @@
+// sgemm_f32.hip -- the C ABI declared in include/sgemm_f32.h.
+//
+// Every entry point validates its arguments first (pure host code, sgemm_validate.hpp),
+// then takes the quick returns, then launches on the caller's stream. Launches go through
+// hipLaunchKernel so the runtime's own status is returned, not a stale error left by
+// earlier calls on the thread.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "sgemm_f32.h"
+#include "sgemm_validate.hpp"
+#include "kernels_simple.hpp"
+#include "kernel_mfma.hpp"
+#include "plan.hpp"
+
+namespace sgemm {
+namespace {
+
+constexpr int kAbiVersion = 1;
+// Hardware grid dimensions above 65535 workgroups in y are avoided; the simple kernels
+// stride their rows over the grid instead.
+constexpr unsigned kMaxGridY = 65535;
+
+template <typename... KArgs, typename... Args>
+int launch(void (*kern)(KArgs...), dim3 grid, dim3 block, void *stream, Args... args)
+{
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count");
+    void *argv[] = {static_cast<void *>(&args)...};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(kern), grid, block,
+                                         argv, 0, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SGEMM_OK : SGEMM_ELAUNCH;
+}
+
+int fill_zero(int M, int N, float *C, int ldc, void *stream)
+{
+    const int64_t total = int64_t(M) * N;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    return launch(k_fill_zero, dim3(unsigned(blocks)), dim3(256), stream, M, N, C, ldc);
+}
+
+// ------------------------------------------------------------------ variants ----------
+
+typedef void (*MfmaKernel)(GemmArgs);
+
+struct VariantEntry {
+    Variant v;
+    MfmaKernel kern;
+    int threads;
+};
+
+template <int BM, int BN, int BK, int WGM, int WGN, bool VEC>
+constexpr VariantEntry entry(const char *name, int wg_per_cu, double rate)
+{
+    return VariantEntry{Variant{name, BM, BN, BK, WGM, WGN, VEC, wg_per_cu, rate},
+                        &k_sgemm_mfma<BM, BN, BK, WGM, WGN, VEC>, 64 * WGM * WGN};
+}
+
+const VariantEntry kVariants[] = {
+    entry<256, 256, 32, 2, 2, true>("mfma_256x256x32_w2x2_vec", 1, 1.00),
+    entry<256, 256, 32, 2, 2, false>("mfma_256x256x32_w2x2_dw", 1, 1.00),
+    entry<128, 128, 32, 2, 2, true>("mfma_128x128x32_w2x2_vec", 2, 0.95),
+    entry<128, 128, 32, 2, 2, false>("mfma_128x128x32_w2x2_dw", 2, 0.95),
+    entry<64, 64, 32, 2, 2, true>("mfma_64x64x32_w2x2_vec", 4, 0.80),
+    entry<64, 64, 32, 2, 2, false>("mfma_64x64x32_w2x2_dw", 4, 0.80),
+};
+constexpr int kNumVariants = int(sizeof(kVariants) / sizeof(kVariants[0]));
+
+Variant g_table[kNumVariants];
+struct TableInit {
+    TableInit() { for (int i = 0; i < kNumVariants; ++i) g_table[i] = kVariants[i].v; }
+} g_table_init;
+
+Operands make_operands(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
+                       const float *C, int ldc)
+{
+    Operands o;
+    o.M = M; o.N = N; o.K = K; o.lda = lda; o.ldb = ldb; o.ldc = ldc;
+    o.a16 = (reinterpret_cast<uintptr_t>(A) & 15u) == 0;
+    o.b16 = (reinterpret_cast<uintptr_t>(B) & 15u) == 0;
+    o.c16 = (reinterpret_cast<uintptr_t>(C) & 15u) == 0;
+    return o;
+}
+
+std::atomic<int> g_cus[64];
+
+int device_cus(int *out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SGEMM_ELAUNCH;
+    if (dev >= 0 && dev < 64) {
+        const int c = g_cus[dev].load(std::memory_order_relaxed);
+        if (c > 0) { *out = c; return SGEMM_OK; }
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+        return SGEMM_ELAUNCH;
+    if (dev >= 0 && dev < 64) g_cus[dev].store(n, std::memory_order_relaxed);
+    *out = n;
+    return SGEMM_OK;
+}
+
+int run_variant(int vi, const Operands &o, const float *A, const float *B, float *C,
+                void *stream)
+{
+    const VariantEntry &e = kVariants[vi];
+    GemmArgs p;
+    p.A = A; p.B = B; p.C = C;
+    p.a_bytes = span_elems(o.M, o.K, o.lda) * 4;
+    p.b_bytes = span_elems(o.K, o.N, o.ldb) * 4;
+    p.M = o.M; p.N = o.N; p.K = o.K; p.lda = o.lda; p.ldb = o.ldb; p.ldc = o.ldc;
+    p.tiles_m = (o.M + e.v.BM - 1) / e.v.BM;
+    p.tiles_n = (o.N + e.v.BN - 1) / e.v.BN;
+    p.store_vec = c_vec_ok(o) ? 1 : 0;
+    const int64_t tiles = int64_t(p.tiles_m) * p.tiles_n;
+    if (tiles > INT32_MAX) return SGEMM_ETOO_LARGE;
+    return launch(e.kern, dim3(unsigned(tiles)), dim3(e.threads), stream, p);
+}
+
+int run_hot(int variant, int M, int N, int K, const float *A, int lda, const float *B, int ldb,
+            float *C, int ldc, void *stream)
+{
+    const int st = validate(M, N, K, A, lda, B, ldb, C, ldc);
+    if (st != SGEMM_OK) return st;
+    if (variant >= kNumVariants) return SGEMM_EINVAL_ARG;
+    if (M == 0 || N == 0) return SGEMM_OK;
+    if (K == 0) return fill_zero(M, N, C, ldc, stream);
+    const Operands o = make_operands(M, N, K, A, lda, B, ldb, C, ldc);
+    if (variant >= 0) {
+        if (kVariants[variant].v.vec && !vec_ok(o)) return SGEMM_EINVAL_ARG;
+        if (!offsets_fit(kVariants[variant].v, o)) return SGEMM_ETOO_LARGE;
+        return run_variant(variant, o, A, B, C, stream);
+    }
+    int cus = 0;
+    const int qs = device_cus(&cus);
+    if (qs != SGEMM_OK) return qs;
+    const int vi = choose_variant(g_table, o, cus);
+    if (vi < 0) return SGEMM_ETOO_LARGE;
+    return run_variant(vi, o, A, B, C, stream);
+}
+
+}  // namespace
+}  // namespace sgemm
+
+using namespace sgemm;
+
+extern "C" int sgemm_f32(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
+                         float *C, int ldc, void *stream)
+{
+    return run_hot(-1, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+extern "C" int sgemm_f32_variant(int variant, int M, int N, int K, const float *A, int lda,
+                                 const float *B, int ldb, float *C, int ldc, void *stream)
+{
+    return run_hot(variant < 0 ? -1 : variant, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+extern "C" int sgemm_f32_naive(int M, int N, int K, const float *A, int lda, const float *B,
+                               int ldb, float *C, int ldc, void *stream)
+{
+    const int st = validate(M, N, K, A, lda, B, ldb, C, ldc);
+    if (st != SGEMM_OK) return st;
+    if (M == 0 || N == 0) return SGEMM_OK;
+    if (K == 0) return fill_zero(M, N, C, ldc, stream);
+    const dim3 block(16, 16);
+    const int64_t gy = (int64_t(M) + 15) / 16;
+    const dim3 grid(unsigned((N + 15) / 16), unsigned(gy < kMaxGridY ? gy : kMaxGridY));
+    return launch(k_sgemm_naive, grid, block, stream, M, N, K, A, lda, B, ldb, C, ldc);
+}
+
+extern "C" int sgemm_f32_tiled(int M, int N, int K, const float *A, int lda, const float *B,
+                               int ldb, float *C, int ldc, int tile, int pad, void *stream)
+{
+    const int st = validate(M, N, K, A, lda, B, ldb, C, ldc);
+    if (st != SGEMM_OK) return st;
+    if ((tile != 16 && tile != 32) || (pad != 0 && pad != 1)) return SGEMM_EINVAL_ARG;
+    if (M == 0 || N == 0) return SGEMM_OK;
+    if (K == 0) return fill_zero(M, N, C, ldc, stream);
+    const int64_t gy = (int64_t(M) + tile - 1) / tile;
+    const dim3 grid(unsigned((N + tile - 1) / tile), unsigned(gy < kMaxGridY ? gy : kMaxGridY));
+    const dim3 block(tile, tile);
+    if (tile == 16)
+        return pad ? launch(k_sgemm_lds_tiled<16, 1>, grid, block, stream, M, N, K, A, lda, B,
+                            ldb, C, ldc)
+                   : launch(k_sgemm_lds_tiled<16, 0>, grid, block, stream, M, N, K, A, lda, B,
+                            ldb, C, ldc);
+    return pad ? launch(k_sgemm_lds_tiled<32, 1>, grid, block, stream, M, N, K, A, lda, B, ldb,
+                        C, ldc)
+               : launch(k_sgemm_lds_tiled<32, 0>, grid, block, stream, M, N, K, A, lda, B, ldb,
+                        C, ldc);
+}
+
+extern "C" int sgemm_f32_variant_count(void) { return kNumVariants; }
+
+extern "C" const char *sgemm_f32_variant_name(int variant)
+{
+    return (variant >= 0 && variant < kNumVariants) ? kVariants[variant].v.name : nullptr;
+}
+
+extern "C" const char *sgemm_f32_status_string(int status)
+{
+    switch (status) {
+    case SGEMM_OK: return "ok";
+    case SGEMM_EINVAL_DIM: return "invalid dimension (M, N or K is negative)";
+    case SGEMM_EINVAL_LD: return "invalid leading dimension (lda < K, ldb < N or ldc < N)";
+    case SGEMM_EINVAL_PTR: return "invalid pointer (NULL or not 4-byte aligned)";
+    case SGEMM_EALIAS: return "C overlaps A or B";
+    case SGEMM_ELAUNCH: return "HIP runtime error (launch or device query)";
+    case SGEMM_EINVAL_ARG: return "invalid option argument";
+    case SGEMM_ETOO_LARGE: return "shape too large for the selected kernel";
+    default: return "unknown status";
+    }
+}
+
+extern "C" int sgemm_f32_plan_describe(int M, int N, int K, const float *A, int lda,
+                                       const float *B, int ldb, const float *C, int ldc,
+                                       int num_cus, char *buf, int buflen)
+{
+    if (!buf || buflen <= 0) return SGEMM_EINVAL_ARG;
+    const Operands o = make_operands(M, N, K, A, lda, B, ldb, C, ldc);
+    if (M < 0 || N < 0 || K < 0) return SGEMM_EINVAL_DIM;
+    int cus = num_cus;
+    if (cus <= 0) {
+        const int qs = device_cus(&cus);
+        if (qs != SGEMM_OK) return qs;
+    }
+    const int vi = choose_variant(g_table, o, cus);
+    if (vi < 0) return SGEMM_ETOO_LARGE;
+    const Variant &v = kVariants[vi].v;
+    const int64_t tm = (int64_t(M) + v.BM - 1) / v.BM, tn = (int64_t(N) + v.BN - 1) / v.BN;
+    // operand bytes the tiles request: every A row panel once per tile column and every
+    // B column panel once per tile row (before any cache reuse)
+    const int64_t tile_bytes = 4 * (int64_t(M) * K * tn + int64_t(K) * N * tm);
+    const int n = snprintf(buf, size_t(buflen),
+                           "{\"variant\": %d, \"name\": \"%s\", \"BM\": %d, \"BN\": %d, "
+                           "\"BK\": %d, \"waves\": [%d, %d], \"threads\": %d, \"grid\": %lld, "
+                           "\"tiles\": [%lld, %lld], \"load\": \"%s\", \"store\": \"%s\", "
+                           "\"cus\": %d, \"tile_request_bytes\": %lld}",
+                           vi, v.name, v.BM, v.BN, v.BK, v.wgm, v.wgn, kVariants[vi].threads,
+                           (long long)(tm * tn), (long long)tm, (long long)tn,
+                           v.vec ? "b128" : "b32", c_vec_ok(o) ? "vector" : "scalar", cus,
+                           (long long)tile_bytes);
+    if (n < 0 || n >= buflen) return SGEMM_EINVAL_ARG;
+    return vi;
+}
+
+extern "C" int sgemm_f32_abi_version(void) { return kAbiVersion; }

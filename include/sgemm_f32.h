@@ -1,0 +1,130 @@
+/*
+ * sgemm_f32.h -- C ABI of the MI355X (gfx950) FP32 matrix multiply C = A x B.
+ *
+ * Operation (every entry point that computes):
+ *     C[i*ldc + j] = sum_{k<K} A[i*lda + k] * B[k*ldb + j]      for 0 <= i < M, 0 <= j < N
+ * The product is the one every page builds on: each output is the dot product of a row of
+ * A with a column of B ("SGEMM: Shared Memory Tiling Visualizer", "Why Tiling Works (The
+ * Math)"; "Shared Memory Tiling", "The naive kernel"). A is M x K, B is K x N, C is M x N,
+ * all row-major FP32; the pages use packed rows (lda = K, ldb = N, ldc = N) and this ABI
+ * adds leading dimensions (in elements) so the operands may be sub-matrices. C is
+ * overwritten, never accumulated into (alpha = 1, beta = 0), as in every kernel the pages
+ * print. Arithmetic is FP32 with FP32 accumulation; the order of the K-sum is not fixed.
+ *
+ * Ownership: A, B and C are device pointers owned by the caller. The library keeps no
+ * mutable state between calls apart from a per-device cache of the compute-unit count,
+ * and is safe to call from several host threads.
+ *
+ * Errors: every argument is validated before any HIP runtime call, so the validation
+ * paths work (and are tested) on a host without a GPU. A negative return value is an
+ * sgemm_status; the library never aborts. Launches are asynchronous on `stream` (a
+ * hipStream_t; NULL is the default stream); a launch failure is reported as
+ * SGEMM_ELAUNCH, and faults during execution surface at the caller's next synchronisation.
+ *
+ * Validation rules (checked in this order):
+ *   M, N, K >= 0                                   else SGEMM_EINVAL_DIM
+ *   lda >= max(1,K), ldb >= max(1,N), ldc >= max(1,N)   else SGEMM_EINVAL_LD
+ *   a pointer whose region is non-empty is non-NULL and 4-byte aligned   else SGEMM_EINVAL_PTR
+ *   C's region does not overlap A's or B's region  else SGEMM_EALIAS
+ * Regions: A spans (M-1)*lda + K elements from A (empty if M or K is 0); B spans
+ * (K-1)*ldb + N (empty if K or N is 0); C spans (M-1)*ldc + N (empty if M or N is 0).
+ * Quick returns: M == 0 or N == 0 launches nothing; K == 0 sets C's M x N region to 0
+ * (the empty sum) with one small kernel.
+ */
+#ifndef SGEMM_F32_H
+#define SGEMM_F32_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SGEMM_OK = 0,
+    SGEMM_EINVAL_DIM = -1,   /* a dimension is negative                                  */
+    SGEMM_EINVAL_LD = -2,    /* a leading dimension is smaller than its row length       */
+    SGEMM_EINVAL_PTR = -3,   /* a needed pointer is NULL or not 4-byte aligned           */
+    SGEMM_EALIAS = -4,       /* C overlaps A or B                                        */
+    SGEMM_ELAUNCH = -5,      /* the HIP runtime refused a launch or device query         */
+    SGEMM_EINVAL_ARG = -6,   /* an option argument (tile, pad, variant, buffer) is invalid */
+    SGEMM_ETOO_LARGE = -7    /* the shape exceeds what the chosen kernel can address     */
+} sgemm_status;
+
+/*
+ * The hot path: the LDS-tiled, register-tiled matrix-core kernel ("SGEMM: 2D Register
+ * Tiling Visualizer", "Why 2D Register Tiling Dominates", carried onto the FP32 MFMA
+ * instructions), with tiles zero-filled past the edges of ragged shapes. The tile shape
+ * is chosen per (M, N, K), pointer alignment and compute-unit count.
+ */
+int sgemm_f32(int M, int N, int K,
+              const float *A, int lda,
+              const float *B, int ldb,
+              float *C, int ldc,
+              void *stream);
+
+/*
+ * The reference kernel: one thread per element of C, a length-K dot product read
+ * straight from global memory ("Shared Memory Tiling", "The naive kernel"), with bounds
+ * checks so any shape works. Slow on purpose; the pages' 2*M*N*K read count applies.
+ */
+int sgemm_f32_naive(int M, int N, int K,
+                    const float *A, int lda,
+                    const float *B, int ldb,
+                    float *C, int ldc,
+                    void *stream);
+
+/*
+ * The scalar shared-memory tiled kernel ("SGEMM: Shared Memory Tiling Visualizer", code
+ * panel; "Shared Memory Tiling", "The tiled kernel"): TILE x TILE threads per block, one
+ * output each, tiles of A and B staged in LDS and zero-filled at the edges, ceil(K/TILE)
+ * steps. tile is 16 or 32; pad is 0 (unpadded rows) or 1 (rows of TILE + 1 words, the
+ * padded layout of "Shared Memory Tiling", "Conflict-free layout"). Anything else is
+ * SGEMM_EINVAL_ARG. Kept as a measurable rung between the naive and the hot kernel.
+ */
+int sgemm_f32_tiled(int M, int N, int K,
+                    const float *A, int lda,
+                    const float *B, int ldb,
+                    float *C, int ldc,
+                    int tile, int pad,
+                    void *stream);
+
+/*
+ * The hot kernel with a fixed tile variant instead of the automatic choice (for tests
+ * and tuning). variant < 0 is the automatic choice (same as sgemm_f32); otherwise an
+ * index below sgemm_f32_variant_count(). A variant whose load path needs 16-byte
+ * aligned rows returns SGEMM_EINVAL_ARG when the operands do not allow it.
+ */
+int sgemm_f32_variant(int variant, int M, int N, int K,
+                      const float *A, int lda,
+                      const float *B, int ldb,
+                      float *C, int ldc,
+                      void *stream);
+
+/* Number of hot-kernel tile variants, and the name of one (NULL when out of range). */
+int sgemm_f32_variant_count(void);
+const char *sgemm_f32_variant_name(int variant);
+
+/* A static, NUL-terminated description of a status code. */
+const char *sgemm_f32_status_string(int status);
+
+/*
+ * Writes a one-line JSON description of the plan sgemm_f32 would run for these
+ * arguments into buf (at most buflen bytes including the NUL): variant, tile shape,
+ * grid, load path and the operand bytes the tiles request. Pointers are used for their
+ * alignment only and are never dereferenced. num_cus > 0 plans for that many compute
+ * units; num_cus <= 0 queries the current device (SGEMM_ELAUNCH if none). Returns the
+ * variant index (>= 0), or a negative sgemm_status (buffer too small: SGEMM_EINVAL_ARG).
+ */
+int sgemm_f32_plan_describe(int M, int N, int K,
+                            const float *A, int lda,
+                            const float *B, int ldb,
+                            const float *C, int ldc,
+                            int num_cus, char *buf, int buflen);
+
+/* Version of this ABI (incremented on any incompatible change). */
+int sgemm_f32_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGEMM_F32_H */

@@ -52,6 +52,8 @@ def _bind(lib):
     lib.oracle_check.restype = ctypes.c_int
     lib.oracle_sample.argtypes = [i64, i64, i64, dp, i64, dp, i64, i64, dp, dp, dp, dp]
     lib.oracle_sample.restype = ctypes.c_int
+    lib.oracle_threads.argtypes = []
+    lib.oracle_threads.restype = ctypes.c_int
     return lib
 
 
@@ -130,3 +132,8 @@ def sample(A: np.ndarray, B: np.ndarray, ii, jj, lib=None):
     if rc:
         raise RuntimeError(f"oracle_sample failed ({rc})")
     return ref, den
+
+
+def threads(lib=None) -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return (lib or load()).oracle_threads()

@@ -29,6 +29,9 @@
  * for any thread count. Build: gcc -O2 -ffp-contract=off -fopenmp (no -ffast-math).
  */
 #include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -187,4 +190,14 @@ int oracle_sample(int64_t M, int64_t N, int64_t K,
         den[t] = d;
     }
     return 0;
+}
+
+/* Threads an OpenMP region of the oracle uses (1 when built without OpenMP). */
+int oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }

@@ -1,0 +1,114 @@
+"""The C ABI on a host without a GPU: the library loads, exports every symbol the header
+declares, and rejects bad arguments before touching the HIP runtime."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp32_gemm_f32_amd as g
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sgemm_f32.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sgemm_f32\w*)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert "sgemm_f32" in names and "sgemm_f32_naive" in names and len(names) >= 8
+    lib = ctypes.CDLL(g.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in sgemm_f32.h but not exported"
+
+
+def test_abi_version_and_status_strings():
+    assert g.abi_version() == 1
+    lib = g.library()
+    for code in range(-7, 1):
+        s = lib.sgemm_f32_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.sgemm_f32_status_string(-99).decode() == "unknown status"
+
+
+def test_variant_table():
+    names = g.variant_names()
+    assert len(names) == g.library().sgemm_f32_variant_count() >= 2
+    assert g.library().sgemm_f32_variant_name(len(names)) is None
+    assert g.library().sgemm_f32_variant_name(-1) is None
+
+
+P = 1 << 20   # a fake, 16-byte aligned "device" address: never dereferenced on these paths
+
+
+def call(fn, *args):
+    return getattr(g.library(), fn)(*args)
+
+
+@pytest.mark.parametrize("fn", ["sgemm_f32", "sgemm_f32_naive"])
+def test_validation_codes(fn):
+    ok = (4, 4, 4, P, 4, P + 4096, 4, P + 8192, 4, None)
+    def with_(**kw):
+        a = list(ok)
+        for k, v in kw.items():
+            a["M N K A lda B ldb C ldc".split().index(k)] = v
+        return call(fn, *a)
+    assert with_(M=-1) == -1 and with_(N=-3) == -1 and with_(K=-2) == -1
+    assert with_(lda=3) == -2 and with_(ldb=3) == -2 and with_(ldc=3) == -2
+    assert with_(lda=0, K=0) == -2            # ld >= max(1, K)
+    assert with_(A=None) == -3 and with_(B=None) == -3 and with_(C=None) == -3
+    assert with_(A=P + 2) == -3               # not 4-byte aligned
+    assert with_(C=P + 4) == -4               # C overlaps A
+    assert with_(C=P + 4096 + 60) == -4       # C overlaps the tail of B
+    # M == 0 or N == 0: nothing to do, no launch, no pointer needed for empty regions
+    assert with_(M=0, A=None, C=None) == 0
+    assert with_(N=0, B=None, C=None) == 0
+
+
+def test_tiled_option_validation():
+    args = (4, 4, 4, P, 4, P + 4096, 4, P + 8192, 4)
+    assert call("sgemm_f32_tiled", *args, 8, 0, None) == -6
+    assert call("sgemm_f32_tiled", *args, 16, 2, None) == -6
+    assert call("sgemm_f32_tiled", 0, 4, 4, P, 4, P + 4096, 4, P + 8192, 4, 32, 1, None) == 0
+
+
+def test_variant_option_validation():
+    n = g.library().sgemm_f32_variant_count()
+    args = (8, 8, 8, P, 8, P + 4096, 8, P + 8192, 8, None)
+    assert call("sgemm_f32_variant", n, *args) == -6
+    # a 16-byte-load variant refuses rows that are not 16-byte aligned (before any launch)
+    vec = [i for i, s in enumerate(g.variant_names()) if s.endswith("_vec")][0]
+    assert call("sgemm_f32_variant", vec, 8, 8, 7, P, 7, P + 4096, 8, P + 8192, 8, None) == -6
+    assert call("sgemm_f32_variant", vec, 8, 8, 8, P + 4, 8, P + 4096, 8, P + 8192, 8, None) == -6
+
+
+@pytest.mark.parametrize("shape,expect_tile,load", [
+    ((8192, 8192, 8192), 256, "b128"),
+    ((16384, 16384, 64), 256, "b128"),
+    ((1024, 1024, 1024), None, "b128"),
+    ((1023, 1025, 1027), None, "b32"),
+    ((6, 6, 9), None, "b32"),
+])
+def test_plan(shape, expect_tile, load):
+    M, N, K = shape
+    plan = g.sgemm_f32_plan_describe(M, N, K, P, None, P + (1 << 30), None, P + (1 << 31), None,
+                                     num_cus=256)
+    assert plan["load"] == load
+    assert plan["grid"] == plan["tiles"][0] * plan["tiles"][1]
+    assert plan["tiles"][0] * plan["BM"] >= M and plan["tiles"][1] * plan["BN"] >= N
+    if expect_tile:
+        assert plan["BM"] == plan["BN"] == expect_tile
+    elif M * N >= 1 << 20:
+        assert plan["grid"] >= 64   # 1024-class shapes still spread over the chip
+    # the request-bytes model: each A panel once per tile column, each B panel per tile row
+    tm, tn = plan["tiles"]
+    assert plan["tile_request_bytes"] == 4 * (M * K * tn + K * N * tm)
+
+
+def test_plan_buffer_too_small():
+    buf = ctypes.create_string_buffer(8)
+    assert g.library().sgemm_f32_plan_describe(64, 64, 64, P, 64, P, 64, P, 64, 256, buf, 8) == -6

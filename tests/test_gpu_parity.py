@@ -1,0 +1,92 @@
+"""Parity of the HIP kernels with the CPU oracle, through the C ABI.
+
+The five workloads run on every kernel of the library (the naive and scalar-tiled rungs
+skip the 8192^3 shape, which only the hot path needs). Small-integer inputs must match
+the oracle exactly (every partial sum is an integer below 2^24, so any summation order
+is exact in FP32); float inputs must have max |C - C_ref| / sum_k |a_ik b_kj| <= 1e-5.
+At the full sizes the oracle checks sampled rows (all their columns), chosen to cover
+tile edges. Every call also checks that nothing outside C's M x N region was written.
+"""
+import numpy as np
+import pytest
+
+import fp32_gemm_f32_amd as g
+import oracle
+import workloads as wl
+from gpu_util import TOL, GuardedC, device_matrix, run_kernel
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    g.library()   # raises if the HIP library is missing: no fallback
+    return torch
+
+
+def sample_rows(M: int, n_random: int, seed: int):
+    """Rows at tile boundaries (multiples of 32/64/128/256 and their neighbours) plus
+    random rows."""
+    if M <= 2048:
+        return None   # the oracle checks every row
+    edges = {0, 1, M - 1, M - 2}
+    for t in (32, 64, 128, 256):
+        for r in range(t, M, max(t, M // 8)):
+            edges.update({r - 1, r})
+    rng = np.random.default_rng(seed)
+    rows = sorted(edges | set(rng.choice(M, n_random, replace=False).tolist()))
+    return [r for r in rows if 0 <= r < M]
+
+
+def run_config(name, variant, kernel, torch):
+    w = wl.WORKLOADS[name]
+    A, B = wl.operands(name, variant)
+    _, dA, lda = device_matrix(A)
+    _, dB, ldb = device_matrix(B)
+    c = GuardedC(w.M, w.N)
+    print(f"[parity] {name} {variant} {kernel} {w.M}x{w.N}x{w.K}", flush=True)
+    run_kernel(kernel, w.M, w.N, w.K, dA, lda, dB, ldb, c)
+    torch.cuda.synchronize()
+    C = c.result()
+    rows = sample_rows(w.M, 24, seed=w.index)
+    rep = oracle.check(A, B, C, rows=rows)
+    assert rep["n_nonfinite"] == 0, rep
+    if variant == "int":
+        assert rep["n_inexact"] == 0, rep
+    else:
+        assert rep["max_err"] <= TOL, rep
+    return rep
+
+
+@pytest.mark.parametrize("variant", ["int", "float"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_hot_path_configs(gpu, name, variant):
+    run_config(name, variant, "auto", gpu)
+
+
+@pytest.mark.parametrize("kernel", ["naive", "tiled16", "tiled32", "tiled32p"])
+@pytest.mark.parametrize("variant", ["int", "float"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c5"])
+def test_reference_kernels_configs(gpu, name, variant, kernel):
+    run_config(name, variant, kernel, gpu)
+
+
+@pytest.mark.parametrize("name", ["c2", "c3"])
+def test_every_variant_on_configs(gpu, name):
+    """Each tile variant of the hot kernel, forced, on the 1024-class shapes."""
+    w = wl.WORKLOADS[name]
+    A, B = wl.operands(name, "int")
+    _, dA, lda = device_matrix(A)
+    _, dB, ldb = device_matrix(B)
+    for v, vname in enumerate(g.variant_names()):
+        if vname.endswith("_vec") and (w.K % 4 or lda % 4 or ldb % 4):
+            continue
+        c = GuardedC(w.M, w.N)
+        print(f"[parity] {name} int variant {vname}", flush=True)
+        run_kernel(f"v{v}", w.M, w.N, w.K, dA, lda, dB, ldb, c)
+        gpu.cuda.synchronize()
+        rep = oracle.check(A, B, c.result())
+        assert rep["n_inexact"] == 0 and rep["n_nonfinite"] == 0, (vname, rep)
