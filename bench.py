@@ -85,8 +85,9 @@ def cpu_baseline(A, B, C_dev, M, N, K, seconds: float):
     lib = oracle.load()
     rows_all = np.linspace(0, M - 1, num=min(M, 4096)).astype(np.int64)
     C_host = C_dev.cpu().numpy()
-    # calibrate on a few rows, then size the sample to the time budget
-    probe = rows_all[:: max(1, len(rows_all) // 8)][:8]
+    # calibrate on two rows per thread, then size the sample to the time budget
+    n_probe = min(len(rows_all), 2 * oracle.threads(lib))
+    probe = rows_all[np.linspace(0, len(rows_all) - 1, num=n_probe).astype(np.int64)]
     t0 = time.perf_counter()
     oracle.check(A, B, C_host, rows=probe, lib=lib)
     t_probe = time.perf_counter() - t0
