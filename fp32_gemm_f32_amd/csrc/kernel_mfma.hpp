@@ -71,7 +71,9 @@ constexpr uint32_t kOob = 0x80000000u;
 constexpr int kXcds = 8;
 // Instruction classes of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008;
+constexpr int kSchedVmemRead = 0x020;
 constexpr int kSchedDsRead = 0x100;
+constexpr int kSchedDsWrite = 0x200;
 constexpr int kGroupM = 8;
 
 struct GemmArgs {
@@ -215,27 +217,31 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_sgemm_mfma(GemmArgs p)
         b_lds[i] = kk * BN + 4 * cc;
     }
 
+    // ---- global -> register staging of one panel ----
     f32x4 ra[A_CH], rb[B_CH];
+    __amdgpu_buffer_rsrc_t rsa, rsb;   // resources rebased at the panel being staged
+    int k_load = 0;
 
-    auto load_panel = [&](int k0) {
-        const __amdgpu_buffer_rsrc_t rsa =
-            make_rsrc(p.A + (int64_t(m0) * lda + k0), p.a_bytes - (int64_t(m0) * lda + k0) * 4);
-        const __amdgpu_buffer_rsrc_t rsb =
-            make_rsrc(p.B + (int64_t(k0) * ldb + n0), p.b_bytes - (int64_t(k0) * ldb + n0) * 4);
-#pragma unroll
-        for (int i = 0; i < A_CH; ++i) {
-            const int kc = k0 + a_k[i];
+    auto set_panel = [&](int k0) {
+        k_load = k0;
+        const int64_t ea = int64_t(m0) * lda + k0, eb = int64_t(k0) * ldb + n0;
+        rsa = make_rsrc(p.A + ea, p.a_bytes - ea * 4);
+        rsb = make_rsrc(p.B + eb, p.b_bytes - eb * 4);
+    };
+    // staging slot l < A_CH is A chunk l, otherwise B chunk l - A_CH
+    auto load_slot = [&](int l) {
+        if (l < A_CH) {
+            const int kc = k_load + a_k[l];
             if constexpr (VEC) {
-                ra[i] = load_b128(rsa, (a_ok[i] && kc < K) ? a_off[i] : kOob);
+                ra[l] = load_b128(rsa, (a_ok[l] && kc < K) ? a_off[l] : kOob);
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    ra[i][e] = load_b32(rsa, (a_ok[i] && kc + e < K) ? a_off[i] + 4u * e : kOob);
+                    ra[l][e] = load_b32(rsa, (a_ok[l] && kc + e < K) ? a_off[l] + 4u * e : kOob);
             }
-        }
-#pragma unroll
-        for (int i = 0; i < B_CH; ++i) {
-            const bool kok = k0 + b_k[i] < K;
+        } else {
+            const int i = l - A_CH;
+            const bool kok = k_load + b_k[i] < K;
             if constexpr (VEC) {
                 rb[i] = load_b128(rsb, (kok && b_n[i] < N) ? b_off[i] : kOob);
             } else {
@@ -245,14 +251,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_sgemm_mfma(GemmArgs p)
             }
         }
     };
-
-    auto store_panel = [&](int stage) {
-        float *As = smem + stage * T::STAGE;
-        float *Bs = As + T::A_TILE;
-#pragma unroll
-        for (int i = 0; i < A_CH; ++i) *reinterpret_cast<f32x4 *>(As + a_lds[i]) = ra[i];
-#pragma unroll
-        for (int i = 0; i < B_CH; ++i) *reinterpret_cast<f32x4 *>(Bs + b_lds[i]) = rb[i];
+    auto write_slot = [&](float *As, int l) {
+        if (l < A_CH) *reinterpret_cast<f32x4 *>(As + a_lds[l]) = ra[l];
+        else *reinterpret_cast<f32x4 *>(As + T::A_TILE + b_lds[l - A_CH]) = rb[l - A_CH];
     };
 
     f32x16 acc[RB][CI * CG];
@@ -267,9 +268,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_sgemm_mfma(GemmArgs p)
     const int a_row0 = (wm * WM + lo) * BK;
     const int b_col0 = wn * WN + CI * lo;
 
-    // One panel: BK/2 MFMA k-steps. Operands of step t+1 (and the A registers of the
-    // next group of 8 k) are read from LDS before the MFMAs of step t are issued, so the
-    // LDS latency is hidden behind matrix-core work instead of stalling the wave.
     auto read_a = [&](const float *As, int kb, f32x4 (&a)[RB]) {
 #pragma unroll
         for (int r = 0; r < RB; ++r)
@@ -281,26 +279,79 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_sgemm_mfma(GemmArgs p)
 #pragma unroll
         for (int g = 0; g < CG; ++g) b[g] = *reinterpret_cast<const bvec *>(brow + g * 32 * CI);
     };
-    auto compute = [&](int stage) {
-        constexpr int STEPS = BK / 2;
-        const float *As = smem + stage * T::STAGE;
+
+    // Operand registers: a[kb & 1] holds the A values of k-group kb, b[t & 1] the B values
+    // of k-step t.
+    f32x4 a[2][RB];
+    bvec b[2][CG];
+
+    // One panel of BK/2 MFMA k-steps from LDS stage `cur`. Everything else the panel does
+    // is placed in the shadow of its MFMAs (each 32x32x2 MFMA holds the matrix pipe for
+    // 64 cycles and the wave issues in order, so an instruction placed between two MFMAs
+    // costs nothing):
+    //   steps 0..LS-1       issue the global loads of the next panel (NEXT only)
+    //   every step t        read the operands of step t+1 from LDS
+    //   steps STEPS-1-WS..  write the staged next panel into the other stage (NEXT only)
+    //   last step           barrier, then read step 0 of the next panel from the other
+    //                       stage; the MFMAs of the last step need only registers, so
+    //                       they cover the latency of those reads.
+    // One barrier per panel is enough: the other stage was last read before the previous
+    // panel's barrier, and this panel's reads of `cur` all precede this barrier.
+    constexpr int STEPS = BK / 2;
+    constexpr int NL = A_CH + B_CH;
+    constexpr int LS = STEPS >= 8 ? 4 : 2;
+    constexpr int WS = 3;
+    constexpr int PER_LOAD = (NL + LS - 1) / LS;
+    constexpr int PER_WRITE = (NL + WS - 1) / WS;
+    static_assert(LS + WS < STEPS, "loads and LDS writes of a panel need separate steps");
+
+    auto panel = [&](int cur, auto next_tag) {
+        constexpr bool NEXT = decltype(next_tag)::value;
+        const float *As = smem + cur * T::STAGE;
         const float *Bs = As + T::A_TILE;
-        f32x4 a[2][RB];
-        bvec b[2][CG];
-        read_a(As, 0, a[0]);
-        read_b(Bs, 0, b[0]);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, RB + CG, 0);
+        float *Anext = smem + (cur ^ 1) * T::STAGE;
         static_for<0, STEPS>([&](auto tc) {
             constexpr int t = decltype(tc)::value;
             constexpr int kb = t >> 2, s = t & 3;
             constexpr bool next_b = t + 1 < STEPS;
             constexpr bool next_a = s == 0 && kb + 1 < BK / 8;
+            constexpr int w0 = t - (STEPS - 1 - WS);   // write group index
+            constexpr int n_load = (NEXT && t < LS)
+                ? ((t + 1) * PER_LOAD < NL ? PER_LOAD : (NL - t * PER_LOAD > 0 ? NL - t * PER_LOAD : 0))
+                : 0;
+            constexpr int n_write = (NEXT && w0 >= 0 && w0 < WS)
+                ? ((w0 + 1) * PER_WRITE < NL ? PER_WRITE
+                                             : (NL - w0 * PER_WRITE > 0 ? NL - w0 * PER_WRITE : 0))
+                : 0;
+            if constexpr (n_load > 0) {
+#pragma unroll
+                for (int l = t * PER_LOAD; l < t * PER_LOAD + n_load; ++l) load_slot(l);
+            }
+            if constexpr (n_write > 0) {
+#pragma unroll
+                for (int l = w0 * PER_WRITE; l < w0 * PER_WRITE + n_write; ++l)
+                    write_slot(Anext, l);
+            }
             if constexpr (next_b) read_b(Bs, t + 1, b[(t + 1) & 1]);
             if constexpr (next_a) read_a(As, kb + 1, a[(kb + 1) & 1]);
-            // the scheduler would otherwise sink these reads next to their first use
+            if constexpr (t == STEPS - 1 && NEXT) {
+                // keep the previous steps' MFMAs above the barrier: they cover the
+                // completion of this panel's LDS writes
+                __builtin_amdgcn_sched_barrier(0);
+                __syncthreads();
+                read_a(Anext, 0, a[0]);
+                read_b(Anext + T::A_TILE, 0, b[0]);
+            }
+            // pin the order: memory instructions of this step first, then its MFMAs
+            if constexpr (n_load > 0)
+                __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, n_load * (VEC ? 1 : 4), 0);
+            if constexpr (n_write > 0)
+                __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, n_write, 0);
             if constexpr (next_b || next_a)
                 __builtin_amdgcn_sched_group_barrier(
                     kSchedDsRead, (next_b ? CG : 0) + (next_a ? RB : 0), 0);
+            if constexpr (t == STEPS - 1 && NEXT)
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, RB + CG, 0);
             __builtin_amdgcn_sched_group_barrier(kSchedMfma, RB * CG * CI, 0);
 #pragma unroll
             for (int r = 0; r < RB; ++r)
@@ -316,19 +367,21 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_sgemm_mfma(GemmArgs p)
         });
     };
 
-    // ---- K loop: two LDS stages, loads of panel p+1 in flight during panel p ----
+    // ---- K loop: two LDS stages; the last panel stages nothing ----
     const int panels = (K + BK - 1) / BK;
-    load_panel(0);
-    store_panel(0);
+    set_panel(0);
+#pragma unroll
+    for (int l = 0; l < NL; ++l) load_slot(l);
+#pragma unroll
+    for (int l = 0; l < NL; ++l) write_slot(smem, l);
     __syncthreads();
-    for (int pnl = 0; pnl < panels; ++pnl) {
-        const int cur = pnl & 1;
-        const bool more = pnl + 1 < panels;
-        if (more) load_panel((pnl + 1) * BK);
-        compute(cur);
-        if (more) store_panel(cur ^ 1);
-        __syncthreads();
+    read_a(smem, 0, a[0]);
+    read_b(smem + T::A_TILE, 0, b[0]);
+    for (int pnl = 0; pnl + 1 < panels; ++pnl) {
+        set_panel((pnl + 1) * BK);
+        panel(pnl & 1, std::true_type{});
     }
+    panel((panels - 1) & 1, std::false_type{});
 
     // ---- epilogue: accumulators to C, masked at the M and N edges ----
     const int ldc = p.ldc;
