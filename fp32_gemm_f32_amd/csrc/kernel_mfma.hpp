@@ -69,12 +69,24 @@ constexpr int kBufferWord3 = 0x00020000;
 // A voffset beyond every resource size built below: loads from it return zero.
 constexpr uint32_t kOob = 0x80000000u;
 constexpr int kXcds = 8;
+// Pipeline placement inside a panel (build-time tuning knobs): the next panel's global
+// loads are spread over the first SGEMM_LOAD_STEPS k-steps and its LDS writes over the
+// SGEMM_WRITE_STEPS steps before the last one.
+#ifndef SGEMM_LOAD_STEPS
+#define SGEMM_LOAD_STEPS 4
+#endif
+#ifndef SGEMM_WRITE_STEPS
+#define SGEMM_WRITE_STEPS 3
+#endif
 // Instruction classes of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedVmemRead = 0x020;
 constexpr int kSchedDsRead = 0x100;
 constexpr int kSchedDsWrite = 0x200;
-constexpr int kGroupM = 8;
+#ifndef SGEMM_GROUP_M
+#define SGEMM_GROUP_M 8
+#endif
+constexpr int kGroupM = SGEMM_GROUP_M;
 
 struct GemmArgs {
     const float *A;
@@ -299,8 +311,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_sgemm_mfma(GemmArgs p)
     // panel's barrier, and this panel's reads of `cur` all precede this barrier.
     constexpr int STEPS = BK / 2;
     constexpr int NL = A_CH + B_CH;
-    constexpr int LS = STEPS >= 8 ? 4 : 2;
-    constexpr int WS = 3;
+    constexpr int LS = SGEMM_LOAD_STEPS;
+    constexpr int WS = SGEMM_WRITE_STEPS;
     constexpr int PER_LOAD = (NL + LS - 1) / LS;
     constexpr int PER_WRITE = (NL + WS - 1) / WS;
     static_assert(LS + WS < STEPS, "loads and LDS writes of a panel need separate steps");

@@ -63,6 +63,7 @@ constexpr VariantEntry entry(const char *name, int wg_per_cu, double rate)
 const VariantEntry kVariants[] = {
     entry<256, 256, 32, 2, 2, true>("mfma_256x256x32_w2x2_vec", 1, 1.00),
     entry<256, 256, 32, 2, 2, false>("mfma_256x256x32_w2x2_dw", 1, 1.00),
+    entry<256, 256, 32, 2, 4, true>("mfma_256x256x32_w2x4_vec", 1, 1.03),
     entry<128, 128, 32, 2, 2, true>("mfma_128x128x32_w2x2_vec", 2, 0.95),
     entry<128, 128, 32, 2, 2, false>("mfma_128x128x32_w2x2_dw", 2, 0.95),
     entry<64, 64, 32, 2, 2, true>("mfma_64x64x32_w2x2_vec", 4, 0.80),
