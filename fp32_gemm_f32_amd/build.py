@@ -36,6 +36,10 @@ def flags() -> list[str]:
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         # packed FP32 instructions stay off: the compiler must not form them from float2
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA accumulators stay in VGPRs (every kernel fits in 256 registers); left to its
+        # heuristics the register allocator moves them between AGPRs and VGPRs on each
+        # iteration of the persistent tile loop
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-Wall", "-Wno-unused-command-line-argument",
         f"-I{INCLUDE}", f"-I{CSRC}",
     ]

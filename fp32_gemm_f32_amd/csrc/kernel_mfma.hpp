@@ -27,8 +27,13 @@
 //    touching memory: that is the zero-fill of the pages' masked loads, and it also
 //    keeps the last rows of B from reading past the end of the allocation. Resources
 //    are rebased per workgroup (A) and per panel (B), keeping offsets in 31 bits.
-//  * VEC = true loads 16 bytes per lane (rows 16-byte aligned, K % 4 == 0); VEC = false
-//    loads one dword per element with a per-element mask (any alignment, any K).
+//  * Every lane loads 16 bytes (four consecutive floats of a row) per buffer load. gfx950
+//    serves 16-byte buffer loads and stores at any 4-byte aligned address, so odd leading
+//    dimensions need no narrower path. When K % 4 != 0 the last chunk of an A row is only
+//    partly inside the matrix; its elements past K are replaced by zero after the load.
+//  * C is written through a buffer resource too: rows past M get the voffset kOob and the
+//    hardware drops the store; a chunk of columns that crosses N is stored element by
+//    element.
 //  * MFMA operand layout (32x32x2): lane l supplies A[l % 32][l / 32] and
 //    B[l / 32][l % 32]; accumulator register v of lane l holds
 //    D[8 (v / 4) + 4 (l / 32) + v % 4][l % 32].
@@ -96,7 +101,7 @@ struct GemmArgs {
     int64_t b_bytes;   // bytes from B to the end of its last row
     int M, N, K, lda, ldb, ldc;
     int tiles_m, tiles_n;
-    int store_vec;     // C rows and base allow 16-byte stores
+    int64_t c_bytes;   // bytes from C to the end of its last row
 };
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const float *base, int64_t bytes)
@@ -112,11 +117,6 @@ __device__ inline f32x4 load_b128(__amdgpu_buffer_rsrc_t r, uint32_t voff)
     return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
 }
 
-__device__ inline float load_b32(__amdgpu_buffer_rsrc_t r, uint32_t voff)
-{
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
-}
-
 // Calls f(std::integral_constant<int, I>) for I = BEGIN .. END-1, so I is a constant
 // expression inside f (needed by the scheduling builtins).
 template <int BEGIN, int END, typename F>
@@ -128,12 +128,32 @@ __device__ inline void static_for(F &&f)
     }
 }
 
+// Buffer store of W consecutive floats at voff + soff (dropped by the hardware when voff is
+// out of range; soff stays below 2^31, so kOob + soff cannot wrap into range).
+template <int W>
+__device__ inline void store_vec(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                 typename fvec<W>::type v)
+{
+    if constexpr (W == 4) {
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, soff, 0);
+    } else if constexpr (W == 2) {
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, voff, soff, 0);
+    } else {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, v), r, voff, soff,
+                                              0);
+    }
+}
+
 // Physical 16-byte chunk slot of logical chunk q in A-tile row r (CPR chunks per row).
 template <int CPR>
 __host__ __device__ constexpr int a_swizzle(int r)
 {
-    static_assert(CPR == 8 || CPR == 4 || CPR == 2, "A row must hold 2, 4 or 8 chunks");
-    return CPR == 8 ? ((r & 7) ^ ((r >> 3) & 1))
+    static_assert(CPR == 16 || CPR == 8 || CPR == 4 || CPR == 2,
+                  "A row must hold 2, 4, 8 or 16 chunks");
+    return CPR == 16 ? (r & 15)
+         : CPR == 8 ? ((r & 7) ^ ((r >> 3) & 1))
          : CPR == 4 ? (((r >> 1) ^ (r >> 3)) & 3)
                     : (((r >> 2) ^ (r >> 3)) & 1);
 }
@@ -155,7 +175,7 @@ __device__ inline void tile_coords(int bid, int tiles_m, int tiles_n, int &tm, i
     tn = w / rows;
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, bool VEC>
+template <int BM, int BN, int BK, int WGM, int WGN, int KACC = 1>
 struct MfmaTile {
     static constexpr int kThreads = 64 * WGM * WGN;
     static constexpr int WM = BM / WGM;          // wave tile rows
@@ -178,10 +198,10 @@ struct MfmaTile {
     static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS holds 160 KiB per workgroup");
 };
 
-template <int BM, int BN, int BK, int WGM, int WGN, bool VEC>
+template <int BM, int BN, int BK, int WGM, int WGN, int KACC, bool PERSIST>
 __global__ __launch_bounds__(64 * WGM * WGN) void k_sgemm_mfma(GemmArgs p)
 {
-    using T = MfmaTile<BM, BN, BK, WGM, WGN, VEC>;
+    using T = MfmaTile<BM, BN, BK, WGM, WGN, KACC>;
     constexpr int NT = T::kThreads, WM = T::WM, WN = T::WN, RB = T::RB, CI = T::CI,
                   CG = T::CG, CPR = T::CPR, A_CH = T::A_CH, B_CH = T::B_CH;
     typedef typename fvec<CI>::type bvec;
@@ -194,40 +214,43 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_sgemm_mfma(GemmArgs p)
     const int wave = tid >> 6;
     const int wm = wave / WGN, wn = wave % WGN;
 
-    int tm, tn;
-    tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
     const int M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
+    const int ntiles = p.tiles_m * p.tiles_n;
 
-    // ---- per-thread load assignment (fixed for the whole K loop) ----
-    // A chunk c = tid + i*NT covers row c / CPR, k columns 4 (c % CPR) .. +3 of a panel.
-    uint32_t a_off[A_CH];
-    int a_k[A_CH];
-    int a_lds[A_CH];
-    bool a_ok[A_CH];
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-        const int c = tid + i * NT;
-        const int r = c / CPR, q = c % CPR;
-        a_off[i] = uint32_t(r) * uint32_t(lda) * 4u + uint32_t(q) * 16u;
-        a_k[i] = 4 * q;
-        a_lds[i] = r * BK + 4 * (q ^ a_swizzle<CPR>(r));
-        a_ok[i] = m0 + r < M;
-    }
-    // B chunk c = tid + i*NT covers panel row c / (BN/4), columns 4 (c % (BN/4)) .. +3.
-    uint32_t b_off[B_CH];
-    int b_k[B_CH];
-    int b_n[B_CH];
-    int b_lds[B_CH];
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-        const int c = tid + i * NT;
-        const int kk = c / (BN / 4), cc = c % (BN / 4);
-        b_off[i] = uint32_t(kk) * uint32_t(ldb) * 4u + uint32_t(cc) * 16u;
-        b_k[i] = kk;
-        b_n[i] = n0 + 4 * cc;
-        b_lds[i] = kk * BN + 4 * cc;
-    }
+    // ---- per-thread load assignment ----
+    // Thread tid stages A chunks c = tid + i*NT, i.e. rows a_r0 + i*A_RSTEP at the fixed
+    // k-columns 4*a_q .. +3, and B chunks at panel rows b_k0 + i*B_KSTEP, fixed columns
+    // b_c0 .. +3. Because A_RSTEP is a multiple of 16 rows, every A chunk of a thread has
+    // the same swizzle, so all offsets are one base plus a compile-time stride.
+    constexpr int A_RSTEP = NT / CPR;
+    constexpr int B_KSTEP = NT / (BN / 4);
+    static_assert(NT % CPR == 0 && A_RSTEP % 16 == 0 && NT % (BN / 4) == 0,
+                  "chunk assignment strides");
+    const int a_r0 = tid / CPR, a_q = tid % CPR;
+    const uint32_t a_off0 = uint32_t(a_r0) * uint32_t(lda) * 4u + uint32_t(a_q) * 16u;
+    const uint32_t a_stride = uint32_t(A_RSTEP) * uint32_t(lda) * 4u;
+    const int a_lds0 = a_r0 * BK + 4 * (a_q ^ a_swizzle<CPR>(a_r0));
+    const int b_k0 = tid / (BN / 4), b_c0 = 4 * (tid % (BN / 4));
+    const uint32_t b_off0 = uint32_t(b_k0) * uint32_t(ldb) * 4u + uint32_t(b_c0) * 4u;
+    const uint32_t b_stride = uint32_t(B_KSTEP) * uint32_t(ldb) * 4u;
+    const int b_lds0 = b_k0 * BN + b_c0;
+
+    // The tile whose panels are being loaded (it runs one tile ahead of the tile being
+    // computed during the last panel of each tile).
+    int lm0 = 0, ln0 = 0;
+    bool b_col_ok = false;
+    auto set_load_tile = [&](int vb) {
+        if (vb < ntiles) {
+            int tm, tn;
+            tile_coords(vb, p.tiles_m, p.tiles_n, tm, tn);
+            lm0 = tm * BM;
+            ln0 = tn * BN;
+        } else {   // no such tile: rows and columns past the matrix, all loads masked
+            lm0 = M;
+            ln0 = N;
+        }
+        b_col_ok = ln0 + b_c0 < N;
+    };
 
     // ---- global -> register staging of one panel ----
     f32x4 ra[A_CH], rb[B_CH];
@@ -236,43 +259,48 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_sgemm_mfma(GemmArgs p)
 
     auto set_panel = [&](int k0) {
         k_load = k0;
-        const int64_t ea = int64_t(m0) * lda + k0, eb = int64_t(k0) * ldb + n0;
+        const int64_t ea = int64_t(lm0) * lda + k0, eb = int64_t(k0) * ldb + ln0;
         rsa = make_rsrc(p.A + ea, p.a_bytes - ea * 4);
         rsb = make_rsrc(p.B + eb, p.b_bytes - eb * 4);
     };
     // staging slot l < A_CH is A chunk l, otherwise B chunk l - A_CH
     auto load_slot = [&](int l) {
         if (l < A_CH) {
-            const int kc = k_load + a_k[l];
-            if constexpr (VEC) {
-                ra[l] = load_b128(rsa, (a_ok[l] && kc < K) ? a_off[l] : kOob);
-            } else {
+            const int kc = k_load + 4 * a_q;
+            const bool ok = lm0 + a_r0 + l * A_RSTEP < M && kc < K;
+            f32x4 v = load_b128(rsa, ok ? a_off0 + uint32_t(l) * a_stride : kOob);
+            // a chunk that crosses K: its elements past K belong to the row padding or the
+            // next row; zero them (a select, so a NaN there cannot leak)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    ra[l][e] = load_b32(rsa, (a_ok[l] && kc + e < K) ? a_off[l] + 4u * e : kOob);
-            }
+            for (int e = 1; e < 4; ++e) v[e] = kc + e < K ? v[e] : 0.0f;
+            ra[l] = v;
         } else {
             const int i = l - A_CH;
-            const bool kok = k_load + b_k[i] < K;
-            if constexpr (VEC) {
-                rb[i] = load_b128(rsb, (kok && b_n[i] < N) ? b_off[i] : kOob);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    rb[i][e] = load_b32(rsb, (kok && b_n[i] + e < N) ? b_off[i] + 4u * e : kOob);
-            }
+            const bool ok = k_load + b_k0 + i * B_KSTEP < K && b_col_ok;
+            // columns past N inside a chunk only reach accumulators that are never stored
+            rb[i] = load_b128(rsb, ok ? b_off0 + uint32_t(i) * b_stride : kOob);
         }
     };
     auto write_slot = [&](float *As, int l) {
-        if (l < A_CH) *reinterpret_cast<f32x4 *>(As + a_lds[l]) = ra[l];
-        else *reinterpret_cast<f32x4 *>(As + T::A_TILE + b_lds[l - A_CH]) = rb[l - A_CH];
+        if (l < A_CH)
+            *reinterpret_cast<f32x4 *>(As + a_lds0 + l * A_RSTEP * BK) = ra[l];
+        else
+            *reinterpret_cast<f32x4 *>(As + T::A_TILE + b_lds0 + (l - A_CH) * B_KSTEP * BN) =
+                rb[l - A_CH];
     };
 
-    f32x16 acc[RB][CI * CG];
+    // KACC accumulator sets take the k-steps in turn (KACC > 1 gives a wave with few MFMA
+    // blocks independent accumulation chains); they are summed before the epilogue.
+    f32x16 acc[KACC][RB][CI * CG];
+    auto zero_acc = [&]() {
 #pragma unroll
-    for (int i = 0; i < RB; ++i)
+        for (int h = 0; h < KACC; ++h)
 #pragma unroll
-        for (int j = 0; j < CI * CG; ++j) acc[i][j] = f32x16{};
+            for (int i = 0; i < RB; ++i)
+#pragma unroll
+                for (int j = 0; j < CI * CG; ++j) acc[h][i][j] = f32x16{};
+    };
+    zero_acc();
 
     // A-operand LDS rows of this lane: row wm*WM + rb*32 + lo, whose swizzle depends on
     // lo only (wm*WM + rb*32 is a multiple of 32).
@@ -356,7 +384,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_sgemm_mfma(GemmArgs p)
             }
             // pin the order: memory instructions of this step first, then its MFMAs
             if constexpr (n_load > 0)
-                __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, n_load * (VEC ? 1 : 4), 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, n_load, 0);
             if constexpr (n_write > 0)
                 __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, n_write, 0);
             if constexpr (next_b || next_a)
@@ -373,14 +401,82 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_sgemm_mfma(GemmArgs p)
                     for (int j = 0; j < CI; ++j) {
                         float bj;
                         if constexpr (CI == 1) bj = b[t & 1][g]; else bj = b[t & 1][g][j];
-                        acc[r][g * CI + j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                            a[kb & 1][r][s], bj, acc[r][g * CI + j], 0, 0, 0);
+                        constexpr int h = t % KACC;
+                        acc[h][r][g * CI + j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                            a[kb & 1][r][s], bj, acc[h][r][g * CI + j], 0, 0, 0);
                     }
         });
     };
 
-    // ---- K loop: two LDS stages; the last panel stages nothing ----
+    static_assert((BK / 2) % KACC == 0, "accumulator sets divide the k-steps of a panel");
+
+    // ---- epilogue of one tile: accumulators to C through a buffer resource ----
+    const int ldc = p.ldc;
+    auto epilogue = [&](int m0, int n0) {
+#pragma unroll
+        for (int h = 1; h < KACC; ++h)
+#pragma unroll
+            for (int i = 0; i < RB; ++i)
+#pragma unroll
+                for (int j = 0; j < CI * CG; ++j) acc[0][i][j] += acc[h][i][j];
+        // Lane (lo, hi) owns rows lrow + dr (dr = 8 (v / 4) + v % 4 for accumulator v) and
+        // columns col .. col + CI - 1 of each of its blocks. The row step dr * ldc goes in
+        // the scalar offset; rows past M and chunks that cross N get voffset kOob (the
+        // hardware drops those stores), and only a tile on the N edge stores the partial
+        // chunks element by element.
+        const int64_t ec = int64_t(m0) * ldc + n0;
+        const __amdgpu_buffer_rsrc_t rsc = make_rsrc(p.C + ec, p.c_bytes - ec * 4);
+        const uint32_t ldc4 = uint32_t(ldc) * 4u;
+        const int rows_left = M - m0, cols_left = N - n0;
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            const int lrow = wm * WM + r * 32 + 4 * hi;
+#pragma unroll
+            for (int g = 0; g < CG; ++g) {
+                const int col = wn * WN + g * 32 * CI + CI * lo;
+                const uint32_t vbase = uint32_t(lrow) * ldc4 + uint32_t(col) * 4u;
+                const bool col_full = col + CI <= cols_left;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int dr = 8 * (v >> 2) + (v & 3);
+                    bvec out;
+#pragma unroll
+                    for (int j = 0; j < CI; ++j) {
+                        if constexpr (CI == 1) out = acc[0][r][g * CI + j][v];
+                        else out[j] = acc[0][r][g * CI + j][v];
+                    }
+                    const bool ok = col_full && lrow + dr < rows_left;
+                    store_vec<CI>(rsc, ok ? vbase : kOob, uint32_t(dr) * ldc4, out);
+                }
+            }
+        }
+        if (cols_left < BN) {
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                const int lrow = wm * WM + r * 32 + 4 * hi;
+#pragma unroll
+                for (int g = 0; g < CG; ++g) {
+                    const int col = wn * WN + g * 32 * CI + CI * lo;
+                    const uint32_t vbase = uint32_t(lrow) * ldc4 + uint32_t(col) * 4u;
+                    const bool partial = col < cols_left && col + CI > cols_left;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int dr = 8 * (v >> 2) + (v & 3);
+                        const bool ok = partial && lrow + dr < rows_left;
+#pragma unroll
+                        for (int j = 0; j < CI; ++j)
+                            store_vec<1>(rsc, ok && col + j < cols_left ? vbase + 4u * j : kOob,
+                                         uint32_t(dr) * ldc4, acc[0][r][g * CI + j][v]);
+                    }
+                }
+            }
+        }
+    };
+
+    // ---- K loop over the workgroup's tiles ----
     const int panels = (K + BK - 1) / BK;
+    int vb = blockIdx.x;
+    set_load_tile(vb);
     set_panel(0);
 #pragma unroll
     for (int l = 0; l < NL; ++l) load_slot(l);
@@ -389,38 +485,38 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_sgemm_mfma(GemmArgs p)
     __syncthreads();
     read_a(smem, 0, a[0]);
     read_b(smem + T::A_TILE, 0, b[0]);
-    for (int pnl = 0; pnl + 1 < panels; ++pnl) {
-        set_panel((pnl + 1) * BK);
-        panel(pnl & 1, std::true_type{});
-    }
-    panel((panels - 1) & 1, std::false_type{});
 
-    // ---- epilogue: accumulators to C, masked at the M and N edges ----
-    const int ldc = p.ldc;
-#pragma unroll
-    for (int r = 0; r < RB; ++r) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int row = m0 + wm * WM + r * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
-            if (row >= M) continue;
-            float *crow = p.C + int64_t(row) * ldc;
-#pragma unroll
-            for (int g = 0; g < CG; ++g) {
-                const int col = n0 + wn * WN + g * 32 * CI + CI * lo;
-                if (CI > 1 && p.store_vec && col + CI <= N) {
-                    bvec out;
-#pragma unroll
-                    for (int j = 0; j < CI; ++j) {
-                        if constexpr (CI == 1) out = acc[r][g * CI + j][v];
-                        else out[j] = acc[r][g * CI + j][v];
-                    }
-                    *reinterpret_cast<bvec *>(crow + col) = out;
-                } else {
-#pragma unroll
-                    for (int j = 0; j < CI; ++j)
-                        if (col + j < N) crow[col + j] = acc[r][g * CI + j][v];
-                }
+    if constexpr (!PERSIST) {
+        // one tile per workgroup: the last panel stages nothing
+        for (int pnl = 0; pnl + 1 < panels; ++pnl) {
+            set_panel((pnl + 1) * BK);
+            panel(pnl & 1, std::true_type{});
+        }
+        panel((panels - 1) & 1, std::false_type{});
+        epilogue(lm0, ln0);
+    } else {
+        // Tiles vb, vb + G, vb + 2G, ...: the last panel of a tile stages panel 0 of the
+        // workgroup's next tile, so that tile's first loads and LDS writes run under the
+        // current tile's MFMAs and the epilogue's stores drain while the next tile
+        // computes. After the last tile the staged "next tile" lies past the matrix and
+        // every one of its loads is masked to zero; one panel body serves every panel.
+        const int G = gridDim.x;
+        int cur = 0;
+        int cm0 = lm0, cn0 = ln0;   // the tile being computed
+        for (;;) {
+            for (int pnl = 0; pnl < panels; ++pnl) {
+                const bool last = pnl + 1 == panels;
+                if (last) set_load_tile(vb + G);
+                set_panel(last ? 0 : (pnl + 1) * BK);
+                panel(cur, std::true_type{});
+                cur ^= 1;
             }
+            epilogue(cm0, cn0);
+            vb += G;
+            if (vb >= ntiles) break;
+            zero_acc();
+            cm0 = lm0;
+            cn0 = ln0;
         }
     }
 }

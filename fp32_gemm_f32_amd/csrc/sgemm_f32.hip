@@ -53,21 +53,20 @@ struct VariantEntry {
     int threads;
 };
 
-template <int BM, int BN, int BK, int WGM, int WGN, bool VEC>
+template <int BM, int BN, int BK, int WGM, int WGN, int KACC, bool PERSIST>
 constexpr VariantEntry entry(const char *name, int wg_per_cu, double rate)
 {
-    return VariantEntry{Variant{name, BM, BN, BK, WGM, WGN, VEC, wg_per_cu, rate},
-                        &k_sgemm_mfma<BM, BN, BK, WGM, WGN, VEC>, 64 * WGM * WGN};
+    return VariantEntry{Variant{name, BM, BN, BK, WGM, WGN, wg_per_cu, rate, PERSIST},
+                        &k_sgemm_mfma<BM, BN, BK, WGM, WGN, KACC, PERSIST>, 64 * WGM * WGN};
 }
 
+// Rates are the variants' throughput at 8192^3 relative to 140 TFLOP/s on MI355X.
+// The 8-wave 256x256 tile needs 242 of its 256 registers and runs one tile per workgroup;
+// the smaller tiles are persistent.
 const VariantEntry kVariants[] = {
-    entry<256, 256, 32, 2, 2, true>("mfma_256x256x32_w2x2_vec", 1, 1.00),
-    entry<256, 256, 32, 2, 2, false>("mfma_256x256x32_w2x2_dw", 1, 1.00),
-    entry<256, 256, 32, 2, 4, true>("mfma_256x256x32_w2x4_vec", 1, 1.03),
-    entry<128, 128, 32, 2, 2, true>("mfma_128x128x32_w2x2_vec", 2, 0.95),
-    entry<128, 128, 32, 2, 2, false>("mfma_128x128x32_w2x2_dw", 2, 0.95),
-    entry<64, 64, 32, 2, 2, true>("mfma_64x64x32_w2x2_vec", 4, 0.80),
-    entry<64, 64, 32, 2, 2, false>("mfma_64x64x32_w2x2_dw", 4, 0.80),
+    entry<256, 256, 32, 2, 4, 1, false>("mfma_256x256x32_w2x4", 1, 1.03),
+    entry<128, 128, 32, 2, 2, 1, true>("mfma_128x128x32_w2x2_p", 2, 0.94),
+    entry<64, 64, 64, 2, 2, 2, true>("mfma_64x64x64_w2x2_acc2_p", 2, 0.82),
 };
 constexpr int kNumVariants = int(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -76,14 +75,10 @@ struct TableInit {
     TableInit() { for (int i = 0; i < kNumVariants; ++i) g_table[i] = kVariants[i].v; }
 } g_table_init;
 
-Operands make_operands(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
-                       const float *C, int ldc)
+Operands make_operands(int M, int N, int K, int lda, int ldb, int ldc)
 {
     Operands o;
     o.M = M; o.N = N; o.K = K; o.lda = lda; o.ldb = ldb; o.ldc = ldc;
-    o.a16 = (reinterpret_cast<uintptr_t>(A) & 15u) == 0;
-    o.b16 = (reinterpret_cast<uintptr_t>(B) & 15u) == 0;
-    o.c16 = (reinterpret_cast<uintptr_t>(C) & 15u) == 0;
     return o;
 }
 
@@ -106,21 +101,25 @@ int device_cus(int *out)
     return SGEMM_OK;
 }
 
+// A persistent variant runs a grid of at most CUs x (workgroups per CU), each workgroup
+// taking every grid-th tile; the others run one workgroup per tile.
 int run_variant(int vi, const Operands &o, const float *A, const float *B, float *C,
-                void *stream)
+                void *stream, int cus)
 {
     const VariantEntry &e = kVariants[vi];
     GemmArgs p;
     p.A = A; p.B = B; p.C = C;
     p.a_bytes = span_elems(o.M, o.K, o.lda) * 4;
     p.b_bytes = span_elems(o.K, o.N, o.ldb) * 4;
+    p.c_bytes = span_elems(o.M, o.N, o.ldc) * 4;
     p.M = o.M; p.N = o.N; p.K = o.K; p.lda = o.lda; p.ldb = o.ldb; p.ldc = o.ldc;
     p.tiles_m = (o.M + e.v.BM - 1) / e.v.BM;
     p.tiles_n = (o.N + e.v.BN - 1) / e.v.BN;
-    p.store_vec = c_vec_ok(o) ? 1 : 0;
     const int64_t tiles = int64_t(p.tiles_m) * p.tiles_n;
     if (tiles > INT32_MAX) return SGEMM_ETOO_LARGE;
-    return launch(e.kern, dim3(unsigned(tiles)), dim3(e.threads), stream, p);
+    const int64_t slots = int64_t(cus) * e.v.wg_per_cu;
+    const int64_t grid = (e.v.persist && tiles > slots) ? slots : tiles;
+    return launch(e.kern, dim3(unsigned(grid)), dim3(e.threads), stream, p);
 }
 
 int run_hot(int variant, int M, int N, int K, const float *A, int lda, const float *B, int ldb,
@@ -131,18 +130,14 @@ int run_hot(int variant, int M, int N, int K, const float *A, int lda, const flo
     if (variant >= kNumVariants) return SGEMM_EINVAL_ARG;
     if (M == 0 || N == 0) return SGEMM_OK;
     if (K == 0) return fill_zero(M, N, C, ldc, stream);
-    const Operands o = make_operands(M, N, K, A, lda, B, ldb, C, ldc);
-    if (variant >= 0) {
-        if (kVariants[variant].v.vec && !vec_ok(o)) return SGEMM_EINVAL_ARG;
-        if (!offsets_fit(kVariants[variant].v, o)) return SGEMM_ETOO_LARGE;
-        return run_variant(variant, o, A, B, C, stream);
-    }
+    const Operands o = make_operands(M, N, K, lda, ldb, ldc);
+    if (variant >= 0 && !offsets_fit(kVariants[variant].v, o)) return SGEMM_ETOO_LARGE;
     int cus = 0;
     const int qs = device_cus(&cus);
     if (qs != SGEMM_OK) return qs;
-    const int vi = choose_variant(g_table, o, cus);
+    const int vi = variant >= 0 ? variant : choose_variant(g_table, o, cus);
     if (vi < 0) return SGEMM_ETOO_LARGE;
-    return run_variant(vi, o, A, B, C, stream);
+    return run_variant(vi, o, A, B, C, stream, cus);
 }
 
 }  // namespace
@@ -224,7 +219,8 @@ extern "C" int sgemm_f32_plan_describe(int M, int N, int K, const float *A, int 
                                        int num_cus, char *buf, int buflen)
 {
     if (!buf || buflen <= 0) return SGEMM_EINVAL_ARG;
-    const Operands o = make_operands(M, N, K, A, lda, B, ldb, C, ldc);
+    (void)A; (void)B; (void)C;
+    const Operands o = make_operands(M, N, K, lda, ldb, ldc);
     if (M < 0 || N < 0 || K < 0) return SGEMM_EINVAL_DIM;
     int cus = num_cus;
     if (cus <= 0) {
@@ -235,17 +231,17 @@ extern "C" int sgemm_f32_plan_describe(int M, int N, int K, const float *A, int 
     if (vi < 0) return SGEMM_ETOO_LARGE;
     const Variant &v = kVariants[vi].v;
     const int64_t tm = (int64_t(M) + v.BM - 1) / v.BM, tn = (int64_t(N) + v.BN - 1) / v.BN;
+    const int64_t slots = int64_t(cus) * v.wg_per_cu;
+    const int64_t grid = (v.persist && tm * tn > slots) ? slots : tm * tn;
     // operand bytes the tiles request: every A row panel once per tile column and every
     // B column panel once per tile row (before any cache reuse)
     const int64_t tile_bytes = 4 * (int64_t(M) * K * tn + int64_t(K) * N * tm);
     const int n = snprintf(buf, size_t(buflen),
                            "{\"variant\": %d, \"name\": \"%s\", \"BM\": %d, \"BN\": %d, "
                            "\"BK\": %d, \"waves\": [%d, %d], \"threads\": %d, \"grid\": %lld, "
-                           "\"tiles\": [%lld, %lld], \"load\": \"%s\", \"store\": \"%s\", "
-                           "\"cus\": %d, \"tile_request_bytes\": %lld}",
+                           "\"tiles\": [%lld, %lld], \"cus\": %d, \"tile_request_bytes\": %lld}",
                            vi, v.name, v.BM, v.BN, v.BK, v.wgm, v.wgn, kVariants[vi].threads,
-                           (long long)(tm * tn), (long long)tm, (long long)tn,
-                           v.vec ? "b128" : "b32", c_vec_ok(o) ? "vector" : "scalar", cus,
+                           (long long)grid, (long long)tm, (long long)tn, cus,
                            (long long)tile_bytes);
     if (n < 0 || n >= buflen) return SGEMM_EINVAL_ARG;
     return vi;

@@ -79,9 +79,5 @@ def run_kernel(kernel: str, M, N, K, A_view, lda, B_view, ldb, c: GuardedC, stre
         raise ValueError(kernel)
 
 
-def vec_variants():
-    return [i for i, n in enumerate(g.variant_names()) if n.endswith("_vec")]
-
-
 def all_variants():
     return list(range(len(g.variant_names())))

@@ -29,13 +29,8 @@ SHAPES = sorted({(s, 65, 33) for s in SIZES} | {(65, s, 33) for s in SIZES} |
                  (600, 7, 600), (513, 511, 68), (260, 260, 260)})
 
 
-def kernels_for(K, lda, ldb, aligned=True):
-    ks = ["auto", "naive", "tiled16", "tiled32"]
-    for v, name in enumerate(g.variant_names()):
-        if name.endswith("_vec") and (K % 4 or lda % 4 or ldb % 4 or not aligned):
-            continue
-        ks.append(f"v{v}")
-    return ks
+def kernels_for():
+    return ["auto", "naive", "tiled16", "tiled32"] + [f"v{v}" for v in range(len(g.variant_names()))]
 
 
 def exact_check(A, B, C, what):
@@ -48,13 +43,11 @@ def test_ragged_shapes_padded_and_guarded(gpu, M, N, K):
     rng = np.random.default_rng(M * 1000003 + N * 1009 + K)
     A = wl.draw(rng, (M, K), "int")
     B = wl.draw(rng, (K, N), "int")
-    # padded rows (NaN in the padding) and a padded, guarded C; the 16-byte variants get
-    # padding that keeps rows aligned
-    for lda, ldb, ldc in [(K + (4 if K % 4 == 0 else 3), N + (4 if N % 4 == 0 else 5), N + 2),
-                          (K, N, N)]:
+    # padded rows (NaN in the padding, odd leading dimensions) and a padded, guarded C
+    for lda, ldb, ldc in [(K + 3, N + 5, N + 2), (K, N, N)]:
         _, dA, _ = device_matrix(A, lda)
         _, dB, _ = device_matrix(B, ldb)
-        for kern in kernels_for(K, lda, ldb):
+        for kern in kernels_for():
             c = GuardedC(M, N, ldc)
             print(f"[edge] {M}x{N}x{K} lda={lda} ldb={ldb} ldc={ldc} {kern}", flush=True)
             run_kernel(kern, M, N, K, dA, lda, dB, ldb, c)
@@ -64,25 +57,19 @@ def test_ragged_shapes_padded_and_guarded(gpu, M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [(257, 129, 65), (64, 64, 64), (1, 1, 1), (300, 301, 302)])
 def test_misaligned_pointers(gpu, M, N, K):
-    """Bases one float past 16-byte alignment: the hot path must take its dword loader
-    and scalar stores; forcing a 16-byte variant is refused."""
+    """Bases one or three floats past 16-byte alignment: every kernel still works (the hot
+    kernel's 16-byte buffer loads and stores only need 4-byte alignment)."""
     rng = np.random.default_rng(7)
     A = wl.draw(rng, (M, K), "int")
     B = wl.draw(rng, (K, N), "int")
     _, dA, lda = device_matrix(A, offset=1)
     _, dB, ldb = device_matrix(B, offset=3)
-    for kern in kernels_for(K, lda, ldb, aligned=False):
+    for kern in kernels_for():
         c = GuardedC(M, N, offset=1)
         print(f"[edge] misaligned {M}x{N}x{K} {kern}", flush=True)
         run_kernel(kern, M, N, K, dA, lda, dB, ldb, c)
         gpu.cuda.synchronize()
         exact_check(A, B, c.result(), ("misaligned", kern))
-    for v, name in enumerate(g.variant_names()):
-        if name.endswith("_vec"):
-            c = GuardedC(M, N)
-            with pytest.raises(g.SgemmError) as e:
-                run_kernel(f"v{v}", M, N, K, dA, lda, dB, ldb, c)
-            assert e.value.status == -6
 
 
 @pytest.mark.parametrize("kern", ["auto", "naive", "tiled16", "tiled32", "v0"])
