@@ -34,6 +34,7 @@ if ROOT not in sys.path:
 
 PEAK_FP32_MFMA_TFLOPS = 157.3     # MI355X dense FP32 matrix peak
 PEAK_HBM_GBS = 8000.0             # MI355X HBM3E
+PEAK_FP32_VALU_TFLOPS = 78.6      # MI355X FP32 vector FMA without packed FP32
 KERNEL_SOURCES = ["fp32_gemm_f32_amd/csrc/kernel_mfma.hpp", "fp32_gemm_f32_amd/csrc/plan.hpp",
                   "fp32_gemm_f32_amd/csrc/sgemm_f32.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
@@ -105,6 +106,52 @@ def cpu_baseline(A, B, C_dev, M, N, K, seconds: float):
             "check_max_err": rep["max_err"], "check_nonfinite": rep["n_nonfinite"]}
 
 
+def bench_transpose(args) -> int:
+    """The LDS bank-geometry microbenchmark: out = A^T for the workload's A (M x K)."""
+    import torch
+
+    import fp32_gemm_f32_amd as g
+    import workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    rows, cols = w.M, w.K
+    tile, pad = int(args.kernel[9:11]), int(args.kernel[-1])
+    A, _ = wl.operands(args.workload)
+    dev = torch.device("cuda:0")
+    dA = torch.from_numpy(A).to(dev)
+    dT = torch.empty((cols, rows), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    lib = g.library()
+    call = (rows, cols, dA.data_ptr(), cols, dT.data_ptr(), rows, tile, pad, stream.cuda_stream)
+    for _ in range(args.warmup):
+        lib.sgemm_f32_lds_transpose(*call)
+    torch.cuda.synchronize(dev)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        rc = lib.sgemm_f32_lds_transpose(*call)
+        if rc:
+            raise g.SgemmError(rc, "sgemm_f32_lds_transpose")
+    end.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = start.elapsed_time(end) / args.steps
+    nbytes = 2.0 * 4 * rows * cols
+    gbs = nbytes / (ms / 1e3) / 1e9
+    log(f"bench: transpose {rows}x{cols} tile {tile} pad {pad}: {ms:.4f} ms, {gbs:.1f} GB/s")
+    print(json.dumps({
+        "metric": "LDS transpose GB/s (read + write)", "value": round(gbs, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": f"transpose of the {rows}x{cols} A operand of {w.name}",
+                   "tile": tile, "pad": pad},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+        "cpu_baseline": None}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,6 +159,12 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--variant", type=int, default=-1, help="force a hot-kernel tile variant")
+    ap.add_argument("--kernel", default="auto",
+                    choices=["auto", "naive", "tiled16", "tiled32", "tiled32p", "regtiled41",
+                             "regtiled44", "regtiled88", "transpose32p0", "transpose32p1",
+                             "transpose64p0", "transpose64p1"],
+                    help="the entry point a step calls (default: the hot path sgemm_f32); the "
+                         "transposes move an M x N matrix of the workload's A shape")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -125,6 +178,8 @@ def main() -> int:
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib, max(args.steps, 1))
         return 0
+    if args.kernel.startswith("transpose"):
+        return bench_transpose(args)
 
     import torch
 
@@ -149,11 +204,26 @@ def main() -> int:
     lib = g.library()
     call_args = (M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, dC.data_ptr(), N, sp)
 
+    kern = args.kernel
+    gemm = call_args[:-1]
+    if kern != "auto":
+        plan["name"] = {"naive": "naive", "tiled16": "lds_tiled_16", "tiled32": "lds_tiled_32",
+                        "tiled32p": "lds_tiled_32_padded", "regtiled41": "regtiled_4x1",
+                        "regtiled44": "regtiled_4x4", "regtiled88": "regtiled_8x8"}[kern]
+        plan["BM"] = plan["BN"] = plan["BK"] = plan["grid"] = None
+
     def step():
-        rc = (lib.sgemm_f32(*call_args) if args.variant < 0
-              else lib.sgemm_f32_variant(args.variant, *call_args))
+        if kern == "auto":
+            rc = (lib.sgemm_f32(*call_args) if args.variant < 0
+                  else lib.sgemm_f32_variant(args.variant, *call_args))
+        elif kern == "naive":
+            rc = lib.sgemm_f32_naive(*call_args)
+        elif kern.startswith("tiled"):
+            rc = lib.sgemm_f32_tiled(*gemm, int(kern[5:7]), 1 if kern.endswith("p") else 0, sp)
+        else:
+            rc = lib.sgemm_f32_regtiled(*gemm, int(kern[8]), int(kern[9]), sp)
         if rc != 0:
-            raise g.SgemmError(rc, "sgemm_f32")
+            raise g.SgemmError(rc, kern)
 
     for _ in range(args.warmup):
         step()
@@ -177,7 +247,13 @@ def main() -> int:
     compulsory = 4.0 * (M * K + K * N + M * N)
     t_mfma = flop / (PEAK_FP32_MFMA_TFLOPS * 1e12)
     t_hbm = compulsory / (PEAK_HBM_GBS * 1e9)
-    if t_mfma >= t_hbm:
+    if kern != "auto":
+        # the scalar rungs run on the vector ALUs without packed FP32: 256 CUs x 4 SIMDs x
+        # 16 lanes x 2 FLOP x 2.4 GHz
+        achieved = flop / (ms / 1e3) / 1e12
+        roof = {"bound": "alu", "achieved": round(achieved, 3), "peak": PEAK_FP32_VALU_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_VALU_TFLOPS, 4)}
+    elif t_mfma >= t_hbm:
         achieved = flop / (ms / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_FP32_MFMA_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4)}
@@ -185,7 +261,7 @@ def main() -> int:
         achieved = compulsory / (ms / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    roof["traffic"] = measured_traffic(args.workload)
+    roof["traffic"] = measured_traffic(args.workload) if kern == "auto" else None
     roof["kernel"] = plan["name"]
 
     cpu = None

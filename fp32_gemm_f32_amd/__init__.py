@@ -7,6 +7,8 @@ if the library is not built, importing the binding's functions raises.
 Raw layer (same names and arguments as the C ABI; pointers are integers):
     sgemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream=0)
     sgemm_f32_naive(...), sgemm_f32_tiled(..., tile=32, pad=0, stream=0)
+    sgemm_f32_regtiled(..., tm=4, tn=4, stream=0)
+    sgemm_f32_lds_transpose(rows, cols, src, ldi, dst, ldo, tile=32, pad=0, stream=0)
     sgemm_f32_variant(variant, M, N, K, A, lda, B, ldb, C, ldc, stream=0)
     sgemm_f32_plan_describe(M, N, K, A, lda, B, ldb, C, ldc, num_cus=0) -> dict
 Tensor layer (torch tensors on the GPU, launched on torch's current stream):
@@ -51,6 +53,10 @@ def _load():
         lib.sgemm_f32_naive.restype = i
         lib.sgemm_f32_tiled.argtypes = gemm + [i, i, p]
         lib.sgemm_f32_tiled.restype = i
+        lib.sgemm_f32_regtiled.argtypes = gemm + [i, i, p]
+        lib.sgemm_f32_regtiled.restype = i
+        lib.sgemm_f32_lds_transpose.argtypes = [i, i, p, i, p, i, i, i, p]
+        lib.sgemm_f32_lds_transpose.restype = i
         lib.sgemm_f32_variant.argtypes = [i] + gemm + [p]
         lib.sgemm_f32_variant.restype = i
         lib.sgemm_f32_variant_count.argtypes = []
@@ -93,6 +99,16 @@ def sgemm_f32_tiled(M, N, K, A, lda, B, ldb, C, ldc, tile=32, pad=0, stream=0) -
            "sgemm_f32_tiled")
 
 
+def sgemm_f32_regtiled(M, N, K, A, lda, B, ldb, C, ldc, tm=4, tn=4, stream=0) -> None:
+    _check(_load().sgemm_f32_regtiled(M, N, K, A, lda, B, ldb, C, ldc, tm, tn, stream or None),
+           "sgemm_f32_regtiled")
+
+
+def sgemm_f32_lds_transpose(rows, cols, src, ldi, dst, ldo, tile=32, pad=0, stream=0) -> None:
+    _check(_load().sgemm_f32_lds_transpose(rows, cols, src, ldi, dst, ldo, tile, pad,
+                                           stream or None), "sgemm_f32_lds_transpose")
+
+
 def sgemm_f32_variant(variant, M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> None:
     _check(_load().sgemm_f32_variant(variant, M, N, K, A, lda, B, ldb, C, ldc, stream or None),
            "sgemm_f32_variant")
@@ -131,11 +147,11 @@ def _ld(t) -> int:
     return max(t.stride(0), t.shape[1], 1)
 
 
-def matmul(A, B, out=None, kernel: str = "auto", variant: int = -1, tile: int = 32,
-           pad: int = 0):
+def matmul(A, B, out=None, kernel: str = "auto", variant: int = -1, tile=32, pad: int = 0):
     """C = A x B for float32 CUDA/HIP tensors, on torch's current stream.
 
-    kernel: "auto" (the hot path, or the given variant), "naive" or "tiled".
+    kernel: "auto" (the hot path, or the given variant), "naive", "tiled" or "regtiled"
+    (tile = (tm, tn) for the latter).
     """
     import torch
 
@@ -163,6 +179,9 @@ def matmul(A, B, out=None, kernel: str = "auto", variant: int = -1, tile: int = 
             sgemm_f32_naive(*args, stream=stream)
         elif kernel == "tiled":
             sgemm_f32_tiled(*args, tile=tile, pad=pad, stream=stream)
+        elif kernel == "regtiled":
+            tm, tn = tile if isinstance(tile, tuple) else (4, 4)
+            sgemm_f32_regtiled(*args, tm=tm, tn=tn, stream=stream)
         else:
             raise ValueError(f"unknown kernel {kernel!r}")
     return out

@@ -14,6 +14,7 @@
 #include "sgemm_f32.h"
 #include "sgemm_validate.hpp"
 #include "kernels_simple.hpp"
+#include "kernels_ladder.hpp"
 #include "kernel_mfma.hpp"
 #include "plan.hpp"
 
@@ -190,6 +191,50 @@ extern "C" int sgemm_f32_tiled(int M, int N, int K, const float *A, int lda, con
                         C, ldc)
                : launch(k_sgemm_lds_tiled<32, 0>, grid, block, stream, M, N, K, A, lda, B, ldb,
                         C, ldc);
+}
+
+extern "C" int sgemm_f32_regtiled(int M, int N, int K, const float *A, int lda, const float *B,
+                                  int ldb, float *C, int ldc, int tm, int tn, void *stream)
+{
+    const int st = validate(M, N, K, A, lda, B, ldb, C, ldc);
+    if (st != SGEMM_OK) return st;
+    const bool t41 = tm == 4 && tn == 1, t44 = tm == 4 && tn == 4, t88 = tm == 8 && tn == 8;
+    if (!t41 && !t44 && !t88) return SGEMM_EINVAL_ARG;
+    if (M == 0 || N == 0) return SGEMM_OK;
+    if (K == 0) return fill_zero(M, N, C, ldc, stream);
+    const int bm = t88 ? 128 : 64, bn = t88 ? 128 : 64;
+    const int64_t gy = (int64_t(M) + bm - 1) / bm;
+    if (gy > int64_t(kMaxGridY)) return SGEMM_ETOO_LARGE;
+    const dim3 grid(unsigned((N + bn - 1) / bn), unsigned(gy));
+    if (t41)
+        return launch(k_sgemm_regtile<64, 64, 8, 4, 1>, grid, dim3(16 * 64), stream, M, N, K, A,
+                      lda, B, ldb, C, ldc);
+    if (t44)
+        return launch(k_sgemm_regtile<64, 64, 8, 4, 4>, grid, dim3(16 * 16), stream, M, N, K, A,
+                      lda, B, ldb, C, ldc);
+    return launch(k_sgemm_regtile<128, 128, 8, 8, 8>, grid, dim3(16 * 16), stream, M, N, K, A,
+                  lda, B, ldb, C, ldc);
+}
+
+extern "C" int sgemm_f32_lds_transpose(int rows, int cols, const float *in, int ldi, float *out,
+                                       int ldo, int tile, int pad, void *stream)
+{
+    if (rows < 0 || cols < 0) return SGEMM_EINVAL_DIM;
+    if (ldi < (cols > 1 ? cols : 1) || ldo < (rows > 1 ? rows : 1)) return SGEMM_EINVAL_LD;
+    const int64_t si = span_elems(rows, cols, ldi), so = span_elems(cols, rows, ldo);
+    if (bad_ptr(in, si) || bad_ptr(out, so)) return SGEMM_EINVAL_PTR;
+    if (overlap(out, so, in, si)) return SGEMM_EALIAS;
+    if ((tile != 32 && tile != 64) || (pad != 0 && pad != 1)) return SGEMM_EINVAL_ARG;
+    if (rows == 0 || cols == 0) return SGEMM_OK;
+    const int64_t gy = (int64_t(rows) + tile - 1) / tile;
+    if (gy > int64_t(kMaxGridY)) return SGEMM_ETOO_LARGE;
+    const dim3 grid(unsigned((cols + tile - 1) / tile), unsigned(gy));
+    const dim3 block(tile * tile / 4);
+    if (tile == 32)
+        return pad ? launch(k_lds_transpose<32, 1>, grid, block, stream, rows, cols, in, ldi, out, ldo)
+                   : launch(k_lds_transpose<32, 0>, grid, block, stream, rows, cols, in, ldi, out, ldo);
+    return pad ? launch(k_lds_transpose<64, 1>, grid, block, stream, rows, cols, in, ldi, out, ldo)
+               : launch(k_lds_transpose<64, 0>, grid, block, stream, rows, cols, in, ldi, out, ldo);
 }
 
 extern "C" int sgemm_f32_variant_count(void) { return kNumVariants; }

@@ -53,7 +53,9 @@ typedef enum {
  * The hot path: the LDS-tiled, register-tiled matrix-core kernel ("SGEMM: 2D Register
  * Tiling Visualizer", "Why 2D Register Tiling Dominates", carried onto the FP32 MFMA
  * instructions), with tiles zero-filled past the edges of ragged shapes. The tile shape
- * is chosen per (M, N, K), pointer alignment and compute-unit count.
+ * is chosen per (M, N, K) and compute-unit count; any 4-byte aligned pointers and any
+ * leading dimensions work. Leading dimensions so large that 256 rows of A or C (or 32
+ * rows of B) exceed 2^31 bytes return SGEMM_ETOO_LARGE.
  */
 int sgemm_f32(int M, int N, int K,
               const float *A, int lda,
@@ -88,10 +90,41 @@ int sgemm_f32_tiled(int M, int N, int K,
                     void *stream);
 
 /*
+ * Scalar register tiling ("SGEMM: 2D Register Tiling Visualizer", code panel and "Why 2D
+ * Register Tiling Dominates"): each thread keeps a tm x tn block of C in registers and,
+ * per k, loads tm values of A and tn values of B from LDS for tm*tn FMAs. (tm, tn) is
+ * (4, 1) (the page's 1-D strip), (4, 4) or (8, 8); anything else is SGEMM_EINVAL_ARG.
+ * A measurable rung of the pages' ladder, on the vector ALUs rather than the matrix cores.
+ * Shapes with more than 65535 row tiles (64 rows, 128 for 8 x 8) return SGEMM_ETOO_LARGE.
+ */
+int sgemm_f32_regtiled(int M, int N, int K,
+                       const float *A, int lda,
+                       const float *B, int ldb,
+                       float *C, int ldc,
+                       int tm, int tn,
+                       void *stream);
+
+/*
+ * LDS bank-geometry microbenchmark: out[j*ldo + i] = in[i*ldi + j] for i < rows, j < cols,
+ * through a tile x tile LDS tile written by rows and read by columns, with rows padded by
+ * `pad` words ("Visual walkthrough - Memory hierarchy", Step 6; "Shared Memory Tiling",
+ * "Conflict-free layout"). tile is 32 or 64, pad 0 or 1. in and out are device pointers
+ * (rows x cols and cols x rows, row-major); validation mirrors the GEMM entry points
+ * (ldi >= max(1, cols), ldo >= max(1, rows), out must not overlap in). More than 65535
+ * row tiles returns SGEMM_ETOO_LARGE.
+ */
+int sgemm_f32_lds_transpose(int rows, int cols,
+                            const float *in, int ldi,
+                            float *out, int ldo,
+                            int tile, int pad,
+                            void *stream);
+
+/*
  * The hot kernel with a fixed tile variant instead of the automatic choice (for tests
  * and tuning). variant < 0 is the automatic choice (same as sgemm_f32); otherwise an
- * index below sgemm_f32_variant_count(). A variant whose load path needs 16-byte
- * aligned rows returns SGEMM_EINVAL_ARG when the operands do not allow it.
+ * index below sgemm_f32_variant_count(), else SGEMM_EINVAL_ARG. A variant whose 31-bit
+ * buffer offsets cannot span one workgroup's rows of A or C or one K-panel of B returns
+ * SGEMM_ETOO_LARGE.
  */
 int sgemm_f32_variant(int variant, int M, int N, int K,
                       const float *A, int lda,
@@ -109,7 +142,7 @@ const char *sgemm_f32_status_string(int status);
 /*
  * Writes a one-line JSON description of the plan sgemm_f32 would run for these
  * arguments into buf (at most buflen bytes including the NUL): variant, tile shape,
- * grid, load path and the operand bytes the tiles request. Pointers are used for their
+ * grid and the operand bytes the tiles request. Pointers are used for their
  * alignment only and are never dereferenced. num_cus > 0 plans for that many compute
  * units; num_cus <= 0 queries the current device (SGEMM_ELAUNCH if none). Returns the
  * variant index (>= 0), or a negative sgemm_status (buffer too small: SGEMM_EINVAL_ARG).

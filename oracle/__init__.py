@@ -52,6 +52,8 @@ def _bind(lib):
     lib.oracle_check.restype = ctypes.c_int
     lib.oracle_sample.argtypes = [i64, i64, i64, dp, i64, dp, i64, i64, dp, dp, dp, dp]
     lib.oracle_sample.restype = ctypes.c_int
+    lib.oracle_transpose.argtypes = [i64, i64, dp, i64, dp, i64]
+    lib.oracle_transpose.restype = ctypes.c_int
     lib.oracle_threads.argtypes = []
     lib.oracle_threads.restype = ctypes.c_int
     return lib
@@ -132,6 +134,17 @@ def sample(A: np.ndarray, B: np.ndarray, ii, jj, lib=None):
     if rc:
         raise RuntimeError(f"oracle_sample failed ({rc})")
     return ref, den
+
+
+def transpose(X: np.ndarray, lib=None) -> np.ndarray:
+    """out = X^T (the LDS microbenchmark's result), as a new packed array."""
+    lib = lib or load()
+    rows, cols = X.shape
+    out = np.empty((cols, rows), dtype=np.float32)
+    rc = lib.oracle_transpose(rows, cols, _ptr(X), _ld(X), _ptr(out), max(rows, 1))
+    if rc:
+        raise RuntimeError(f"oracle_transpose failed ({rc})")
+    return out
 
 
 def threads(lib=None) -> int:

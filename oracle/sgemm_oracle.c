@@ -192,6 +192,19 @@ int oracle_sample(int64_t M, int64_t N, int64_t K,
     return 0;
 }
 
+/*
+ * The transpose that the LDS bank-geometry microbenchmark computes ("Visual walkthrough -
+ * Memory hierarchy", Step 6): out[j][i] = in[i][j]. A copy, so exact.
+ */
+int oracle_transpose(int64_t rows, int64_t cols, const float *in, int64_t ldi,
+                     float *out, int64_t ldo)
+{
+    if (rows < 0 || cols < 0) return -1;
+    for (int64_t i = 0; i < rows; ++i)
+        for (int64_t j = 0; j < cols; ++j) out[j * ldo + i] = in[i * ldi + j];
+    return 0;
+}
+
 /* Threads an OpenMP region of the oracle uses (1 when built without OpenMP). */
 int oracle_threads(void)
 {

@@ -234,7 +234,25 @@ def pin_sample(lib):
     assert np.array_equal(ref, exact.ravel()), "sample on integer brute force"
 
 
+def pin_transpose(lib):
+    """The transpose oracle: a hand-written 2 x 3 case, involution, and (AB)^T = B^T A^T
+    through the GEMM oracle on integers."""
+    X = np.array([[1, 2, 3], [4, 5, 6]], np.float32)
+    assert np.array_equal(oracle.transpose(X, lib=lib), np.array([[1, 4], [2, 5], [3, 6]], np.float32))
+    rng = np.random.default_rng(22)
+    Y = rng.standard_normal((37, 19)).astype(np.float32)
+    assert np.array_equal(oracle.transpose(oracle.transpose(Y, lib=lib), lib=lib), Y)
+    A = _ints(rng, (5, 7))
+    B = _ints(rng, (7, 4))
+    AB = oracle.gemm_f64(A, B, lib=lib).astype(np.float32)
+    BtAt = oracle.gemm_f64(oracle.transpose(B, lib=lib), oracle.transpose(A, lib=lib), lib=lib)
+    assert np.array_equal(oracle.transpose(AB, lib=lib), BtAt.astype(np.float32))
+    Z = np.full((3, 8), np.nan, np.float32)
+    Z[:, :5] = 1
+    assert np.array_equal(oracle.transpose(Z[:, :5], lib=lib), np.ones((5, 3), np.float32))
+
+
 ALL_PINS = [pin_identity, pin_permutation, pin_all_ones, pin_rank_one,
             pin_worked_shapes_exact, pin_transpose_identity, pin_k_split,
             pin_rational_bound, pin_numpy_matmul, pin_leading_dimensions,
-            pin_check_exact, pin_sample]
+            pin_check_exact, pin_sample, pin_transpose]

@@ -116,3 +116,24 @@ def test_plan(shape, expect_tile):
 def test_plan_buffer_too_small():
     buf = ctypes.create_string_buffer(8)
     assert g.library().sgemm_f32_plan_describe(64, 64, 64, P, 64, P, 64, P, 64, 256, buf, 8) == -6
+
+
+def test_regtiled_validation():
+    args = (8, 8, 8, P, 8, P + 4096, 8, P + 8192, 8)
+    for tm, tn in [(2, 2), (4, 2), (8, 4), (1, 4), (0, 0)]:
+        assert call("sgemm_f32_regtiled", *args, tm, tn, None) == -6
+    assert call("sgemm_f32_regtiled", -1, 8, 8, P, 8, P + 4096, 8, P + 8192, 8, 4, 4, None) == -1
+    assert call("sgemm_f32_regtiled", 8, 8, 8, P, 8, P + 4096, 8, P + 16, 8, 4, 1, None) == -4
+    assert call("sgemm_f32_regtiled", 0, 8, 8, P, 8, P + 4096, 8, P + 8192, 8, 8, 8, None) == 0
+
+
+def test_lds_transpose_validation():
+    t = lambda *a: call("sgemm_f32_lds_transpose", *a)
+    assert t(-1, 4, P, 4, P + 4096, 4, 32, 0, None) == -1
+    assert t(4, 5, P, 4, P + 4096, 4, 32, 0, None) == -2     # ldi < cols
+    assert t(5, 4, P, 4, P + 4096, 4, 32, 0, None) == -2     # ldo < rows
+    assert t(4, 4, None, 4, P + 4096, 4, 32, 0, None) == -3
+    assert t(4, 4, P, 4, P + 8, 4, 32, 0, None) == -4        # out overlaps in
+    assert t(4, 4, P, 4, P + 4096, 4, 16, 0, None) == -6
+    assert t(4, 4, P, 4, P + 4096, 4, 64, 2, None) == -6
+    assert t(0, 4, P, 4, P + 4096, 1, 64, 1, None) == 0

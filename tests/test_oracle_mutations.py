@@ -40,6 +40,7 @@ MUTANTS = [
     ("check_nan_passes", "if (!isfinite(c)) {", "if (0) {", 0),
     ("sample_wrong_B_index", "(double)B[k * ldb + jj[t]]", "(double)B[jj[t] * ldb + k]", 0),
     ("sample_den_signed", "d += fabs(p);", "d += p;", 0),
+    ("transpose_not_transposed", "out[j * ldo + i] = in[i * ldi + j];", "out[i * ldo + j] = in[i * ldi + j];", 0),
 ]
 
 
