@@ -7,6 +7,8 @@ if the library is not built, importing the binding's functions raises.
 Raw layer (same names and arguments as the C ABI; pointers are integers):
     sgemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream=0)
     sgemm_f32_naive(...), sgemm_f32_tiled(..., tile=32, pad=0, stream=0)
+    sgemm_f32_splitk(..., splits, workspace, workspace_bytes, stream=0)
+    sgemm_f32_splitk_workspace_size(M, N, K, splits) -> int
     sgemm_f32_regtiled(..., tm=4, tn=4, stream=0)
     sgemm_f32_lds_transpose(rows, cols, src, ldi, dst, ldo, tile=32, pad=0, stream=0)
     sgemm_f32_variant(variant, M, N, K, A, lda, B, ldb, C, ldc, stream=0)
@@ -53,6 +55,10 @@ def _load():
         lib.sgemm_f32_naive.restype = i
         lib.sgemm_f32_tiled.argtypes = gemm + [i, i, p]
         lib.sgemm_f32_tiled.restype = i
+        lib.sgemm_f32_splitk.argtypes = gemm + [i, p, ctypes.c_size_t, p]
+        lib.sgemm_f32_splitk.restype = i
+        lib.sgemm_f32_splitk_workspace_size.argtypes = [i, i, i, i]
+        lib.sgemm_f32_splitk_workspace_size.restype = ctypes.c_size_t
         lib.sgemm_f32_regtiled.argtypes = gemm + [i, i, p]
         lib.sgemm_f32_regtiled.restype = i
         lib.sgemm_f32_lds_transpose.argtypes = [i, i, p, i, p, i, i, i, p]
@@ -97,6 +103,16 @@ def sgemm_f32_naive(M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> None:
 def sgemm_f32_tiled(M, N, K, A, lda, B, ldb, C, ldc, tile=32, pad=0, stream=0) -> None:
     _check(_load().sgemm_f32_tiled(M, N, K, A, lda, B, ldb, C, ldc, tile, pad, stream or None),
            "sgemm_f32_tiled")
+
+
+def sgemm_f32_splitk(M, N, K, A, lda, B, ldb, C, ldc, splits, workspace, workspace_bytes,
+                     stream=0) -> None:
+    _check(_load().sgemm_f32_splitk(M, N, K, A, lda, B, ldb, C, ldc, splits, workspace or None,
+                                    workspace_bytes, stream or None), "sgemm_f32_splitk")
+
+
+def sgemm_f32_splitk_workspace_size(M, N, K, splits) -> int:
+    return _load().sgemm_f32_splitk_workspace_size(M, N, K, splits)
 
 
 def sgemm_f32_regtiled(M, N, K, A, lda, B, ldb, C, ldc, tm=4, tn=4, stream=0) -> None:
@@ -150,8 +166,9 @@ def _ld(t) -> int:
 def matmul(A, B, out=None, kernel: str = "auto", variant: int = -1, tile=32, pad: int = 0):
     """C = A x B for float32 CUDA/HIP tensors, on torch's current stream.
 
-    kernel: "auto" (the hot path, or the given variant), "naive", "tiled" or "regtiled"
-    (tile = (tm, tn) for the latter).
+    kernel: "auto" (the hot path, or the given variant), "naive", "tiled", "regtiled"
+    (tile = (tm, tn)) or "splitk" (variant = number of splits, -1 for automatic; the
+    workspace is a torch allocation made here).
     """
     import torch
 
@@ -179,6 +196,11 @@ def matmul(A, B, out=None, kernel: str = "auto", variant: int = -1, tile=32, pad
             sgemm_f32_naive(*args, stream=stream)
         elif kernel == "tiled":
             sgemm_f32_tiled(*args, tile=tile, pad=pad, stream=stream)
+        elif kernel == "splitk":
+            splits = variant if variant >= 0 else 0
+            ws_bytes = sgemm_f32_splitk_workspace_size(M, N, K, splits)
+            ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device=A.device)
+            sgemm_f32_splitk(*args, splits, ws.data_ptr(), ws_bytes, stream=stream)
         elif kernel == "regtiled":
             tm, tn = tile if isinstance(tile, tuple) else (4, 4)
             sgemm_f32_regtiled(*args, tm=tm, tn=tn, stream=stream)

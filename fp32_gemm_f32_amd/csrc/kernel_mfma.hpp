@@ -101,6 +101,11 @@ struct GemmArgs {
     int64_t b_bytes;   // bytes from B to the end of its last row
     int M, N, K, lda, ldb, ldc;
     int tiles_m, tiles_n;
+    // Split-K: item i of the tiles_m * tiles_n * splits work items is tile i % tiles over
+    // k in [s * k_chunk, min(K, (s + 1) * k_chunk)) with s = i / tiles, written to
+    // C + s * c_split_stride. splits = 1, k_chunk = K is the plain product.
+    int splits, k_chunk;
+    int64_t c_split_stride;
     int64_t c_bytes;   // bytes from C to the end of its last row
 };
 
@@ -216,6 +221,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_sgemm_mfma(GemmArgs p)
 
     const int M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
     const int ntiles = p.tiles_m * p.tiles_n;
+    const int nitems = ntiles * p.splits;
 
     // ---- per-thread load assignment ----
     // Thread tid stages A chunks c = tid + i*NT, i.e. rows a_r0 + i*A_RSTEP at the fixed
@@ -235,19 +241,26 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_sgemm_mfma(GemmArgs p)
     const uint32_t b_stride = uint32_t(B_KSTEP) * uint32_t(ldb) * 4u;
     const int b_lds0 = b_k0 * BN + b_c0;
 
-    // The tile whose panels are being loaded (it runs one tile ahead of the tile being
-    // computed during the last panel of each tile).
-    int lm0 = 0, ln0 = 0;
+    // The item whose panels are being loaded (it runs one item ahead of the item being
+    // computed during the last panel of each item): tile origin lm0, ln0, K range
+    // [lkb, lkb + lK) and split index ls.
+    int lm0 = 0, ln0 = 0, lkb = 0, lK = 0, ls = 0;
     bool b_col_ok = false;
     auto set_load_tile = [&](int vb) {
-        if (vb < ntiles) {
+        if (vb < nitems) {
             int tm, tn;
-            tile_coords(vb, p.tiles_m, p.tiles_n, tm, tn);
+            ls = vb / ntiles;
+            tile_coords(vb - ls * ntiles, p.tiles_m, p.tiles_n, tm, tn);
             lm0 = tm * BM;
             ln0 = tn * BN;
-        } else {   // no such tile: rows and columns past the matrix, all loads masked
+            lkb = ls * p.k_chunk;
+            lK = min(K - lkb, p.k_chunk);
+        } else {   // no such item: rows, columns and k past the matrix, all loads masked
             lm0 = M;
             ln0 = N;
+            lkb = 0;
+            lK = 0;
+            ls = 0;
         }
         b_col_ok = ln0 + b_c0 < N;
     };
@@ -259,7 +272,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_sgemm_mfma(GemmArgs p)
 
     auto set_panel = [&](int k0) {
         k_load = k0;
-        const int64_t ea = int64_t(lm0) * lda + k0, eb = int64_t(k0) * ldb + ln0;
+        const int64_t ea = int64_t(lm0) * lda + lkb + k0, eb = int64_t(lkb + k0) * ldb + ln0;
         rsa = make_rsrc(p.A + ea, p.a_bytes - ea * 4);
         rsb = make_rsrc(p.B + eb, p.b_bytes - eb * 4);
     };
@@ -267,16 +280,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_sgemm_mfma(GemmArgs p)
     auto load_slot = [&](int l) {
         if (l < A_CH) {
             const int kc = k_load + 4 * a_q;
-            const bool ok = lm0 + a_r0 + l * A_RSTEP < M && kc < K;
+            const bool ok = lm0 + a_r0 + l * A_RSTEP < M && kc < lK;
             f32x4 v = load_b128(rsa, ok ? a_off0 + uint32_t(l) * a_stride : kOob);
             // a chunk that crosses K: its elements past K belong to the row padding or the
             // next row; zero them (a select, so a NaN there cannot leak)
 #pragma unroll
-            for (int e = 1; e < 4; ++e) v[e] = kc + e < K ? v[e] : 0.0f;
+            for (int e = 1; e < 4; ++e) v[e] = kc + e < lK ? v[e] : 0.0f;
             ra[l] = v;
         } else {
             const int i = l - A_CH;
-            const bool ok = k_load + b_k0 + i * B_KSTEP < K && b_col_ok;
+            const bool ok = k_load + b_k0 + i * B_KSTEP < lK && b_col_ok;
             // columns past N inside a chunk only reach accumulators that are never stored
             rb[i] = load_b128(rsb, ok ? b_off0 + uint32_t(i) * b_stride : kOob);
         }
@@ -412,7 +425,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_sgemm_mfma(GemmArgs p)
 
     // ---- epilogue of one tile: accumulators to C through a buffer resource ----
     const int ldc = p.ldc;
-    auto epilogue = [&](int m0, int n0) {
+    auto epilogue = [&](int m0, int n0, int split) {
 #pragma unroll
         for (int h = 1; h < KACC; ++h)
 #pragma unroll
@@ -424,7 +437,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_sgemm_mfma(GemmArgs p)
         // the scalar offset; rows past M and chunks that cross N get voffset kOob (the
         // hardware drops those stores), and only a tile on the N edge stores the partial
         // chunks element by element.
-        const int64_t ec = int64_t(m0) * ldc + n0;
+        const int64_t ec = split * p.c_split_stride + int64_t(m0) * ldc + n0;
         const __amdgpu_buffer_rsrc_t rsc = make_rsrc(p.C + ec, p.c_bytes - ec * 4);
         const uint32_t ldc4 = uint32_t(ldc) * 4u;
         const int rows_left = M - m0, cols_left = N - n0;
@@ -473,8 +486,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_sgemm_mfma(GemmArgs p)
         }
     };
 
-    // ---- K loop over the workgroup's tiles ----
-    const int panels = (K + BK - 1) / BK;
+    // ---- K loop over the workgroup's items ----
     int vb = blockIdx.x;
     set_load_tile(vb);
     set_panel(0);
@@ -487,23 +499,25 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_sgemm_mfma(GemmArgs p)
     read_b(smem + T::A_TILE, 0, b[0]);
 
     if constexpr (!PERSIST) {
-        // one tile per workgroup: the last panel stages nothing
+        // one item per workgroup: the last panel stages nothing
+        const int panels = (lK + BK - 1) / BK;
         for (int pnl = 0; pnl + 1 < panels; ++pnl) {
             set_panel((pnl + 1) * BK);
             panel(pnl & 1, std::true_type{});
         }
         panel((panels - 1) & 1, std::false_type{});
-        epilogue(lm0, ln0);
+        epilogue(lm0, ln0, ls);
     } else {
-        // Tiles vb, vb + G, vb + 2G, ...: the last panel of a tile stages panel 0 of the
-        // workgroup's next tile, so that tile's first loads and LDS writes run under the
-        // current tile's MFMAs and the epilogue's stores drain while the next tile
-        // computes. After the last tile the staged "next tile" lies past the matrix and
+        // Items vb, vb + G, vb + 2G, ...: the last panel of an item stages panel 0 of the
+        // workgroup's next item, so that item's first loads and LDS writes run under the
+        // current item's MFMAs and the epilogue's stores drain while the next item
+        // computes. After the last item the staged "next item" lies past the matrix and
         // every one of its loads is masked to zero; one panel body serves every panel.
         const int G = gridDim.x;
         int cur = 0;
-        int cm0 = lm0, cn0 = ln0;   // the tile being computed
         for (;;) {
+            const int cm0 = lm0, cn0 = ln0, cs = ls;   // the item being computed
+            const int panels = (lK + BK - 1) / BK;
             for (int pnl = 0; pnl < panels; ++pnl) {
                 const bool last = pnl + 1 == panels;
                 if (last) set_load_tile(vb + G);
@@ -511,13 +525,26 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_sgemm_mfma(GemmArgs p)
                 panel(cur, std::true_type{});
                 cur ^= 1;
             }
-            epilogue(cm0, cn0);
+            epilogue(cm0, cn0, cs);
             vb += G;
-            if (vb >= ntiles) break;
+            if (vb >= nitems) break;
             zero_acc();
-            cm0 = lm0;
-            cn0 = ln0;
         }
+    }
+}
+
+// C[i][j] = sum over s of W[s * stride + i * N + j], in ascending s: the second pass of
+// split-K (a fixed summation order, so repeated runs give identical bits).
+__global__ __launch_bounds__(256) void k_splitk_reduce(int M, int N, int splits,
+                                                      const float *__restrict__ W, int64_t stride,
+                                                      float *__restrict__ C, int ldc)
+{
+    const int64_t total = int64_t(M) * N;
+    for (int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
+         e += int64_t(gridDim.x) * blockDim.x) {
+        float v = W[e];
+        for (int s = 1; s < splits; ++s) v += W[s * stride + e];
+        C[(e / N) * ldc + e % N] = v;
     }
 }
 

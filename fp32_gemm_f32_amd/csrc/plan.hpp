@@ -25,6 +25,7 @@ struct Variant {
 
 struct Operands {
     int M, N, K, lda, ldb, ldc;
+    int splits = 1;         // split-K: each tile's K range is cut into this many items
 };
 
 // Buffer offsets inside one workgroup's rows of A and C and one panel of B must stay
@@ -51,8 +52,8 @@ inline double variant_cost(const Variant &v, const Operands &o, int cus)
     const int64_t tn = (int64_t(o.N) + v.BN - 1) / v.BN;
     // the busiest CU runs ceil(tiles / CUs) tiles; each is BM*BN*K multiply-adds at the
     // variant's measured relative rate plus the per-tile overhead
-    const int64_t per_cu = (tm * tn + cus - 1) / cus;
-    const double k = o.K > 0 ? o.K : 1;
+    const int64_t per_cu = (tm * tn * o.splits + cus - 1) / cus;
+    const double k = o.K > 0 ? double(o.K) / o.splits : 1;
     return double(per_cu) * double(v.BM) * v.BN *
            (k / v.rate + (v.persist ? kTileOverheadKPersistent : kTileOverheadK));
 }

@@ -116,11 +116,72 @@ int run_variant(int vi, const Operands &o, const float *A, const float *B, float
     p.M = o.M; p.N = o.N; p.K = o.K; p.lda = o.lda; p.ldb = o.ldb; p.ldc = o.ldc;
     p.tiles_m = (o.M + e.v.BM - 1) / e.v.BM;
     p.tiles_n = (o.N + e.v.BN - 1) / e.v.BN;
+    p.splits = 1;
+    p.k_chunk = o.K;
+    p.c_split_stride = 0;
     const int64_t tiles = int64_t(p.tiles_m) * p.tiles_n;
     if (tiles > INT32_MAX) return SGEMM_ETOO_LARGE;
     const int64_t slots = int64_t(cus) * e.v.wg_per_cu;
     const int64_t grid = (e.v.persist && tiles > slots) ? slots : tiles;
     return launch(e.kern, dim3(unsigned(grid)), dim3(e.threads), stream, p);
+}
+
+// Split-K geometry: K is cut into `splits` ranges of whole BK panels (the last may be
+// shorter); returns the number of non-empty ranges and the range length.
+void splitk_geometry(int K, int BK, int splits, int *eff, int *k_chunk)
+{
+    const int panels = (K + BK - 1) / BK;
+    const int per = (panels + splits - 1) / splits;
+    *k_chunk = per * BK;
+    *eff = (K + *k_chunk - 1) / *k_chunk;
+}
+
+// Splits chosen automatically: enough items to give every CU about two, each range at
+// least four panels long, at most kMaxSplits.
+constexpr int kMaxSplits = 32;
+int auto_splits(const Operands &o, int cus)
+{
+    const int64_t tiles = ((int64_t(o.M) + 63) / 64) * ((int64_t(o.N) + 63) / 64);
+    int64_t s = (2 * int64_t(cus) + tiles - 1) / tiles;
+    const int64_t by_k = o.K / (4 * 64);
+    if (s > by_k) s = by_k;
+    if (s > kMaxSplits) s = kMaxSplits;
+    return s < 1 ? 1 : int(s);
+}
+
+int run_splitk(int splits, const Operands &o0, const float *A, const float *B, float *C,
+               float *W, size_t w_bytes, void *stream, int cus)
+{
+    Operands o = o0;
+    o.splits = splits;
+    const int vi = choose_variant(g_table, o, cus);
+    if (vi < 0) return SGEMM_ETOO_LARGE;
+    const VariantEntry &e = kVariants[vi];
+    int eff = 0, k_chunk = 0;
+    splitk_geometry(o.K, e.v.BK, splits, &eff, &k_chunk);
+    const int64_t mn = int64_t(o.M) * o.N;
+    if (w_bytes < size_t(eff) * size_t(mn) * 4u) return SGEMM_EINVAL_ARG;
+    GemmArgs p;
+    p.A = A; p.B = B; p.C = W;
+    p.a_bytes = span_elems(o.M, o.K, o.lda) * 4;
+    p.b_bytes = span_elems(o.K, o.N, o.ldb) * 4;
+    p.c_bytes = int64_t(eff) * mn * 4;
+    p.M = o.M; p.N = o.N; p.K = o.K; p.lda = o.lda; p.ldb = o.ldb; p.ldc = o.N;
+    p.tiles_m = (o.M + e.v.BM - 1) / e.v.BM;
+    p.tiles_n = (o.N + e.v.BN - 1) / e.v.BN;
+    p.splits = eff;
+    p.k_chunk = k_chunk;
+    p.c_split_stride = mn;
+    const int64_t items = int64_t(p.tiles_m) * p.tiles_n * eff;
+    if (items > INT32_MAX) return SGEMM_ETOO_LARGE;
+    const int64_t slots = int64_t(cus) * e.v.wg_per_cu;
+    const int64_t grid = (e.v.persist && items > slots) ? slots : items;
+    int st = launch(e.kern, dim3(unsigned(grid)), dim3(e.threads), stream, p);
+    if (st != SGEMM_OK) return st;
+    int64_t blocks = (mn + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    return launch(k_splitk_reduce, dim3(unsigned(blocks)), dim3(256), stream, o.M, o.N, eff,
+                  static_cast<const float *>(W), mn, C, o.ldc);
 }
 
 int run_hot(int variant, int M, int N, int K, const float *A, int lda, const float *B, int ldb,
@@ -156,6 +217,52 @@ extern "C" int sgemm_f32_variant(int variant, int M, int N, int K, const float *
                                  const float *B, int ldb, float *C, int ldc, void *stream)
 {
     return run_hot(variant < 0 ? -1 : variant, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+extern "C" size_t sgemm_f32_splitk_workspace_size(int M, int N, int K, int splits)
+{
+    if (M <= 0 || N <= 0 || K <= 0 || splits < 0 || splits > kMaxSplits) return 0;
+    if (splits == 0) {
+        int cus = 0;
+        if (device_cus(&cus) != SGEMM_OK) return 0;
+        splits = auto_splits(make_operands(M, N, K, K, N, N), cus);
+    }
+    if (splits <= 1) return 0;
+    return size_t(splits) * size_t(M) * size_t(N) * 4u;   // one M x N slice per range
+}
+
+extern "C" int sgemm_f32_splitk(int M, int N, int K, const float *A, int lda, const float *B,
+                                int ldb, float *C, int ldc, int splits, float *workspace,
+                                size_t workspace_bytes, void *stream)
+{
+    const int st = validate(M, N, K, A, lda, B, ldb, C, ldc);
+    if (st != SGEMM_OK) return st;
+    if (splits < 0 || splits > kMaxSplits) return SGEMM_EINVAL_ARG;
+    if (M == 0 || N == 0) return SGEMM_OK;
+    const Operands o = make_operands(M, N, K, lda, ldb, ldc);
+    int cus = 0;
+    if (splits == 0 && K > 0) {
+        const int qs = device_cus(&cus);
+        if (qs != SGEMM_OK) return qs;
+        splits = auto_splits(o, cus);
+    }
+    if (splits >= 2 && K > 0) {
+        // workspace checks come before any HIP call when the split count is given
+        const int64_t w_elems = int64_t(workspace_bytes / 4);
+        if (bad_ptr(workspace, w_elems > 0 ? w_elems : 1)) return SGEMM_EINVAL_PTR;
+        if (workspace_bytes < size_t(splits) * size_t(M) * size_t(N) * 4u) return SGEMM_EINVAL_ARG;
+        if (overlap(workspace, w_elems, A, span_elems(M, K, lda)) ||
+            overlap(workspace, w_elems, B, span_elems(K, N, ldb)) ||
+            overlap(workspace, w_elems, C, span_elems(M, N, ldc)))
+            return SGEMM_EALIAS;
+    }
+    if (K == 0) return fill_zero(M, N, C, ldc, stream);
+    if (splits <= 1) return run_hot(-1, M, N, K, A, lda, B, ldb, C, ldc, stream);
+    if (cus == 0) {
+        const int qs = device_cus(&cus);
+        if (qs != SGEMM_OK) return qs;
+    }
+    return run_splitk(splits, o, A, B, C, workspace, workspace_bytes, stream, cus);
 }
 
 extern "C" int sgemm_f32_naive(int M, int N, int K, const float *A, int lda, const float *B,

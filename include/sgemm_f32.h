@@ -34,6 +34,8 @@
 #ifndef SGEMM_F32_H
 #define SGEMM_F32_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -62,6 +64,31 @@ int sgemm_f32(int M, int N, int K,
               const float *B, int ldb,
               float *C, int ldc,
               void *stream);
+
+/*
+ * Split-K for shapes whose M x N gives too few tiles to fill the GPU (small M * N, large
+ * K): K is cut into `splits` ranges of whole K-panels; the hot kernel computes each
+ * (tile, range) item into its own M x N slice of `workspace` (packed rows of N floats),
+ * and a second kernel sums the slices in ascending range order into C, so repeated calls
+ * give identical bits. splits = 0 lets the library choose (about two items per compute
+ * unit, ranges of at least four panels); splits = 1 is sgemm_f32. At most 32.
+ * workspace is a caller-owned device buffer of at least splits * M * N * 4 bytes
+ * (sgemm_f32_splitk_workspace_size) that must not overlap A, B or C (SGEMM_EINVAL_PTR if
+ * NULL or misaligned, SGEMM_EINVAL_ARG if too small, SGEMM_EALIAS on overlap; checked
+ * before any HIP call when splits >= 2); its contents on return are unspecified. Both
+ * kernels run on `stream`.
+ */
+int sgemm_f32_splitk(int M, int N, int K,
+                     const float *A, int lda,
+                     const float *B, int ldb,
+                     float *C, int ldc,
+                     int splits, float *workspace, size_t workspace_bytes,
+                     void *stream);
+
+/* Bytes of workspace sgemm_f32_splitk needs for this shape and split count (0 when it
+ * needs none: splits of 1, empty shapes, or arguments out of range). splits = 0 asks for
+ * the automatic choice and queries the current device. */
+size_t sgemm_f32_splitk_workspace_size(int M, int N, int K, int splits);
 
 /*
  * The reference kernel: one thread per element of C, a length-K dot product read

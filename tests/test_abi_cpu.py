@@ -137,3 +137,25 @@ def test_lds_transpose_validation():
     assert t(4, 4, P, 4, P + 4096, 4, 16, 0, None) == -6
     assert t(4, 4, P, 4, P + 4096, 4, 64, 2, None) == -6
     assert t(0, 4, P, 4, P + 4096, 1, 64, 1, None) == 0
+
+
+def test_splitk_validation_and_workspace_size():
+    lib = g.library()
+    args = (64, 48, 4096, P, 4096, P + (1 << 26), 48, P + (1 << 27), 48)
+    ws = P + (1 << 28)
+    assert lib.sgemm_f32_splitk_workspace_size(64, 48, 4096, 1) == 0
+    assert lib.sgemm_f32_splitk_workspace_size(64, 48, 4096, 4) == 4 * 64 * 48 * 4
+    assert lib.sgemm_f32_splitk_workspace_size(64, 48, 4096, 33) == 0
+    assert lib.sgemm_f32_splitk_workspace_size(0, 48, 4096, 4) == 0
+    need = 4 * 64 * 48 * 4
+    assert lib.sgemm_f32_splitk(*args, 33, ws, need, None) == -6
+    assert lib.sgemm_f32_splitk(*args, -1, ws, need, None) == -6
+    assert lib.sgemm_f32_splitk(*args, 4, None, need, None) == -3
+    assert lib.sgemm_f32_splitk(*args, 4, ws + 2, need, None) == -3
+    assert lib.sgemm_f32_splitk(*args, 4, ws, need - 4, None) == -6
+    assert lib.sgemm_f32_splitk(*args, 4, P + 64, need, None) == -4     # overlaps A
+    assert lib.sgemm_f32_splitk(*args, 4, P + (1 << 27) - 64, need, None) == -4   # overlaps C
+    assert lib.sgemm_f32_splitk(-1, 48, 4096, P, 4096, P + 4096, 48, P + 8192, 48, 4, ws, need,
+                                None) == -1
+    assert lib.sgemm_f32_splitk(0, 48, 4096, P, 4096, P + 4096, 48, P + 8192, 48, 4, ws, need,
+                                None) == 0
