@@ -203,7 +203,7 @@ struct MfmaTile {
     static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS holds 160 KiB per workgroup");
 };
 
-template <int BM, int BN, int BK, int WGM, int WGN, int KACC, bool PERSIST>
+template <int BM, int BN, int BK, int WGM, int WGN, int KACC, bool PERSIST, int PH>
 __global__ __launch_bounds__(64 * WGM * WGN) void k_sgemm_mfma(GemmArgs p)
 {
     using T = MfmaTile<BM, BN, BK, WGM, WGN, KACC>;
@@ -262,6 +262,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_sgemm_mfma(GemmArgs p)
             lK = 0;
             ls = 0;
         }
+        // all wave-uniform: keep them (and the loops they bound) on the scalar unit
+        lm0 = __builtin_amdgcn_readfirstlane(lm0);
+        ln0 = __builtin_amdgcn_readfirstlane(ln0);
+        lkb = __builtin_amdgcn_readfirstlane(lkb);
+        lK = __builtin_amdgcn_readfirstlane(lK);
+        ls = __builtin_amdgcn_readfirstlane(ls);
         b_col_ok = ln0 + b_c0 < N;
     };
 
@@ -281,12 +287,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_sgemm_mfma(GemmArgs p)
         if (l < A_CH) {
             const int kc = k_load + 4 * a_q;
             const bool ok = lm0 + a_r0 + l * A_RSTEP < M && kc < lK;
-            f32x4 v = load_b128(rsa, ok ? a_off0 + uint32_t(l) * a_stride : kOob);
-            // a chunk that crosses K: its elements past K belong to the row padding or the
-            // next row; zero them (a select, so a NaN there cannot leak)
-#pragma unroll
-            for (int e = 1; e < 4; ++e) v[e] = kc + e < lK ? v[e] : 0.0f;
-            ra[l] = v;
+            ra[l] = load_b128(rsa, ok ? a_off0 + uint32_t(l) * a_stride : kOob);
         } else {
             const int i = l - A_CH;
             const bool ok = k_load + b_k0 + i * B_KSTEP < lK && b_col_ok;
@@ -295,9 +296,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_sgemm_mfma(GemmArgs p)
         }
     };
     auto write_slot = [&](float *As, int l) {
-        if (l < A_CH)
-            *reinterpret_cast<f32x4 *>(As + a_lds0 + l * A_RSTEP * BK) = ra[l];
-        else
+        if (l < A_CH) {
+            // a chunk that crosses K: its elements past K belong to the row padding or the
+            // next row; zero them (a select, so a NaN there cannot leak). Done here, where
+            // the data is needed anyway, so the select does not wait on the load early.
+            const int kc = k_load + 4 * a_q;
+            f32x4 v = ra[l];
+#pragma unroll
+            for (int e = 1; e < 4; ++e) v[e] = kc + e < lK ? v[e] : 0.0f;
+            *reinterpret_cast<f32x4 *>(As + a_lds0 + l * A_RSTEP * BK) = v;
+        } else
             *reinterpret_cast<f32x4 *>(As + T::A_TILE + b_lds0 + (l - A_CH) * B_KSTEP * BN) =
                 rb[l - A_CH];
     };
@@ -350,13 +358,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_sgemm_mfma(GemmArgs p)
     //                       they cover the latency of those reads.
     // One barrier per panel is enough: the other stage was last read before the previous
     // panel's barrier, and this panel's reads of `cur` all precede this barrier.
+    // Staging phases: with PH = 2 the panel is staged in two halves (loads at the start of
+    // each half of the panel, LDS writes near its end), so only half the staging registers
+    // are live at a time.
     constexpr int STEPS = BK / 2;
     constexpr int NL = A_CH + B_CH;
-    constexpr int LS = SGEMM_LOAD_STEPS;
-    constexpr int WS = SGEMM_WRITE_STEPS;
-    constexpr int PER_LOAD = (NL + LS - 1) / LS;
-    constexpr int PER_WRITE = (NL + WS - 1) / WS;
-    static_assert(LS + WS < STEPS, "loads and LDS writes of a panel need separate steps");
+    constexpr int P = STEPS / PH;                       // steps per phase
+    constexpr int NP = NL / PH;                         // staging slots per phase
+    constexpr int LS = PH == 1 ? SGEMM_LOAD_STEPS : 2;  // load steps per phase
+    constexpr int WS = PH == 1 ? SGEMM_WRITE_STEPS : 2; // write steps per phase
+    constexpr int PER_LOAD = (NP + LS - 1) / LS;
+    constexpr int PER_WRITE = (NP + WS - 1) / WS;
+    static_assert(STEPS % PH == 0 && NL % PH == 0, "phases divide the panel");
+    static_assert(LS + WS < P, "loads and LDS writes of a phase need separate steps");
 
     auto panel = [&](int cur, auto next_tag) {
         constexpr bool NEXT = decltype(next_tag)::value;
@@ -368,22 +382,24 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_sgemm_mfma(GemmArgs p)
             constexpr int kb = t >> 2, s = t & 3;
             constexpr bool next_b = t + 1 < STEPS;
             constexpr bool next_a = s == 0 && kb + 1 < BK / 8;
-            constexpr int w0 = t - (STEPS - 1 - WS);   // write group index
-            constexpr int n_load = (NEXT && t < LS)
-                ? ((t + 1) * PER_LOAD < NL ? PER_LOAD : (NL - t * PER_LOAD > 0 ? NL - t * PER_LOAD : 0))
+            constexpr int h = t / P, u = t % P;                 // phase and step in it
+            constexpr int w0 = u - (P - 1 - WS);                // write group in the phase
+            constexpr int l_first = h * NP + u * PER_LOAD;
+            constexpr int n_load = (NEXT && u < LS)
+                ? ((u + 1) * PER_LOAD < NP ? PER_LOAD : (NP - u * PER_LOAD > 0 ? NP - u * PER_LOAD : 0))
                 : 0;
+            constexpr int w_first = h * NP + (w0 > 0 ? w0 : 0) * PER_WRITE;
             constexpr int n_write = (NEXT && w0 >= 0 && w0 < WS)
-                ? ((w0 + 1) * PER_WRITE < NL ? PER_WRITE
-                                             : (NL - w0 * PER_WRITE > 0 ? NL - w0 * PER_WRITE : 0))
+                ? ((w0 + 1) * PER_WRITE < NP ? PER_WRITE
+                                             : (NP - w0 * PER_WRITE > 0 ? NP - w0 * PER_WRITE : 0))
                 : 0;
             if constexpr (n_load > 0) {
 #pragma unroll
-                for (int l = t * PER_LOAD; l < t * PER_LOAD + n_load; ++l) load_slot(l);
+                for (int l = l_first; l < l_first + n_load; ++l) load_slot(l);
             }
             if constexpr (n_write > 0) {
 #pragma unroll
-                for (int l = w0 * PER_WRITE; l < w0 * PER_WRITE + n_write; ++l)
-                    write_slot(Anext, l);
+                for (int l = w_first; l < w_first + n_write; ++l) write_slot(Anext, l);
             }
             if constexpr (next_b) read_b(Bs, t + 1, b[(t + 1) & 1]);
             if constexpr (next_a) read_a(As, kb + 1, a[(kb + 1) & 1]);
