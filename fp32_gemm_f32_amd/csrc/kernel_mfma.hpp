@@ -134,20 +134,25 @@ __device__ inline void static_for(F &&f)
 }
 
 // Buffer store of W consecutive floats at voff + soff (dropped by the hardware when voff is
-// out of range; soff stays below 2^31, so kOob + soff cannot wrap into range).
+// out of range; soff stays below 2^31, so kOob + soff cannot wrap into range). C is written
+// once and not read again by the kernel, so the stores carry the non-temporal hint (cache
+// policy bit 1 on gfx950), which measurably speeds up the store-heavy low-K shapes.
+constexpr int kStoreNonTemporal = 2;
 template <int W>
 __device__ inline void store_vec(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
                                  typename fvec<W>::type v)
 {
     if constexpr (W == 4) {
         typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, soff, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, soff,
+                                               kStoreNonTemporal);
     } else if constexpr (W == 2) {
         typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, voff, soff, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, voff, soff,
+                                              kStoreNonTemporal);
     } else {
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, v), r, voff, soff,
-                                              0);
+                                              kStoreNonTemporal);
     }
 }
 
