@@ -185,44 +185,61 @@ __device__ inline void tile_coords(int bid, int tiles_m, int tiles_n, int &tm, i
     tn = w / rows;
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, int KACC = 1>
+template <int BM, int BN, int BK, int WGM, int WGN, int KACC = 1, int KG = 1>
 struct MfmaTile {
-    static constexpr int kThreads = 64 * WGM * WGN;
+    static constexpr int kGroupThreads = 64 * WGM * WGN;   // one K-group of waves
+    static constexpr int kThreads = kGroupThreads * KG;
     static constexpr int WM = BM / WGM;          // wave tile rows
     static constexpr int WN = BN / WGN;          // wave tile columns
     static constexpr int RB = WM / 32;           // 32-row MFMA blocks per wave
     static constexpr int CI = WN >= 128 ? 4 : WN / 32;   // column interleave
     static constexpr int CG = WN / (32 * CI);    // interleaved column groups
+    static constexpr int NACC = RB * CI * CG;    // 32 x 32 accumulator blocks per wave
     static constexpr int CPR = BK / 4;           // 16-byte chunks per A-tile row
-    static constexpr int A_CH = BM * BK / 4 / kThreads;  // A chunks per thread per panel
-    static constexpr int B_CH = BK * BN / 4 / kThreads;  // B chunks per thread per panel
+    static constexpr int A_CH = BM * BK / 4 / kGroupThreads;  // A chunks per thread per panel
+    static constexpr int B_CH = BK * BN / 4 / kGroupThreads;  // B chunks per thread per panel
     static constexpr int A_TILE = BM * BK;       // floats per A stage
     static constexpr int B_TILE = BK * BN;       // floats per B stage
     static constexpr int STAGE = A_TILE + B_TILE;
-    static constexpr int LDS_BYTES = 2 * STAGE * 4;
+    // partial sums of K-groups 1 .. KG-1, handed to group 0 at the end of each item
+    static constexpr int RED = (KG - 1) * kGroupThreads * NACC * 16;
+    static constexpr int LDS_FLOATS = 2 * KG * STAGE + RED;
+    static constexpr int LDS_BYTES = LDS_FLOATS * 4;
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile is made of 32 x 32 blocks");
     static_assert(WN % (32 * CI) == 0, "column groups");
     static_assert(BK % 8 == 0, "four MFMA k-steps consume 8 k values");
-    static_assert((BM * BK / 4) % kThreads == 0 && (BK * BN / 4) % kThreads == 0,
-                  "panel chunks divide evenly over the workgroup");
+    static_assert((BM * BK / 4) % kGroupThreads == 0 && (BK * BN / 4) % kGroupThreads == 0,
+                  "panel chunks divide evenly over a K-group");
     static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS holds 160 KiB per workgroup");
 };
 
-template <int BM, int BN, int BK, int WGM, int WGN, int KACC, bool PERSIST, int PH>
-__global__ __launch_bounds__(64 * WGM * WGN) void k_sgemm_mfma(GemmArgs p)
+// KG > 1 splits K inside the workgroup: KG groups of WGM x WGN waves compute the same
+// tile, group g taking K-panels g, g + KG, g + 2 KG, ..., each with its own LDS stages;
+// at the end of a tile groups 1 .. KG-1 pass their sums through LDS to group 0, which adds
+// them in ascending group order (deterministic) and stores C. This puts KG waves on each
+// SIMD for tiles too small to fill the GPU otherwise.
+template <int BM, int BN, int BK, int WGM, int WGN, int KACC, bool PERSIST, int PH, int KG>
+__global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
 {
-    using T = MfmaTile<BM, BN, BK, WGM, WGN, KACC>;
-    constexpr int NT = T::kThreads, WM = T::WM, WN = T::WN, RB = T::RB, CI = T::CI,
+    using T = MfmaTile<BM, BN, BK, WGM, WGN, KACC, KG>;
+    constexpr int NT = T::kGroupThreads, WM = T::WM, WN = T::WN, RB = T::RB, CI = T::CI,
                   CG = T::CG, CPR = T::CPR, A_CH = T::A_CH, B_CH = T::B_CH;
     typedef typename fvec<CI>::type bvec;
 
-    __shared__ __attribute__((aligned(16))) float smem[2 * T::STAGE];
+    __shared__ __attribute__((aligned(16))) float lds_all[T::LDS_FLOATS];
 
-    const int tid = threadIdx.x;
+    // K-group of this wave: uniform across the wave (NT is a multiple of 64), which the
+    // compiler must be told, or every buffer load's resource looks divergent
+    const int kg = KG == 1 ? 0 : __builtin_amdgcn_readfirstlane(int(threadIdx.x) / NT);
+    const int tid = threadIdx.x % NT;         // thread index inside the K-group
     const int lane = tid & 63;
     const int lo = lane & 31, hi = lane >> 5;
     const int wave = tid >> 6;
     const int wm = wave / WGN, wn = wave % WGN;
+    // this group's stages: stage s at smem + s * KG * STAGE
+    float *const smem = lds_all + kg * T::STAGE;
+    constexpr int SSTRIDE = KG * T::STAGE;
+    float *const red = lds_all + 2 * KG * T::STAGE;
 
     const int M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
     const int ntiles = p.tiles_m * p.tiles_n;
@@ -379,9 +396,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_sgemm_mfma(GemmArgs p)
 
     auto panel = [&](int cur, auto next_tag) {
         constexpr bool NEXT = decltype(next_tag)::value;
-        const float *As = smem + cur * T::STAGE;
+        const float *As = smem + cur * SSTRIDE;
         const float *Bs = As + T::A_TILE;
-        float *Anext = smem + (cur ^ 1) * T::STAGE;
+        float *Anext = smem + (cur ^ 1) * SSTRIDE;
         static_for<0, STEPS>([&](auto tc) {
             constexpr int t = decltype(tc)::value;
             constexpr int kb = t >> 2, s = t & 3;
@@ -446,13 +463,49 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_sgemm_mfma(GemmArgs p)
 
     // ---- epilogue of one tile: accumulators to C through a buffer resource ----
     const int ldc = p.ldc;
-    auto epilogue = [&](int m0, int n0, int split) {
+    // Sum the accumulator sets, then (KG > 1) the K-groups, into group 0's acc[0].
+    auto finish = [&]() {
 #pragma unroll
         for (int h = 1; h < KACC; ++h)
 #pragma unroll
             for (int i = 0; i < RB; ++i)
 #pragma unroll
                 for (int j = 0; j < CI * CG; ++j) acc[0][i][j] += acc[h][i][j];
+        if constexpr (KG > 1) {
+            // group g > 0 writes quad q of its sums at red[((g-1) * NACC * 4 + q) * NT + tid]
+            if (kg > 0) {
+#pragma unroll
+                for (int i = 0; i < RB; ++i)
+#pragma unroll
+                    for (int j = 0; j < CI * CG; ++j)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const f32x16 &x = acc[0][i][j];
+                            const f32x4 v = {x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
+                            const int quad = ((kg - 1) * T::NACC + i * CI * CG + j) * 4 + q;
+                            *reinterpret_cast<f32x4 *>(red + (quad * NT + tid) * 4) = v;
+                        }
+            }
+            __syncthreads();
+            if (kg == 0) {
+                for (int g = 1; g < KG; ++g)
+#pragma unroll
+                    for (int i = 0; i < RB; ++i)
+#pragma unroll
+                        for (int j = 0; j < CI * CG; ++j)
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                const int quad = ((g - 1) * T::NACC + i * CI * CG + j) * 4 + q;
+                                const f32x4 v =
+                                    *reinterpret_cast<const f32x4 *>(red + (quad * NT + tid) * 4);
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) acc[0][i][j][4 * q + e] += v[e];
+                            }
+            }
+        }
+    };
+
+    auto epilogue = [&](int m0, int n0, int split) {
         // Lane (lo, hi) owns rows lrow + dr (dr = 8 (v / 4) + v % 4 for accumulator v) and
         // columns col .. col + CI - 1 of each of its blocks. The row step dr * ldc goes in
         // the scalar offset; rows past M and chunks that cross N get voffset kOob (the
@@ -507,10 +560,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_sgemm_mfma(GemmArgs p)
         }
     };
 
-    // ---- K loop over the workgroup's items ----
+    // ---- K loop over the workgroup's items; group kg takes panels kg, kg + KG, ... ----
     int vb = blockIdx.x;
     set_load_tile(vb);
-    set_panel(0);
+    set_panel(kg * BK);
 #pragma unroll
     for (int l = 0; l < NL; ++l) load_slot(l);
 #pragma unroll
@@ -520,33 +573,35 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_sgemm_mfma(GemmArgs p)
     read_b(smem + T::A_TILE, 0, b[0]);
 
     if constexpr (!PERSIST) {
-        // one item per workgroup: the last panel stages nothing
-        const int panels = (lK + BK - 1) / BK;
-        for (int pnl = 0; pnl + 1 < panels; ++pnl) {
-            set_panel((pnl + 1) * BK);
-            panel(pnl & 1, std::true_type{});
+        // one item per workgroup: the last round stages nothing
+        const int rounds = ((lK + BK - 1) / BK + KG - 1) / KG;
+        for (int r = 0; r + 1 < rounds; ++r) {
+            set_panel(((r + 1) * KG + kg) * BK);
+            panel(r & 1, std::true_type{});
         }
-        panel((panels - 1) & 1, std::false_type{});
-        epilogue(lm0, ln0, ls);
+        panel((rounds - 1) & 1, std::false_type{});
+        finish();
+        if (kg == 0) epilogue(lm0, ln0, ls);
     } else {
-        // Items vb, vb + G, vb + 2G, ...: the last panel of an item stages panel 0 of the
-        // workgroup's next item, so that item's first loads and LDS writes run under the
-        // current item's MFMAs and the epilogue's stores drain while the next item
+        // Items vb, vb + G, vb + 2G, ...: the last round of an item stages the first round
+        // of the workgroup's next item, so that item's first loads and LDS writes run under
+        // the current item's MFMAs and the epilogue's stores drain while the next item
         // computes. After the last item the staged "next item" lies past the matrix and
-        // every one of its loads is masked to zero; one panel body serves every panel.
+        // every one of its loads is masked to zero; one panel body serves every round.
         const int G = gridDim.x;
         int cur = 0;
         for (;;) {
             const int cm0 = lm0, cn0 = ln0, cs = ls;   // the item being computed
-            const int panels = (lK + BK - 1) / BK;
-            for (int pnl = 0; pnl < panels; ++pnl) {
-                const bool last = pnl + 1 == panels;
+            const int rounds = ((lK + BK - 1) / BK + KG - 1) / KG;
+            for (int r = 0; r < rounds; ++r) {
+                const bool last = r + 1 == rounds;
                 if (last) set_load_tile(vb + G);
-                set_panel(last ? 0 : (pnl + 1) * BK);
+                set_panel(((last ? 0 : r + 1) * KG + kg) * BK);
                 panel(cur, std::true_type{});
                 cur ^= 1;
             }
-            epilogue(cm0, cn0, cs);
+            finish();
+            if (kg == 0) epilogue(cm0, cn0, cs);
             vb += G;
             if (vb >= nitems) break;
             zero_acc();

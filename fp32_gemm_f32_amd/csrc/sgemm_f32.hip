@@ -54,21 +54,25 @@ struct VariantEntry {
     int threads;
 };
 
-template <int BM, int BN, int BK, int WGM, int WGN, int KACC, bool PERSIST, int PH = 1>
+template <int BM, int BN, int BK, int WGM, int WGN, int KACC, bool PERSIST, int KG = 1>
 constexpr VariantEntry entry(const char *name, int wg_per_cu, double rate)
 {
     return VariantEntry{Variant{name, BM, BN, BK, WGM, WGN, wg_per_cu, rate, PERSIST},
-                        &k_sgemm_mfma<BM, BN, BK, WGM, WGN, KACC, PERSIST, PH>, 64 * WGM * WGN};
+                        &k_sgemm_mfma<BM, BN, BK, WGM, WGN, KACC, PERSIST, 1, KG>,
+                        64 * WGM * WGN * KG};
 }
 
-// Rates are the variants' throughput at 8192^3 relative to 140 TFLOP/s on MI355X.
-// The 8-wave 256x256 tile comes in both forms: one tile per workgroup (fastest when K is
-// long) and persistent (its epilogue overlaps the next tile: best when K is short).
+// Rates are the variants' throughput at 8192^3 relative to 140 TFLOP/s on MI355X. The
+// 8-wave 256x256 tile comes in both forms: one tile per workgroup (fastest when K is long)
+// and persistent (its epilogue overlaps the next tile: best when K is short). The two
+// K-group variants (KG = 2: two waves per SIMD on one tile) serve shapes too small to give
+// every CU more than one tile.
 const VariantEntry kVariants[] = {
     entry<256, 256, 32, 2, 4, 1, false>("mfma_256x256x32_w2x4", 1, 1.03),
-    entry<256, 256, 32, 2, 4, 1, true>("mfma_256x256x32_w2x4_p", 1, 1.01),
-    entry<128, 128, 32, 2, 2, 1, true>("mfma_128x128x32_w2x2_p", 2, 0.94),
-    entry<64, 64, 64, 2, 2, 2, true>("mfma_64x64x64_w2x2_acc2_p", 2, 0.82),
+    entry<256, 256, 32, 2, 4, 1, true>("mfma_256x256x32_w2x4_p", 1, 1.015),
+    entry<128, 128, 32, 2, 2, 1, true>("mfma_128x128x32_w2x2_p", 2, 0.945),
+    entry<128, 64, 32, 2, 2, 1, true, 2>("mfma_128x64x32_w2x2_kg2_p", 1, 0.85),
+    entry<64, 64, 64, 2, 2, 2, true, 2>("mfma_64x64x64_w2x2_acc2_kg2_p", 1, 0.80),
 };
 constexpr int kNumVariants = int(sizeof(kVariants) / sizeof(kVariants[0]));
 
