@@ -157,10 +157,10 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5", "sk"])
     ap.add_argument("--variant", type=int, default=-1, help="force a hot-kernel tile variant")
     ap.add_argument("--kernel", default="auto",
-                    choices=["auto", "naive", "tiled16", "tiled32", "tiled32p", "regtiled41",
+                    choices=["auto", "splitk", "naive", "tiled16", "tiled32", "tiled32p", "regtiled41",
                              "regtiled44", "regtiled88", "transpose32p0", "transpose32p1",
                              "transpose64p0", "transpose64p1"],
                     help="the entry point a step calls (default: the hot path sgemm_f32); the "
@@ -206,7 +206,14 @@ def main() -> int:
 
     kern = args.kernel
     gemm = call_args[:-1]
-    if kern != "auto":
+    ws = None
+    if kern == "splitk":
+        ws_bytes = lib.sgemm_f32_splitk_workspace_size(M, N, K, 0)
+        ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device=dev)
+        plan["splitk_workspace_bytes"] = ws_bytes
+        plan["splits"] = ws_bytes // (4 * M * N) if ws_bytes else 1
+        plan["name"] = f"splitk{plan['splits']}+reduce"
+    if kern not in ("auto", "splitk"):
         plan["name"] = {"naive": "naive", "tiled16": "lds_tiled_16", "tiled32": "lds_tiled_32",
                         "tiled32p": "lds_tiled_32_padded", "regtiled41": "regtiled_4x1",
                         "regtiled44": "regtiled_4x4", "regtiled88": "regtiled_8x8"}[kern]
@@ -216,6 +223,8 @@ def main() -> int:
         if kern == "auto":
             rc = (lib.sgemm_f32(*call_args) if args.variant < 0
                   else lib.sgemm_f32_variant(args.variant, *call_args))
+        elif kern == "splitk":
+            rc = lib.sgemm_f32_splitk(*gemm, 0, ws.data_ptr(), plan["splitk_workspace_bytes"], sp)
         elif kern == "naive":
             rc = lib.sgemm_f32_naive(*call_args)
         elif kern.startswith("tiled"):
@@ -247,7 +256,7 @@ def main() -> int:
     compulsory = 4.0 * (M * K + K * N + M * N)
     t_mfma = flop / (PEAK_FP32_MFMA_TFLOPS * 1e12)
     t_hbm = compulsory / (PEAK_HBM_GBS * 1e9)
-    if kern != "auto":
+    if kern not in ("auto", "splitk"):
         # the scalar rungs run on the vector ALUs without packed FP32: 256 CUs x 4 SIMDs x
         # 16 lanes x 2 FLOP x 2.4 GHz
         achieved = flop / (ms / 1e3) / 1e12

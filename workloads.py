@@ -14,6 +14,7 @@ shape, the large square headline shape and a low-K shape:
   c3    1023   1025   1027  standard normal
   c4    8192   8192   8192  uniform[-1, 1]
   c5    16384  16384  64    uniform[-1, 1]
+  sk    256    256    32768 uniform[-1, 1]    (an under-filled shape for split-K)
 
 Seeds: A = 1000*i + 1, B = 1000*i + 2 for config ci; the integer variant uses
 1000*i + 3 and 1000*i + 4. All operands are packed row-major (lda = K, ldb = N).
@@ -49,6 +50,8 @@ WORKLOADS = {
     "c3": Workload("c3", 3, 1023, 1025, 1027, "normal", "ragged 1023x1025x1027"),
     "c4": Workload("c4", 4, 8192, 8192, 8192, "uniform", "square 8192^3"),
     "c5": Workload("c5", 5, 16384, 16384, 64, "uniform", "low-K 16384x16384x64"),
+    # not one of the five: an under-filled shape (16 tiles of 64 x 64) for split-K
+    "sk": Workload("sk", 6, 256, 256, 32768, "uniform", "under-filled 256x256x32768"),
 }
 
 
