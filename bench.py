@@ -213,6 +213,7 @@ def main() -> int:
         plan["splitk_workspace_bytes"] = ws_bytes
         plan["splits"] = ws_bytes // (4 * M * N) if ws_bytes else 1
         plan["name"] = f"splitk{plan['splits']}+reduce"
+        plan["BM"] = plan["BN"] = plan["BK"] = plan["grid"] = None   # chosen per split count
     if kern not in ("auto", "splitk"):
         plan["name"] = {"naive": "naive", "tiled16": "lds_tiled_16", "tiled32": "lds_tiled_32",
                         "tiled32p": "lds_tiled_32_padded", "regtiled41": "regtiled_4x1",

@@ -610,17 +610,45 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
 }
 
 // C[i][j] = sum over s of W[s * stride + i * N + j], in ascending s: the second pass of
-// split-K (a fixed summation order, so repeated runs give identical bits).
-__global__ __launch_bounds__(256) void k_splitk_reduce(int M, int N, int splits,
-                                                      const float *__restrict__ W, int64_t stride,
-                                                      float *__restrict__ C, int ldc)
+// split-K (a fixed summation order, so repeated runs give identical bits). Each lane owns
+// VW consecutive columns of one row (VW = 4 needs N % 4 == 0 and a 16-byte aligned W; the
+// stores to C are 16-byte wide only when c_vec says C's rows allow it). The slices are
+// loaded in batches of kReduceBatch, all in flight together, and then added in order, so
+// a whole batch costs one memory latency rather than one per slice.
+constexpr int kReduceBatch = 16;
+
+template <int VW>
+__global__ __launch_bounds__(64) void k_splitk_reduce(int M, int N, int splits,
+                                                     const float *__restrict__ W, int64_t stride,
+                                                     float *__restrict__ C, int ldc, int c_vec)
 {
-    const int64_t total = int64_t(M) * N;
-    for (int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
-         e += int64_t(gridDim.x) * blockDim.x) {
-        float v = W[e];
-        for (int s = 1; s < splits; ++s) v += W[s * stride + e];
-        C[(e / N) * ldc + e % N] = v;
+    using V = typename std::conditional<VW == 4, f32x4, float>::type;
+    const int64_t groups = int64_t(M) * (N / VW);
+    for (int64_t gi = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; gi < groups;
+         gi += int64_t(gridDim.x) * blockDim.x) {
+        const int64_t e = gi * VW;
+        V acc = *reinterpret_cast<const V *>(W + e);
+        for (int s0 = 1; s0 < splits; s0 += kReduceBatch) {
+            V t[kReduceBatch];
+#pragma unroll
+            for (int u = 0; u < kReduceBatch; ++u)
+                if (s0 + u < splits) t[u] = *reinterpret_cast<const V *>(W + (s0 + u) * stride + e);
+#pragma unroll
+            for (int u = 0; u < kReduceBatch; ++u)
+                if (s0 + u < splits) acc += t[u];
+        }
+        const int64_t row = e / N;
+        float *dst = C + row * ldc + (e - row * N);
+        if constexpr (VW == 4) {
+            if (c_vec) {
+                *reinterpret_cast<f32x4 *>(dst) = acc;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) dst[j] = acc[j];
+            }
+        } else {
+            *dst = acc;
+        }
     }
 }
 

@@ -183,10 +183,16 @@ int run_splitk(int splits, const Operands &o0, const float *A, const float *B, f
     const int64_t grid = (e.v.persist && items > slots) ? slots : items;
     int st = launch(e.kern, dim3(unsigned(grid)), dim3(e.threads), stream, p);
     if (st != SGEMM_OK) return st;
-    int64_t blocks = (mn + 255) / 256;
+    const bool w_vec = (o.N % 4 == 0) && (reinterpret_cast<uintptr_t>(W) % 16 == 0);
+    const int c_vec = (o.ldc % 4 == 0) && (reinterpret_cast<uintptr_t>(C) % 16 == 0);
+    const int64_t groups = w_vec ? mn / 4 : mn;
+    int64_t blocks = (groups + 63) / 64;
     if (blocks > 65536) blocks = 65536;
-    return launch(k_splitk_reduce, dim3(unsigned(blocks)), dim3(256), stream, o.M, o.N, eff,
-                  static_cast<const float *>(W), mn, C, o.ldc);
+    const float *Wc = W;
+    return w_vec ? launch(k_splitk_reduce<4>, dim3(unsigned(blocks)), dim3(64), stream, o.M, o.N,
+                          eff, Wc, mn, C, o.ldc, c_vec)
+                 : launch(k_splitk_reduce<1>, dim3(unsigned(blocks)), dim3(64), stream, o.M, o.N,
+                          eff, Wc, mn, C, o.ldc, c_vec);
 }
 
 int run_hot(int variant, int M, int N, int K, const float *A, int lda, const float *B, int ldb,

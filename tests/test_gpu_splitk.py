@@ -50,7 +50,7 @@ def test_splitk_exact_integers(gpu, M, N, K, splits):
     assert rep["n_inexact"] == 0 and rep["n_nonfinite"] == 0, rep
 
 
-@pytest.mark.parametrize("name,splits", [("c2", 4), ("c3", 2), ("c3", 0)])
+@pytest.mark.parametrize("name,splits", [("c2", 4), ("c3", 2), ("c3", 0), ("sk", 0), ("sk", 32)])
 def test_splitk_configs_float(gpu, name, splits):
     A, B = wl.operands(name)
     C = run_splitk(gpu, A, B, splits)
