@@ -6,7 +6,9 @@
 // gfx950 the parallelism to fill is 256 compute units of 4 SIMDs. The choice below
 // estimates, for each variant the operands allow, the time of the busiest compute unit,
 //     ceil(tiles / CUs) x (work of one tile / the variant's measured rate + per-tile overhead),
-// and takes the smallest.
+// and takes the smallest. The overhead (first-panel latency and epilogue stores not hidden
+// behind MFMAs) depends on the variant: a persistent workgroup overlaps it with its next
+// tile, and two resident workgroups per CU overlap one's epilogue with the other's MFMAs.
 #pragma once
 
 #include <cstdint>
@@ -20,6 +22,7 @@ struct Variant {
     int wgm, wgn;           // waves along M and N
     int wg_per_cu;          // workgroups resident per CU (LDS / register bound)
     double rate;            // relative per-CU throughput, measured at 8192^3
+    double overhead;        // per-tile cost that does not scale with K, in units of K
     bool persist;           // one workgroup walks several tiles
 };
 
@@ -40,22 +43,16 @@ inline bool offsets_fit(const Variant &v, const Operands &o)
 
 inline bool variant_allowed(const Variant &v, const Operands &o) { return offsets_fit(v, o); }
 
-// Per-tile cost that does not scale with K (first-panel latency, epilogue stores), in
-// units of K: fitted from the 8192^3 and 16384x16384x64 timings on MI355X. A persistent
-// variant overlaps most of it with the next tile.
-constexpr double kTileOverheadK = 52.0;
-constexpr double kTileOverheadKPersistent = 26.0;
-
 inline double variant_cost(const Variant &v, const Operands &o, int cus)
 {
     const int64_t tm = (int64_t(o.M) + v.BM - 1) / v.BM;
     const int64_t tn = (int64_t(o.N) + v.BN - 1) / v.BN;
     // the busiest CU runs ceil(tiles / CUs) tiles; each is BM*BN*K multiply-adds at the
-    // variant's measured relative rate plus the per-tile overhead
+    // variant's measured relative rate plus the variant's per-tile overhead
     const int64_t per_cu = (tm * tn * o.splits + cus - 1) / cus;
     const double k = o.K > 0 ? double(o.K) / o.splits : 1;
     return double(per_cu) * double(v.BM) * v.BN *
-           (k / v.rate + (v.persist ? kTileOverheadKPersistent : kTileOverheadK));
+           (k / v.rate + v.overhead);
 }
 
 template <int NV>

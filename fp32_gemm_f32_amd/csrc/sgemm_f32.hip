@@ -55,24 +55,28 @@ struct VariantEntry {
 };
 
 template <int BM, int BN, int BK, int WGM, int WGN, int KACC, bool PERSIST, int KG = 1>
-constexpr VariantEntry entry(const char *name, int wg_per_cu, double rate)
+constexpr VariantEntry entry(const char *name, int wg_per_cu, double rate, double overhead)
 {
-    return VariantEntry{Variant{name, BM, BN, BK, WGM, WGN, wg_per_cu, rate, PERSIST},
+    return VariantEntry{Variant{name, BM, BN, BK, WGM, WGN, wg_per_cu, rate, overhead, PERSIST},
                         &k_sgemm_mfma<BM, BN, BK, WGM, WGN, KACC, PERSIST, 1, KG>,
                         64 * WGM * WGN * KG};
 }
 
-// Rates are the variants' throughput at 8192^3 relative to 140 TFLOP/s on MI355X. The
-// 8-wave 256x256 tile comes in both forms: one tile per workgroup (fastest when K is long)
-// and persistent (its epilogue overlaps the next tile: best when K is short). The two
-// K-group variants (KG = 2: two waves per SIMD on one tile) serve shapes too small to give
-// every CU more than one tile.
+// Rates are the variants' throughput at 8192^3 relative to 140 TFLOP/s on MI355X;
+// overheads (per tile, in units of K) are fitted from the 8192^3 and 16384x16384x64
+// timings. The 8-wave 256x256 tile with one tile per workgroup is fastest when K is long.
+// When K is short the epilogue's stores dominate and must overlap MFMAs: the 128x256 tile
+// (4 waves, 48 KiB of LDS) keeps two workgroups on each CU, so one stores while the other
+// computes, and its 64 x 128 wave tile stores 16 bytes per lane. The two K-group variants
+// (KG = 2: two waves per SIMD on one tile) serve shapes too small to give every CU more
+// than one tile.
 const VariantEntry kVariants[] = {
-    entry<256, 256, 32, 2, 4, 1, false>("mfma_256x256x32_w2x4", 1, 1.03),
-    entry<256, 256, 32, 2, 4, 1, true>("mfma_256x256x32_w2x4_p", 1, 1.015),
-    entry<128, 128, 32, 2, 2, 1, true>("mfma_128x128x32_w2x2_p", 2, 0.945),
-    entry<128, 64, 32, 2, 2, 1, true, 2>("mfma_128x64x32_w2x2_kg2_p", 1, 0.85),
-    entry<64, 64, 64, 2, 2, 2, true, 2>("mfma_64x64x64_w2x2_acc2_kg2_p", 1, 0.80),
+    entry<256, 256, 32, 2, 4, 1, false>("mfma_256x256x32_w2x4", 1, 1.03, 52),
+    entry<256, 256, 32, 2, 4, 1, true>("mfma_256x256x32_w2x4_p", 1, 1.015, 26),
+    entry<128, 256, 16, 2, 2, 1, false>("mfma_128x256x16_w2x2", 2, 1.003, 17),
+    entry<128, 128, 32, 2, 2, 1, true>("mfma_128x128x32_w2x2_p", 2, 0.945, 26),
+    entry<128, 64, 32, 2, 2, 1, true, 2>("mfma_128x64x32_w2x2_kg2_p", 1, 0.85, 26),
+    entry<64, 64, 64, 2, 2, 2, true, 2>("mfma_64x64x64_w2x2_acc2_kg2_p", 1, 0.80, 26),
 };
 constexpr int kNumVariants = int(sizeof(kVariants) / sizeof(kVariants[0]));
 

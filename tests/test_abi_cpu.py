@@ -91,7 +91,7 @@ def test_variant_option_validation():
 
 @pytest.mark.parametrize("shape,expect_tile", [
     ((8192, 8192, 8192), 256),
-    ((16384, 16384, 64), 256),
+    ((16384, 16384, 64), None),
     ((1024, 1024, 1024), None),
     ((1023, 1025, 1027), None),
     ((6, 6, 9), None),
