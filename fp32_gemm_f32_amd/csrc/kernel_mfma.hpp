@@ -218,7 +218,19 @@ struct MfmaTile {
 // at the end of a tile groups 1 .. KG-1 pass their sums through LDS to group 0, which adds
 // them in ascending group order (deterministic) and stores C. This puts KG waves on each
 // SIMD for tiles too small to fill the GPU otherwise.
-template <int BM, int BN, int BK, int WGM, int WGN, int KACC, bool PERSIST, int PH, int KG>
+//
+// DL selects direct global -> LDS loads: each 16-byte buffer load writes its lane's chunk
+// straight into LDS (lane l of a wave at the wave's base + 16 l), so the next panel needs
+// no staging registers, no LDS write instructions and no wait in the middle of the panel;
+// the wave waits for its loads once, just before the panel's barrier. A lane picks the
+// global chunk that belongs at its LDS slot, which keeps the A swizzle. Out-of-range
+// lanes write zeros, as register loads return them. An A chunk that crosses K cannot be
+// cleaned on its way into LDS, so in the panel that holds the end of the K range each lane
+// zeroes the elements past K of its own chunks once they have landed, before the barrier.
+//
+// One workgroup computes one item (a tile, or a tile's K range under split-K); the grid
+// has one workgroup per item.
+template <int BM, int BN, int BK, int WGM, int WGN, int KACC, int KG, bool DL>
 __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
 {
     using T = MfmaTile<BM, BN, BK, WGM, WGN, KACC, KG>;
@@ -243,7 +255,6 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
 
     const int M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
     const int ntiles = p.tiles_m * p.tiles_n;
-    const int nitems = ntiles * p.splits;
 
     // ---- per-thread load assignment ----
     // Thread tid stages A chunks c = tid + i*NT, i.e. rows a_r0 + i*A_RSTEP at the fixed
@@ -254,7 +265,11 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     constexpr int B_KSTEP = NT / (BN / 4);
     static_assert(NT % CPR == 0 && A_RSTEP % 16 == 0 && NT % (BN / 4) == 0,
                   "chunk assignment strides");
-    const int a_r0 = tid / CPR, a_q = tid % CPR;
+    // A register-staged lane loads logical chunk tid % CPR of its row and stores it at the
+    // swizzled slot; a direct-loading lane owns LDS slot tid % CPR and loads the logical
+    // chunk that belongs there.
+    const int a_r0 = tid / CPR;
+    const int a_q = DL ? (tid % CPR) ^ a_swizzle<CPR>(a_r0) : tid % CPR;
     const uint32_t a_off0 = uint32_t(a_r0) * uint32_t(lda) * 4u + uint32_t(a_q) * 16u;
     const uint32_t a_stride = uint32_t(A_RSTEP) * uint32_t(lda) * 4u;
     const int a_lds0 = a_r0 * BK + 4 * (a_q ^ a_swizzle<CPR>(a_r0));
@@ -263,35 +278,22 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     const uint32_t b_stride = uint32_t(B_KSTEP) * uint32_t(ldb) * 4u;
     const int b_lds0 = b_k0 * BN + b_c0;
 
-    // The item whose panels are being loaded (it runs one item ahead of the item being
-    // computed during the last panel of each item): tile origin lm0, ln0, K range
-    // [lkb, lkb + lK) and split index ls.
-    int lm0 = 0, ln0 = 0, lkb = 0, lK = 0, ls = 0;
-    bool b_col_ok = false;
-    auto set_load_tile = [&](int vb) {
-        if (vb < nitems) {
-            int tm, tn;
-            ls = vb / ntiles;
-            tile_coords(vb - ls * ntiles, p.tiles_m, p.tiles_n, tm, tn);
-            lm0 = tm * BM;
-            ln0 = tn * BN;
-            lkb = ls * p.k_chunk;
-            lK = min(K - lkb, p.k_chunk);
-        } else {   // no such item: rows, columns and k past the matrix, all loads masked
-            lm0 = M;
-            ln0 = N;
-            lkb = 0;
-            lK = 0;
-            ls = 0;
-        }
-        // all wave-uniform: keep them (and the loops they bound) on the scalar unit
-        lm0 = __builtin_amdgcn_readfirstlane(lm0);
-        ln0 = __builtin_amdgcn_readfirstlane(ln0);
-        lkb = __builtin_amdgcn_readfirstlane(lkb);
-        lK = __builtin_amdgcn_readfirstlane(lK);
+    // This workgroup's item: split ls of tile item % tiles, i.e. tile origin (lm0, ln0) and
+    // K range [lkb, lkb + lK). All wave-uniform: keep them (and the loops they bound) on
+    // the scalar unit.
+    int lm0, ln0, lkb, lK, ls;
+    {
+        int tm, tn;
+        const int item = blockIdx.x;
+        ls = item / ntiles;
+        tile_coords(item - ls * ntiles, p.tiles_m, p.tiles_n, tm, tn);
+        lm0 = __builtin_amdgcn_readfirstlane(tm * BM);
+        ln0 = __builtin_amdgcn_readfirstlane(tn * BN);
+        lkb = __builtin_amdgcn_readfirstlane(ls * p.k_chunk);
+        lK = __builtin_amdgcn_readfirstlane(min(K - lkb, p.k_chunk));
         ls = __builtin_amdgcn_readfirstlane(ls);
-        b_col_ok = ln0 + b_c0 < N;
-    };
+    }
+    const bool b_col_ok = ln0 + b_c0 < N;
 
     // ---- global -> register staging of one panel ----
     f32x4 ra[A_CH], rb[B_CH];
@@ -331,19 +333,54 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
             *reinterpret_cast<f32x4 *>(As + T::A_TILE + b_lds0 + (l - A_CH) * B_KSTEP * BN) =
                 rb[l - A_CH];
     };
+    // direct load of staging slot l into stage As: A chunk tid + l * NT sits at byte
+    // 16 (tid + l * NT) of the A tile, B chunk tid + i * NT at byte 16 (tid + i * NT) of the
+    // B tile, so a wave's 64 chunks are contiguous and the wave passes its first chunk's
+    // address (uniform) as the LDS base
+    typedef __attribute__((address_space(3))) void *lds_ptr;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    // after the direct loads of a panel have landed: zero the elements past the K range in
+    // this lane's A chunks (their LDS slots are 16 (tid + l NT) bytes into the A tile). The
+    // branch is uniform and taken only in the panel that holds the end of the range.
+    auto fix_k_tail = [&](float *As) {
+        if (k_load + BK > lK && (lK & 3) != 0) {
+            const int kc = k_load + 4 * a_q;
+            if (kc < lK && kc + 4 > lK) {
+#pragma unroll
+                for (int l = 0; l < A_CH; ++l) {
+                    float *chunk = As + (tid + l * NT) * 4;
+#pragma unroll
+                    for (int e = 1; e < 4; ++e)
+                        if (kc + e >= lK) chunk[e] = 0.0f;
+                }
+            }
+        }
+    };
+    auto load_direct = [&](float *As, int l) {
+        if (l < A_CH) {
+            const int kc = k_load + 4 * a_q;
+            const bool ok = lm0 + a_r0 + l * A_RSTEP < M && kc < lK;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsa, (lds_ptr)(As + (wave_u * 64 + l * NT) * 4), 16,
+                ok ? a_off0 + uint32_t(l) * a_stride : kOob, 0, 0, 0);
+        } else {
+            const int i = l - A_CH;
+            const bool ok = k_load + b_k0 + i * B_KSTEP < lK && b_col_ok;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsb, (lds_ptr)(As + T::A_TILE + (wave_u * 64 + i * NT) * 4), 16,
+                ok ? b_off0 + uint32_t(i) * b_stride : kOob, 0, 0, 0);
+        }
+    };
 
     // KACC accumulator sets take the k-steps in turn (KACC > 1 gives a wave with few MFMA
     // blocks independent accumulation chains); they are summed before the epilogue.
     f32x16 acc[KACC][RB][CI * CG];
-    auto zero_acc = [&]() {
 #pragma unroll
-        for (int h = 0; h < KACC; ++h)
+    for (int h = 0; h < KACC; ++h)
 #pragma unroll
-            for (int i = 0; i < RB; ++i)
+        for (int i = 0; i < RB; ++i)
 #pragma unroll
-                for (int j = 0; j < CI * CG; ++j) acc[h][i][j] = f32x16{};
-    };
-    zero_acc();
+            for (int j = 0; j < CI * CG; ++j) acc[h][i][j] = f32x16{};
 
     // A-operand LDS rows of this lane: row wm*WM + rb*32 + lo, whose swizzle depends on
     // lo only (wm*WM + rb*32 is a multiple of 32).
@@ -379,20 +416,16 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     //                       stage; the MFMAs of the last step need only registers, so
     //                       they cover the latency of those reads.
     // One barrier per panel is enough: the other stage was last read before the previous
-    // panel's barrier, and this panel's reads of `cur` all precede this barrier.
-    // Staging phases: with PH = 2 the panel is staged in two halves (loads at the start of
-    // each half of the panel, LDS writes near its end), so only half the staging registers
-    // are live at a time.
+    // panel's barrier, and this panel's reads of `cur` all precede this barrier. With
+    // direct loads there are no LDS write steps; the wave waits for its loads before the
+    // barrier instead.
     constexpr int STEPS = BK / 2;
-    constexpr int NL = A_CH + B_CH;
-    constexpr int P = STEPS / PH;                       // steps per phase
-    constexpr int NP = NL / PH;                         // staging slots per phase
-    constexpr int LS = PH == 1 ? SGEMM_LOAD_STEPS : 2;  // load steps per phase
-    constexpr int WS = PH == 1 ? SGEMM_WRITE_STEPS : 2; // write steps per phase
-    constexpr int PER_LOAD = (NP + LS - 1) / LS;
-    constexpr int PER_WRITE = (NP + WS - 1) / WS;
-    static_assert(STEPS % PH == 0 && NL % PH == 0, "phases divide the panel");
-    static_assert(LS + WS < P, "loads and LDS writes of a phase need separate steps");
+    constexpr int NL = A_CH + B_CH;                     // staging slots per panel
+    constexpr int LS = SGEMM_LOAD_STEPS;
+    constexpr int WS = SGEMM_WRITE_STEPS;
+    constexpr int PER_LOAD = (NL + LS - 1) / LS;
+    constexpr int PER_WRITE = (NL + WS - 1) / WS;
+    static_assert(LS + WS < STEPS, "loads and LDS writes of a panel need separate steps");
 
     auto panel = [&](int cur, auto next_tag) {
         constexpr bool NEXT = decltype(next_tag)::value;
@@ -404,20 +437,21 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
             constexpr int kb = t >> 2, s = t & 3;
             constexpr bool next_b = t + 1 < STEPS;
             constexpr bool next_a = s == 0 && kb + 1 < BK / 8;
-            constexpr int h = t / P, u = t % P;                 // phase and step in it
-            constexpr int w0 = u - (P - 1 - WS);                // write group in the phase
-            constexpr int l_first = h * NP + u * PER_LOAD;
-            constexpr int n_load = (NEXT && u < LS)
-                ? ((u + 1) * PER_LOAD < NP ? PER_LOAD : (NP - u * PER_LOAD > 0 ? NP - u * PER_LOAD : 0))
+            constexpr int w0 = t - (STEPS - 1 - WS);            // write group of this step
+            constexpr int l_first = t * PER_LOAD;
+            constexpr int n_load = (NEXT && t < LS)
+                ? ((t + 1) * PER_LOAD < NL ? PER_LOAD : (NL - t * PER_LOAD > 0 ? NL - t * PER_LOAD : 0))
                 : 0;
-            constexpr int w_first = h * NP + (w0 > 0 ? w0 : 0) * PER_WRITE;
-            constexpr int n_write = (NEXT && w0 >= 0 && w0 < WS)
-                ? ((w0 + 1) * PER_WRITE < NP ? PER_WRITE
-                                             : (NP - w0 * PER_WRITE > 0 ? NP - w0 * PER_WRITE : 0))
+            constexpr int w_first = (w0 > 0 ? w0 : 0) * PER_WRITE;
+            constexpr int n_write = (NEXT && !DL && w0 >= 0 && w0 < WS)
+                ? ((w0 + 1) * PER_WRITE < NL ? PER_WRITE
+                                             : (NL - w0 * PER_WRITE > 0 ? NL - w0 * PER_WRITE : 0))
                 : 0;
             if constexpr (n_load > 0) {
 #pragma unroll
-                for (int l = l_first; l < l_first + n_load; ++l) load_slot(l);
+                for (int l = l_first; l < l_first + n_load; ++l) {
+                    if constexpr (DL) load_direct(Anext, l); else load_slot(l);
+                }
             }
             if constexpr (n_write > 0) {
 #pragma unroll
@@ -429,6 +463,11 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
                 // keep the previous steps' MFMAs above the barrier: they cover the
                 // completion of this panel's LDS writes
                 __builtin_amdgcn_sched_barrier(0);
+                // direct loads land in LDS when vmcnt counts them done
+                if constexpr (DL) {
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                    fix_k_tail(Anext);
+                }
                 __syncthreads();
                 read_a(Anext, 0, a[0]);
                 read_b(Anext + T::A_TILE, 0, b[0]);
@@ -560,53 +599,33 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
         }
     };
 
-    // ---- K loop over the workgroup's items; group kg takes panels kg, kg + KG, ... ----
-    int vb = blockIdx.x;
-    set_load_tile(vb);
+    // ---- K loop; group kg takes panels kg, kg + KG, ... ----
     set_panel(kg * BK);
+    if constexpr (DL) {
 #pragma unroll
-    for (int l = 0; l < NL; ++l) load_slot(l);
+        for (int l = 0; l < NL; ++l) load_direct(smem, l);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        fix_k_tail(smem);
+    } else {
 #pragma unroll
-    for (int l = 0; l < NL; ++l) write_slot(smem, l);
+        for (int l = 0; l < NL; ++l) load_slot(l);
+#pragma unroll
+        for (int l = 0; l < NL; ++l) write_slot(smem, l);
+    }
     __syncthreads();
     read_a(smem, 0, a[0]);
     read_b(smem + T::A_TILE, 0, b[0]);
 
-    if constexpr (!PERSIST) {
-        // one item per workgroup: the last round stages nothing
-        const int rounds = ((lK + BK - 1) / BK + KG - 1) / KG;
-        for (int r = 0; r + 1 < rounds; ++r) {
-            set_panel(((r + 1) * KG + kg) * BK);
-            panel(r & 1, std::true_type{});
-        }
-        panel((rounds - 1) & 1, std::false_type{});
-        finish();
-        if (kg == 0) epilogue(lm0, ln0, ls);
-    } else {
-        // Items vb, vb + G, vb + 2G, ...: the last round of an item stages the first round
-        // of the workgroup's next item, so that item's first loads and LDS writes run under
-        // the current item's MFMAs and the epilogue's stores drain while the next item
-        // computes. After the last item the staged "next item" lies past the matrix and
-        // every one of its loads is masked to zero; one panel body serves every round.
-        const int G = gridDim.x;
-        int cur = 0;
-        for (;;) {
-            const int cm0 = lm0, cn0 = ln0, cs = ls;   // the item being computed
-            const int rounds = ((lK + BK - 1) / BK + KG - 1) / KG;
-            for (int r = 0; r < rounds; ++r) {
-                const bool last = r + 1 == rounds;
-                if (last) set_load_tile(vb + G);
-                set_panel(((last ? 0 : r + 1) * KG + kg) * BK);
-                panel(cur, std::true_type{});
-                cur ^= 1;
-            }
-            finish();
-            if (kg == 0) epilogue(cm0, cn0, cs);
-            vb += G;
-            if (vb >= nitems) break;
-            zero_acc();
-        }
+    // the last round stages nothing; a group whose last panel lies past the K range loads
+    // only zeros for it
+    const int rounds = ((lK + BK - 1) / BK + KG - 1) / KG;
+    for (int r = 0; r + 1 < rounds; ++r) {
+        set_panel(((r + 1) * KG + kg) * BK);
+        panel(r & 1, std::true_type{});
     }
+    panel((rounds - 1) & 1, std::false_type{});
+    finish();
+    if (kg == 0) epilogue(lm0, ln0, ls);
 }
 
 // C[i][j] = sum over s of W[s * stride + i * N + j], in ascending s: the second pass of

@@ -7,8 +7,8 @@
 // estimates, for each variant the operands allow, the time of the busiest compute unit,
 //     ceil(tiles / CUs) x (work of one tile / the variant's measured rate + per-tile overhead),
 // and takes the smallest. The overhead (first-panel latency and epilogue stores not hidden
-// behind MFMAs) depends on the variant: a persistent workgroup overlaps it with its next
-// tile, and two resident workgroups per CU overlap one's epilogue with the other's MFMAs.
+// behind MFMAs) depends on the variant: with two resident workgroups per CU one's epilogue
+// overlaps the other's MFMAs.
 #pragma once
 
 #include <cstdint>
@@ -20,10 +20,10 @@ struct Variant {
     const char *name;
     int BM, BN, BK;
     int wgm, wgn;           // waves along M and N
-    int wg_per_cu;          // workgroups resident per CU (LDS / register bound)
+    int wg_per_cu;          // workgroups resident per CU (LDS / register bound), reported
     double rate;            // relative per-CU throughput, measured at 8192^3
     double overhead;        // per-tile cost that does not scale with K, in units of K
-    bool persist;           // one workgroup walks several tiles
+    bool direct;            // direct global -> LDS loads
 };
 
 struct Operands {

@@ -54,29 +54,31 @@ struct VariantEntry {
     int threads;
 };
 
-template <int BM, int BN, int BK, int WGM, int WGN, int KACC, bool PERSIST, int KG = 1>
+template <int BM, int BN, int BK, int WGM, int WGN, int KACC, int KG, bool DL>
 constexpr VariantEntry entry(const char *name, int wg_per_cu, double rate, double overhead)
 {
-    return VariantEntry{Variant{name, BM, BN, BK, WGM, WGN, wg_per_cu, rate, overhead, PERSIST},
-                        &k_sgemm_mfma<BM, BN, BK, WGM, WGN, KACC, PERSIST, 1, KG>,
+    return VariantEntry{Variant{name, BM, BN, BK, WGM, WGN, wg_per_cu, rate, overhead, DL},
+                        &k_sgemm_mfma<BM, BN, BK, WGM, WGN, KACC, KG, DL>,
                         64 * WGM * WGN * KG};
 }
 
-// Rates are the variants' throughput at 8192^3 relative to 140 TFLOP/s on MI355X;
-// overheads (per tile, in units of K) are fitted from the 8192^3 and 16384x16384x64
-// timings. The 8-wave 256x256 tile with one tile per workgroup is fastest when K is long.
-// When K is short the epilogue's stores dominate and must overlap MFMAs: the 128x256 tile
-// (4 waves, 48 KiB of LDS) keeps two workgroups on each CU, so one stores while the other
-// computes, and its 64 x 128 wave tile stores 16 bytes per lane. The two K-group variants
-// (KG = 2: two waves per SIMD on one tile) serve shapes too small to give every CU more
-// than one tile.
+// Rates (throughput at 8192^3 relative to 140 TFLOP/s) and per-tile overheads (in units of
+// K) are fitted on MI355X to the timings of eleven shapes from 1024^3 to 16384^2 x 64; the
+// plan then picks the measured best, or one within 2 % of it, on each of them. Every
+// variant but one loads its panels straight into LDS ("_dl"), which measured faster than
+// staging through registers on all of these shapes except the shortest K: at K = 64 the
+// register-staged 128 x 256 tile wins. The 256 x 256 tile (8 waves) is fastest when K is
+// long. The 128 x 256 tile (4 waves, 48 KiB of LDS) keeps two workgroups on each CU, so one
+// stores while the other computes, and its 64 x 128 wave tile stores 16 bytes per lane:
+// best when K is short. The two K-group variants (KG = 2: two waves per SIMD on one tile)
+// serve shapes too small to give every CU more than one tile.
 const VariantEntry kVariants[] = {
-    entry<256, 256, 32, 2, 4, 1, false>("mfma_256x256x32_w2x4", 1, 1.03, 52),
-    entry<256, 256, 32, 2, 4, 1, true>("mfma_256x256x32_w2x4_p", 1, 1.015, 26),
-    entry<128, 256, 16, 2, 2, 1, false>("mfma_128x256x16_w2x2", 2, 1.003, 17),
-    entry<128, 128, 32, 2, 2, 1, true>("mfma_128x128x32_w2x2_p", 2, 0.945, 26),
-    entry<128, 64, 32, 2, 2, 1, true, 2>("mfma_128x64x32_w2x2_kg2_p", 1, 0.85, 26),
-    entry<64, 64, 64, 2, 2, 2, true, 2>("mfma_64x64x64_w2x2_acc2_kg2_p", 1, 0.80, 26),
+    entry<256, 256, 32, 2, 4, 1, 1, true>("mfma_256x256x32_w2x4_dl", 1, 1.055, 48),
+    entry<128, 256, 16, 2, 2, 1, 1, false>("mfma_128x256x16_w2x2", 2, 0.97, 16),
+    entry<128, 256, 16, 2, 2, 1, 1, true>("mfma_128x256x16_w2x2_dl", 2, 1.0, 20),
+    entry<128, 128, 32, 2, 2, 1, 1, true>("mfma_128x128x32_w2x2_dl", 2, 0.97, 16),
+    entry<128, 64, 32, 2, 2, 1, 2, true>("mfma_128x64x32_w2x2_kg2_dl", 1, 0.92, 90),
+    entry<64, 64, 64, 2, 2, 2, 2, true>("mfma_64x64x64_w2x2_acc2_kg2_dl", 1, 0.85, 144),
 };
 constexpr int kNumVariants = int(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -111,10 +113,9 @@ int device_cus(int *out)
     return SGEMM_OK;
 }
 
-// A persistent variant runs a grid of at most CUs x (workgroups per CU), each workgroup
-// taking every grid-th tile; the others run one workgroup per tile.
+// One workgroup per tile.
 int run_variant(int vi, const Operands &o, const float *A, const float *B, float *C,
-                void *stream, int cus)
+                void *stream)
 {
     const VariantEntry &e = kVariants[vi];
     GemmArgs p;
@@ -130,9 +131,7 @@ int run_variant(int vi, const Operands &o, const float *A, const float *B, float
     p.c_split_stride = 0;
     const int64_t tiles = int64_t(p.tiles_m) * p.tiles_n;
     if (tiles > INT32_MAX) return SGEMM_ETOO_LARGE;
-    const int64_t slots = int64_t(cus) * e.v.wg_per_cu;
-    const int64_t grid = (e.v.persist && tiles > slots) ? slots : tiles;
-    return launch(e.kern, dim3(unsigned(grid)), dim3(e.threads), stream, p);
+    return launch(e.kern, dim3(unsigned(tiles)), dim3(e.threads), stream, p);
 }
 
 // Split-K geometry: K is cut into `splits` ranges of whole BK panels (the last may be
@@ -183,9 +182,7 @@ int run_splitk(int splits, const Operands &o0, const float *A, const float *B, f
     p.c_split_stride = mn;
     const int64_t items = int64_t(p.tiles_m) * p.tiles_n * eff;
     if (items > INT32_MAX) return SGEMM_ETOO_LARGE;
-    const int64_t slots = int64_t(cus) * e.v.wg_per_cu;
-    const int64_t grid = (e.v.persist && items > slots) ? slots : items;
-    int st = launch(e.kern, dim3(unsigned(grid)), dim3(e.threads), stream, p);
+    int st = launch(e.kern, dim3(unsigned(items)), dim3(e.threads), stream, p);
     if (st != SGEMM_OK) return st;
     const bool w_vec = (o.N % 4 == 0) && (reinterpret_cast<uintptr_t>(W) % 16 == 0);
     const int c_vec = (o.ldc % 4 == 0) && (reinterpret_cast<uintptr_t>(C) % 16 == 0);
@@ -214,7 +211,7 @@ int run_hot(int variant, int M, int N, int K, const float *A, int lda, const flo
     if (qs != SGEMM_OK) return qs;
     const int vi = variant >= 0 ? variant : choose_variant(g_table, o, cus);
     if (vi < 0) return SGEMM_ETOO_LARGE;
-    return run_variant(vi, o, A, B, C, stream, cus);
+    return run_variant(vi, o, A, B, C, stream);
 }
 
 }  // namespace
@@ -398,18 +395,18 @@ extern "C" int sgemm_f32_plan_describe(int M, int N, int K, const float *A, int 
     if (vi < 0) return SGEMM_ETOO_LARGE;
     const Variant &v = kVariants[vi].v;
     const int64_t tm = (int64_t(M) + v.BM - 1) / v.BM, tn = (int64_t(N) + v.BN - 1) / v.BN;
-    const int64_t slots = int64_t(cus) * v.wg_per_cu;
-    const int64_t grid = (v.persist && tm * tn > slots) ? slots : tm * tn;
+    const int64_t grid = tm * tn;
     // operand bytes the tiles request: every A row panel once per tile column and every
     // B column panel once per tile row (before any cache reuse)
     const int64_t tile_bytes = 4 * (int64_t(M) * K * tn + int64_t(K) * N * tm);
     const int n = snprintf(buf, size_t(buflen),
                            "{\"variant\": %d, \"name\": \"%s\", \"BM\": %d, \"BN\": %d, "
                            "\"BK\": %d, \"waves\": [%d, %d], \"threads\": %d, \"grid\": %lld, "
-                           "\"tiles\": [%lld, %lld], \"cus\": %d, \"tile_request_bytes\": %lld}",
+                           "\"tiles\": [%lld, %lld], \"cus\": %d, \"wg_per_cu\": %d, "
+                           "\"direct_loads\": %s, \"tile_request_bytes\": %lld}",
                            vi, v.name, v.BM, v.BN, v.BK, v.wgm, v.wgn, kVariants[vi].threads,
-                           (long long)grid, (long long)tm, (long long)tn, cus,
-                           (long long)tile_bytes);
+                           (long long)grid, (long long)tm, (long long)tn, cus, v.wg_per_cu,
+                           v.direct ? "true" : "false", (long long)tile_bytes);
     if (n < 0 || n >= buflen) return SGEMM_EINVAL_ARG;
     return vi;
 }

@@ -101,8 +101,8 @@ def test_plan(shape, expect_tile):
     plan = g.sgemm_f32_plan_describe(M, N, K, P, None, P + (1 << 30), None, P + (1 << 31), None,
                                      num_cus=256)
     tiles = plan["tiles"][0] * plan["tiles"][1]
-    # a persistent variant launches at most (CUs x workgroups per CU) workgroups
-    assert plan["grid"] == tiles or (plan["name"].endswith("_p") and plan["grid"] < tiles)
+    assert plan["grid"] == tiles            # one workgroup per tile
+    assert plan["direct_loads"] == plan["name"].endswith("_dl")
     assert plan["tiles"][0] * plan["BM"] >= M and plan["tiles"][1] * plan["BN"] >= N
     if expect_tile:
         assert plan["BM"] == plan["BN"] == expect_tile
@@ -159,3 +159,4 @@ def test_splitk_validation_and_workspace_size():
                                 None) == -1
     assert lib.sgemm_f32_splitk(0, 48, 4096, P, 4096, P + 4096, 48, P + 8192, 48, 4, ws, need,
                                 None) == 0
+

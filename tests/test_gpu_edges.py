@@ -26,7 +26,9 @@ SIZES = [1, 2, 3, 5, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 257]
 SHAPES = sorted({(s, 65, 33) for s in SIZES} | {(65, s, 33) for s in SIZES} |
                 {(65, 33, s) for s in SIZES} |
                 {(257, 255, 129), (129, 257, 255), (300, 520, 9), (7, 600, 600),
-                 (600, 7, 600), (513, 511, 68), (260, 260, 260)})
+                 (600, 7, 600), (513, 511, 68), (260, 260, 260),
+                 # K % 4 == 0 but not a multiple of the panel depth
+                 (65, 33, 4), (65, 33, 36), (33, 300, 100), (270, 130, 20)})
 
 
 def kernels_for():
@@ -55,7 +57,8 @@ def test_ragged_shapes_padded_and_guarded(gpu, M, N, K):
             exact_check(A, B, c.result(), (M, N, K, lda, ldb, ldc, kern))
 
 
-@pytest.mark.parametrize("M,N,K", [(257, 129, 65), (64, 64, 64), (1, 1, 1), (300, 301, 302)])
+@pytest.mark.parametrize("M,N,K", [(257, 129, 65), (64, 64, 64), (1, 1, 1), (300, 301, 302),
+                                   (300, 260, 132)])
 def test_misaligned_pointers(gpu, M, N, K):
     """Bases one or three floats past 16-byte alignment: every kernel still works (the hot
     kernel's 16-byte buffer loads and stores only need 4-byte alignment)."""
