@@ -201,9 +201,10 @@ struct MfmaTile {
     static constexpr int A_TILE = BM * BK;       // floats per A stage
     static constexpr int B_TILE = BK * BN;       // floats per B stage
     static constexpr int STAGE = A_TILE + B_TILE;
-    // partial sums of K-groups 1 .. KG-1, handed to group 0 at the end of each item
+    // partial sums of K-groups 1 .. KG-1, handed to group 0 after the last panel; they reuse
+    // the stages' memory
     static constexpr int RED = (KG - 1) * kGroupThreads * NACC * 16;
-    static constexpr int LDS_FLOATS = 2 * KG * STAGE + RED;
+    static constexpr int LDS_FLOATS = 2 * KG * STAGE > RED ? 2 * KG * STAGE : RED;
     static constexpr int LDS_BYTES = LDS_FLOATS * 4;
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile is made of 32 x 32 blocks");
     static_assert(WN % (32 * CI) == 0, "column groups");
@@ -251,7 +252,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     // this group's stages: stage s at smem + s * KG * STAGE
     float *const smem = lds_all + kg * T::STAGE;
     constexpr int SSTRIDE = KG * T::STAGE;
-    float *const red = lds_all + 2 * KG * T::STAGE;
+    float *const red = lds_all;   // K-group sums, written once every stage is read
 
     const int M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
     const int ntiles = p.tiles_m * p.tiles_n;
@@ -511,7 +512,9 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
 #pragma unroll
                 for (int j = 0; j < CI * CG; ++j) acc[0][i][j] += acc[h][i][j];
         if constexpr (KG > 1) {
-            // group g > 0 writes quad q of its sums at red[((g-1) * NACC * 4 + q) * NT + tid]
+            // every group has read its stages for the last time before red overwrites them;
+            // then group g > 0 writes quad q of its sums at red[((g-1) * NACC * 4 + q) * NT + tid]
+            __syncthreads();
             if (kg > 0) {
 #pragma unroll
                 for (int i = 0; i < RB; ++i)

@@ -24,6 +24,7 @@ struct Variant {
     double rate;            // relative per-CU throughput, measured at 8192^3
     double overhead;        // per-tile cost that does not scale with K, in units of K
     bool direct;            // direct global -> LDS loads
+    bool planned;           // candidate for the automatic choice (else forced use only)
 };
 
 struct Operands {
@@ -62,7 +63,7 @@ inline int choose_variant(const Variant (&table)[NV], const Operands &o, int cus
     double best_cost = 0.0;
     for (int i = 0; i < NV; ++i) {
         const Variant &v = table[i];
-        if (!variant_allowed(v, o)) continue;
+        if (!v.planned || !variant_allowed(v, o)) continue;
         const double c = variant_cost(v, o, cus);
         if (best < 0 || c < best_cost) { best = i; best_cost = c; }
     }
