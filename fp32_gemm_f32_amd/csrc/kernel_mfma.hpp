@@ -30,7 +30,8 @@
 //  * Every lane loads 16 bytes (four consecutive floats of a row) per buffer load. gfx950
 //    serves 16-byte buffer loads and stores at any 4-byte aligned address, so odd leading
 //    dimensions need no narrower path. When K % 4 != 0 the last chunk of an A row is only
-//    partly inside the matrix; its elements past K are replaced by zero after the load.
+//    partly inside the matrix; its elements past K are replaced by zero (in registers on
+//    the way to LDS, or in LDS after a direct load has landed).
 //  * C is written through a buffer resource too: rows past M get the voffset kOob and the
 //    hardware drops the store; a chunk of columns that crosses N is stored element by
 //    element.

@@ -149,9 +149,12 @@ int sgemm_f32_lds_transpose(int rows, int cols,
 /*
  * The hot kernel with a fixed tile variant instead of the automatic choice (for tests
  * and tuning). variant < 0 is the automatic choice (same as sgemm_f32); otherwise an
- * index below sgemm_f32_variant_count(), else SGEMM_EINVAL_ARG. A variant whose 31-bit
- * buffer offsets cannot span one workgroup's rows of A or C or one K-panel of B returns
- * SGEMM_ETOO_LARGE.
+ * index below sgemm_f32_variant_count(), else SGEMM_EINVAL_ARG. Every variant computes
+ * the same product for every shape; they differ in tile shape, waves and how panels reach
+ * LDS (names ending in "_dl" load straight from global memory into LDS, the others stage
+ * through registers), and some are never chosen automatically (kept for comparison). A
+ * variant whose 31-bit buffer offsets cannot span one workgroup's rows of A or C or one
+ * K-panel of B returns SGEMM_ETOO_LARGE.
  */
 int sgemm_f32_variant(int variant, int M, int N, int K,
                       const float *A, int lda,
@@ -169,7 +172,8 @@ const char *sgemm_f32_status_string(int status);
 /*
  * Writes a one-line JSON description of the plan sgemm_f32 would run for these
  * arguments into buf (at most buflen bytes including the NUL): variant, tile shape,
- * grid and the operand bytes the tiles request. Pointers are used for their
+ * waves, grid, workgroups resident per CU, whether panels load straight into LDS, and
+ * the operand bytes the tiles request. Pointers are used for their
  * alignment only and are never dereferenced. num_cus > 0 plans for that many compute
  * units; num_cus <= 0 queries the current device (SGEMM_ELAUNCH if none). Returns the
  * variant index (>= 0), or a negative sgemm_status (buffer too small: SGEMM_EINVAL_ARG).
