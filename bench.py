@@ -44,11 +44,38 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def strip_comments(src: str) -> str:
+    """C++ source without comments, each line's whitespace collapsed (string literals kept)."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c == '"':
+            j = i + 1
+            while j < n and src[j] != '"':
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    lines = (" ".join(line.split()) for line in "".join(out).splitlines())
+    return "\n".join(line for line in lines if line)
+
+
 def kernel_sources_hash() -> str:
+    """Hash of the kernel and plan sources with comments and layout removed: the counters
+    in profiles/hbm_traffic.json stay valid across comment edits, not across code edits."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(strip_comments(f.read()).encode())
     return h.hexdigest()[:16]
 
 
@@ -172,8 +199,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        log("bench.py: this build measures one GPU only; multi-GPU runs are not supported "
-            "(the product shards by output tiles, see the design notes)")
+        log("bench.py: runs on one GPU only; more than one GPU is not supported (a multi-GPU "
+            "product would shard C by output tiles, each GPU running this kernel on its share)")
         return 2
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib, max(args.steps, 1))
