@@ -88,3 +88,31 @@ def test_every_variant_on_configs(gpu, name):
         gpu.cuda.synchronize()
         rep = oracle.check(A, B, c.result())
         assert rep["n_inexact"] == 0 and rep["n_nonfinite"] == 0, (vname, rep)
+
+
+@pytest.mark.parametrize("M,N,K", [(2048, 2048, 2048), (3000, 3000, 3000), (16384, 16384, 256),
+                                   (4096, 4096, 4096)])
+def test_planned_variants_at_scale(gpu, M, N, K):
+    """Every tile variant the plan picks, at a size where it picks it (the mid-size shapes
+    of the plan's fit), on small-integer inputs: exact on sampled rows at tile edges."""
+    plan = g.sgemm_f32_plan_describe(M, N, K)
+    rng = np.random.default_rng(M + 3 * N + 7 * K)
+    A = wl.draw(rng, (M, K), "int")
+    B = wl.draw(rng, (K, N), "int")
+    _, dA, lda = device_matrix(A)
+    _, dB, ldb = device_matrix(B)
+    c = GuardedC(M, N)
+    print(f"[parity] {M}x{N}x{K} int auto -> {plan['name']}", flush=True)
+    run_kernel("auto", M, N, K, dA, lda, dB, ldb, c)
+    gpu.cuda.synchronize()
+    rep = oracle.check(A, B, c.result(), rows=sample_rows(M, 16, seed=M))
+    assert rep["n_nonfinite"] == 0 and rep["n_inexact"] == 0, (plan["name"], rep)
+
+
+def test_plan_covers_every_planned_variant(gpu):
+    """The shapes above, with the five workloads, reach every variant the plan can pick."""
+    shapes = [(2048, 2048, 2048), (3000, 3000, 3000), (16384, 16384, 256), (4096, 4096, 4096)]
+    shapes += [(w.M, w.N, w.K) for w in wl.WORKLOADS.values()]
+    picked = {g.sgemm_f32_plan_describe(*s)["name"] for s in shapes}
+    planned = {n for n in g.variant_names() if n.endswith("_dl")}
+    assert planned <= picked, planned - picked
