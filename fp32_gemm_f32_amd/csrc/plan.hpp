@@ -8,7 +8,9 @@
 //     ceil(tiles / CUs) x (work of one tile / the variant's measured rate + per-tile overhead),
 // and takes the smallest. The overhead (first-panel latency and epilogue stores not hidden
 // behind MFMAs) depends on the variant: with two resident workgroups per CU one's epilogue
-// overlaps the other's MFMAs.
+// overlaps the other's MFMAs. Such a variant runs slower when the busiest CU gets fewer
+// tiles than it can hold at once (it then lacks the second workgroup to overlap with); its
+// rate is scaled by `solo` in that case.
 #pragma once
 
 #include <cstdint>
@@ -20,9 +22,10 @@ struct Variant {
     const char *name;
     int BM, BN, BK;
     int wgm, wgn;           // waves along M and N
-    int wg_per_cu;          // workgroups resident per CU (LDS / register bound), reported
+    int wg_per_cu;          // workgroups resident per CU (LDS / register bound)
     double rate;            // relative per-CU throughput, measured at 8192^3
     double overhead;        // per-tile cost that does not scale with K, in units of K
+    double solo;            // rate factor when a CU holds fewer than wg_per_cu tiles
     bool direct;            // direct global -> LDS loads
     bool planned;           // candidate for the automatic choice (else forced use only)
 };
@@ -52,8 +55,8 @@ inline double variant_cost(const Variant &v, const Operands &o, int cus)
     // variant's measured relative rate plus the variant's per-tile overhead
     const int64_t per_cu = (tm * tn * o.splits + cus - 1) / cus;
     const double k = o.K > 0 ? double(o.K) / o.splits : 1;
-    return double(per_cu) * double(v.BM) * v.BN *
-           (k / v.rate + v.overhead);
+    const double rate = per_cu >= v.wg_per_cu ? v.rate : v.rate * v.solo;
+    return double(per_cu) * double(v.BM) * v.BN * (k / rate + v.overhead);
 }
 
 template <int NV>

@@ -56,36 +56,36 @@ struct VariantEntry {
 
 template <int BM, int BN, int BK, int WGM, int WGN, int KACC, int KG, bool DL>
 constexpr VariantEntry entry(const char *name, int wg_per_cu, double rate, double overhead,
-                             bool planned = true)
+                             double solo, bool planned = true)
 {
     return VariantEntry{
-        Variant{name, BM, BN, BK, WGM, WGN, wg_per_cu, rate, overhead, DL, planned},
+        Variant{name, BM, BN, BK, WGM, WGN, wg_per_cu, rate, overhead, solo, DL, planned},
         &k_sgemm_mfma<BM, BN, BK, WGM, WGN, KACC, KG, DL>, 64 * WGM * WGN * KG};
 }
 
-// Rates (throughput at 8192^3 relative to 140 TFLOP/s) and per-tile overheads (in units of
-// K) are fitted on MI355X to one run that timed every variant on eleven shapes from 1024^3
-// to 16384^2 x 64; the plan then picks the measured best on ten of them and a variant
-// within 1 % of it on the eleventh. All planned variants load their panels straight into
-// LDS ("_dl"), which measured as fast as or faster than staging through registers on every
-// one of those shapes.
+// Rates (throughput at 8192^3 relative to 140 TFLOP/s), per-tile overheads (in units of K)
+// and solo factors are fitted on MI355X to one run that timed every variant on twelve
+// shapes from 1024^3 to 16384^2 x 64; the plan then picks the measured best on nine of
+// them and a variant within 0.7 % of it on the other three. All planned variants load
+// their panels straight into LDS ("_dl"), which measured as fast as or faster than staging
+// through registers on every one of those shapes.
 //  * 256 x 256 (8 waves of 64 x 128): long K and many tiles.
 //  * 128 x 256 (4 waves, 48 KiB of LDS): two workgroups per CU, so one stores while the
 //    other computes; best when K is short and C's stores weigh as much as the MFMAs.
-//  * 128 x 128: shapes with about one 256 x 256 tile per CU or fewer.
-//  * K-group variants (KG > 1: several waves per SIMD on one tile) for shapes too small to
-//    give every CU more than one tile; the 64 x 64 one runs four K-groups of two 32 x 64
-//    waves, two MFMAs per k-step each, which hides the operand reads' LDS latency better
-//    than one 32 x 32 MFMA block per wave.
+//  * 128 x 128 (4 waves, two per CU): shapes with about one 256 x 256 tile per CU or fewer.
+//  * 64 x 64 as four K-groups of two 32 x 64 waves (several waves per SIMD on one tile,
+//    two MFMAs per k-step each): shapes that give every CU about one tile.
+//  * 64 x 64 as two K-groups, two workgroups per CU: shapes with a few such tiles per CU,
+//    and ragged ones whose tile count just exceeds the CU count.
 // The last entry stages through registers; it is never planned and stays as the measured
 // comparison for the direct loads (forced through sgemm_f32_variant).
 const VariantEntry kVariants[] = {
-    entry<256, 256, 32, 4, 2, 1, 1, true>("mfma_256x256x32_w4x2_dl", 1, 1.07, 46),
-    entry<128, 256, 16, 2, 2, 1, 1, true>("mfma_128x256x16_w2x2_dl", 2, 0.99, 20),
-    entry<128, 128, 32, 2, 2, 1, 1, true>("mfma_128x128x32_w2x2_dl", 2, 0.96, 28),
-    entry<128, 64, 32, 2, 2, 1, 2, true>("mfma_128x64x32_w2x2_kg2_dl", 1, 0.91, 84),
-    entry<64, 64, 32, 2, 1, 2, 4, true>("mfma_64x64x32_w2x1_acc2_kg4_dl", 1, 0.90, 216),
-    entry<256, 256, 32, 4, 2, 1, 1, false>("mfma_256x256x32_w4x2", 1, 1.045, 52, false),
+    entry<256, 256, 32, 4, 2, 1, 1, true>("mfma_256x256x32_w4x2_dl", 1, 1.055, 40, 1.0),
+    entry<128, 256, 16, 2, 2, 1, 1, true>("mfma_128x256x16_w2x2_dl", 2, 1.02, 24, 0.94),
+    entry<128, 128, 32, 2, 2, 1, 1, true>("mfma_128x128x32_w2x2_dl", 2, 1.01, 32, 0.90),
+    entry<64, 64, 32, 2, 1, 2, 4, true>("mfma_64x64x32_w2x1_acc2_kg4_dl", 1, 0.89, 212, 1.0),
+    entry<64, 64, 32, 2, 1, 1, 2, true>("mfma_64x64x32_w2x1_kg2_dl", 2, 0.915, 64, 0.80),
+    entry<256, 256, 32, 4, 2, 1, 1, false>("mfma_256x256x32_w4x2", 1, 1.045, 52, 1.0, false),
 };
 constexpr int kNumVariants = int(sizeof(kVariants) / sizeof(kVariants[0]));
 
