@@ -13,7 +13,8 @@ Prints one JSON line on stdout:
                launch time) against the MI355X FP32 matrix peak; for a workload whose
                HBM floor is the larger one, GB/s of compulsory bytes against 8 TB/s.
                traffic = measured HBM bytes per launch from the committed rocprofv3
-               counter summary, or null if the kernel sources changed since then.
+               counter summary, or null unless it was taken on the same gfx950 machine
+               code and the same tile variant as this run.
   cpu_baseline the CPU oracle (fp64 triple loop) timed on this host on a bounded sample
                of rows of the same product; the same rows of the GPU result are checked
                against it.
@@ -25,6 +26,7 @@ import argparse
 import hashlib
 import json
 import os
+import struct
 import sys
 import time
 
@@ -35,8 +37,7 @@ if ROOT not in sys.path:
 PEAK_FP32_MFMA_TFLOPS = 157.3     # MI355X dense FP32 matrix peak
 PEAK_HBM_GBS = 8000.0             # MI355X HBM3E
 PEAK_FP32_VALU_TFLOPS = 78.6      # MI355X FP32 vector FMA without packed FP32
-KERNEL_SOURCES = ["fp32_gemm_f32_amd/csrc/kernel_mfma.hpp", "fp32_gemm_f32_amd/csrc/plan.hpp",
-                  "fp32_gemm_f32_amd/csrc/sgemm_f32.hip"]
+LIB_PATH = os.path.join(ROOT, "fp32_gemm_f32_amd", "libsgemm_f32.so")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
@@ -44,50 +45,58 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def strip_comments(src: str) -> str:
-    """C++ source without comments, each line's whitespace collapsed (string literals kept)."""
-    out, i, n = [], 0, len(src)
-    while i < n:
-        c = src[i]
-        if src.startswith("//", i):
-            j = src.find("\n", i)
-            i = n if j < 0 else j
-        elif src.startswith("/*", i):
-            j = src.find("*/", i + 2)
-            i = n if j < 0 else j + 2
-            out.append(" ")
-        elif c == '"':
-            j = i + 1
-            while j < n and src[j] != '"':
-                j += 2 if src[j] == "\\" else 1
-            out.append(src[i:j + 1])
-            i = j + 1
-        else:
-            out.append(c)
-            i += 1
-    lines = (" ".join(line.split()) for line in "".join(out).splitlines())
-    return "\n".join(line for line in lines if line)
+def _elf_sections(data: bytes) -> dict:
+    """Section name -> bytes of a little-endian ELF64 image (only what the hash below needs)."""
+    shoff, = struct.unpack_from("<Q", data, 0x28)
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", data, 0x3A)
+    hdr = lambda i: struct.unpack_from("<IIQQQQIIQQ", data, shoff + i * shentsize)
+    strtab = hdr(shstrndx)
+    names = data[strtab[4]:strtab[4] + strtab[5]]
+    out = {}
+    for i in range(shnum):
+        h = hdr(i)
+        out[names[h[0]:names.index(b"\0", h[0])].decode()] = data[h[4]:h[4] + h[5]]
+    return out
 
 
-def kernel_sources_hash() -> str:
-    """Hash of the kernel and plan sources with comments and layout removed: the counters
-    in profiles/hbm_traffic.json stay valid across comment edits, not across code edits."""
+def kernel_code_hash(lib_path: str = LIB_PATH):
+    """Hash of the gfx950 machine code in the built library: the .text (instructions) and
+    .rodata (kernel descriptors: registers, LDS) of the device code object inside the
+    library's offload bundle. Comments, asserts and the build directory do not change it;
+    any change to what the GPU executes does. None when the library is not built."""
+    try:
+        with open(lib_path, "rb") as f:
+            fat = _elf_sections(f.read())[".hip_fatbin"]
+    except (OSError, KeyError, struct.error):
+        return None
+    if not fat.startswith(b"__CLANG_OFFLOAD_BUNDLE__"):
+        return None
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
-            h.update(strip_comments(f.read()).encode())
+    n, = struct.unpack_from("<Q", fat, 24)
+    off = 32
+    for _ in range(n):
+        o, size, tlen = struct.unpack_from("<QQQ", fat, off)
+        off += 24
+        triple = fat[off:off + tlen].decode()
+        off += tlen
+        if "gfx950" in triple:
+            secs = _elf_sections(fat[o:o + size])
+            h.update(secs[".text"])
+            h.update(secs[".rodata"])
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch from the committed counter summary, if it is current."""
+def measured_traffic(workload: str, variant: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the
+    machine code that runs now and on the variant the plan picks now."""
     try:
         with open(TRAFFIC_FILE) as f:
             data = json.load(f)
     except (OSError, ValueError):
         return None
     entry = data.get(workload)
-    if not entry or entry.get("kernel_sources_sha") != kernel_sources_hash():
+    if (not entry or entry.get("kernel_code_sha") != kernel_code_hash()
+            or entry.get("variant") != variant):
         return None
     return entry.get("bytes_per_launch")
 
@@ -298,7 +307,8 @@ def main() -> int:
         achieved = compulsory / (ms / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    roof["traffic"] = measured_traffic(args.workload) if kern == "auto" else None
+    roof["traffic"] = (measured_traffic(args.workload, plan["name"])
+                       if kern == "auto" and args.variant < 0 else None)
     roof["kernel"] = plan["name"]
 
     cpu = None

@@ -169,6 +169,15 @@ __host__ __device__ constexpr int a_swizzle(int r)
                     : (((r >> 2) ^ (r >> 3)) & 1);
 }
 
+// Rows after which a_swizzle<CPR> repeats. The kernel relies on it twice: all A chunks one
+// thread stages lie a multiple of it apart (one swizzle per thread), and the rows one lane
+// reads lie 32 apart (so 32 must be a multiple of it).
+template <int CPR>
+__host__ __device__ constexpr int a_swizzle_period()
+{
+    return CPR == 4 ? 32 : 16;
+}
+
 // Tile coordinates of workgroup bid: a contiguous range of tiles per XCD, then groups of
 // kGroupM tile rows walked column by column.
 __device__ inline void tile_coords(int bid, int tiles_m, int tiles_n, int &tm, int &tn)
@@ -261,12 +270,14 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     // ---- per-thread load assignment ----
     // Thread tid stages A chunks c = tid + i*NT, i.e. rows a_r0 + i*A_RSTEP at the fixed
     // k-columns 4*a_q .. +3, and B chunks at panel rows b_k0 + i*B_KSTEP, fixed columns
-    // b_c0 .. +3. Because A_RSTEP is a multiple of 16 rows, every A chunk of a thread has
-    // the same swizzle, so all offsets are one base plus a compile-time stride.
+    // b_c0 .. +3. Because A_RSTEP is a multiple of the swizzle's period, every A chunk of a
+    // thread has the same swizzle, so all offsets are one base plus a compile-time stride.
     constexpr int A_RSTEP = NT / CPR;
     constexpr int B_KSTEP = NT / (BN / 4);
-    static_assert(NT % CPR == 0 && A_RSTEP % 16 == 0 && NT % (BN / 4) == 0,
+    static_assert(NT % CPR == 0 && A_RSTEP % a_swizzle_period<CPR>() == 0 &&
+                      NT % (BN / 4) == 0,
                   "chunk assignment strides");
+    static_assert(32 % a_swizzle_period<CPR>() == 0, "a lane's A rows share one swizzle");
     // A register-staged lane loads logical chunk tid % CPR of its row and stores it at the
     // swizzled slot; a direct-loading lane owns LDS slot tid % CPR and loads the logical
     // chunk that belongs there.

@@ -1,5 +1,5 @@
-"""Host-side pieces of bench.py: the JSON contract's fixed fields, the multi-GPU refusal and
-the kernel-source hash that decides whether the committed HBM counters still apply."""
+"""Host-side pieces of bench.py: the multi-GPU refusal and the machine-code hash that decides
+whether the committed HBM counters still apply."""
 import json
 import subprocess
 import sys
@@ -10,18 +10,23 @@ import bench
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def test_strip_comments_ignores_comments_and_layout():
-    a = 'int f(int x) { // add one\n  return x + 1; /* done */ }\nconst char *s = "// not a comment";\n'
-    b = 'int f(int x)\n{\n    return x + 1;\n}\n/* a new\n   block comment */\nconst char *s = "// not a comment";'
-    assert bench.strip_comments(a).split() == bench.strip_comments(b).split()
-    assert '"// not a comment"' in bench.strip_comments(a)
-    c = a.replace("x + 1", "x + 2")
-    assert bench.strip_comments(c) != bench.strip_comments(a)
+def test_kernel_code_hash(tmp_path):
+    """The hash covers the gfx950 code object inside the built library, is stable, and is
+    None for a file that is not such a library."""
+    h = bench.kernel_code_hash()
+    assert h is not None and len(h) == 16 and h == bench.kernel_code_hash()
+    junk = tmp_path / "not_a_library.so"
+    junk.write_bytes(b"not an ELF file at all" * 10)
+    assert bench.kernel_code_hash(str(junk)) is None
+    assert bench.kernel_code_hash(str(tmp_path / "missing.so")) is None
 
 
-def test_kernel_hash_is_stable_and_sized():
-    h = bench.kernel_sources_hash()
-    assert h == bench.kernel_sources_hash() and len(h) == 16
+def test_traffic_needs_matching_variant():
+    with open(bench.TRAFFIC_FILE) as f:
+        data = json.load(f)
+    for name, entry in data.items():
+        if not name.startswith("_"):
+            assert bench.measured_traffic(name, entry["variant"] + "_other") is None
 
 
 def test_committed_traffic_entries_are_well_formed():
@@ -33,7 +38,7 @@ def test_committed_traffic_entries_are_well_formed():
         if name.startswith("_"):
             continue
         assert entry["bytes_per_launch"] >= entry["compulsory_bytes"] * 0.9, name
-        assert len(entry["kernel_sources_sha"]) == 16
+        assert len(entry["kernel_code_sha"]) == 16 and entry["variant"].startswith("mfma_")
 
 
 def test_more_than_one_gpu_is_refused():
