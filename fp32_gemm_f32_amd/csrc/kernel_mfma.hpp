@@ -158,6 +158,10 @@ __device__ inline void store_vec(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32
 }
 
 // Physical 16-byte chunk slot of logical chunk q in A-tile row r (CPR chunks per row).
+// The 4-chunk form (64-byte rows) was chosen by measurement on gfx950: of seven XOR
+// swizzles, those whose low bit follows row bit 3 alone (((r >> 1) ^ (r >> 3)) & 3 and
+// (r >> 1) & 3) cost 4 bank-conflict cycles per ds_read_b128 and r & 3 cost 12, while this
+// one and three others cost none.
 template <int CPR>
 __host__ __device__ constexpr int a_swizzle(int r)
 {
@@ -165,7 +169,7 @@ __host__ __device__ constexpr int a_swizzle(int r)
                   "A row must hold 2, 4, 8 or 16 chunks");
     return CPR == 16 ? (r & 15)
          : CPR == 8 ? ((r & 7) ^ ((r >> 3) & 1))
-         : CPR == 4 ? (((r >> 1) ^ (r >> 3)) & 3)
+         : CPR == 4 ? (((r >> 1) ^ (r >> 2)) & 3)
                     : (((r >> 2) ^ (r >> 3)) & 1);
 }
 
@@ -175,7 +179,7 @@ __host__ __device__ constexpr int a_swizzle(int r)
 template <int CPR>
 __host__ __device__ constexpr int a_swizzle_period()
 {
-    return CPR == 4 ? 32 : 16;
+    return CPR == 4 ? 8 : 16;
 }
 
 // Tile coordinates of workgroup bid: a contiguous range of tiles per XCD, then groups of
