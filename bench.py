@@ -14,7 +14,7 @@ Prints one JSON line on stdout:
                HBM floor is the larger one, GB/s of compulsory bytes against 8 TB/s.
                traffic = measured HBM bytes per launch from the committed rocprofv3
                counter summary, or null unless it was taken on the same gfx950 machine
-               code and the same tile variant as this run.
+               code of that kernel and the same tile variant as this run.
   cpu_baseline the CPU oracle (fp64 triple loop) timed on this host on a bounded sample
                of rows of the same product; the same rows of the GPU result are checked
                against it.
@@ -46,7 +46,8 @@ def log(*a):
 
 
 def _elf_sections(data: bytes) -> dict:
-    """Section name -> bytes of a little-endian ELF64 image (only what the hash below needs)."""
+    """Section name -> (bytes, load address, index) of a little-endian ELF64 image (only what
+    the hashes below need)."""
     shoff, = struct.unpack_from("<Q", data, 0x28)
     shentsize, shnum, shstrndx = struct.unpack_from("<HHH", data, 0x3A)
     hdr = lambda i: struct.unpack_from("<IIQQQQIIQQ", data, shoff + i * shentsize)
@@ -55,23 +56,21 @@ def _elf_sections(data: bytes) -> dict:
     out = {}
     for i in range(shnum):
         h = hdr(i)
-        out[names[h[0]:names.index(b"\0", h[0])].decode()] = data[h[4]:h[4] + h[5]]
+        out[names[h[0]:names.index(b"\0", h[0])].decode()] = (data[h[4]:h[4] + h[5]], h[3], i)
     return out
 
 
-def kernel_code_hash(lib_path: str = LIB_PATH):
-    """Hash of the gfx950 machine code in the built library: the .text (instructions) and
-    .rodata (kernel descriptors: registers, LDS) of the device code object inside the
-    library's offload bundle. Comments, asserts and the build directory do not change it;
-    any change to what the GPU executes does. None when the library is not built."""
+def _gfx950_code_objects(lib_path: str):
+    """The gfx950 device code objects inside the library's offload bundle (empty when the
+    file is missing or is not such a library)."""
     try:
         with open(lib_path, "rb") as f:
-            fat = _elf_sections(f.read())[".hip_fatbin"]
-    except (OSError, KeyError, struct.error):
-        return None
+            fat = _elf_sections(f.read())[".hip_fatbin"][0]
+    except (OSError, KeyError, struct.error, ValueError):
+        return []
     if not fat.startswith(b"__CLANG_OFFLOAD_BUNDLE__"):
-        return None
-    h = hashlib.sha256()
+        return []
+    out = []
     n, = struct.unpack_from("<Q", fat, 24)
     off = 32
     for _ in range(n):
@@ -80,23 +79,57 @@ def kernel_code_hash(lib_path: str = LIB_PATH):
         triple = fat[off:off + tlen].decode()
         off += tlen
         if "gfx950" in triple:
-            secs = _elf_sections(fat[o:o + size])
-            h.update(secs[".text"])
-            h.update(secs[".rodata"])
-    return h.hexdigest()[:16]
+            out.append(fat[o:o + size])
+    return out
+
+
+def kernel_symbols(lib_path: str = LIB_PATH) -> dict:
+    """Mangled kernel name -> hash of its gfx950 machine code: the function's instructions
+    and its kernel descriptor (registers, LDS, launch settings). Comments, asserts, other
+    kernels and the build directory do not change a kernel's hash; any change to what that
+    kernel executes does."""
+    out = {}
+    for co in _gfx950_code_objects(lib_path):
+        secs = _elf_sections(co)
+        by_index = {idx: (data, addr) for data, addr, idx in secs.values()}
+        symtab, strtab = secs[".symtab"][0], secs[".strtab"][0]
+        syms = {}
+        for i in range(len(symtab) // 24):
+            st_name, st_info, _, shndx, value, size = struct.unpack_from("<IBBHQQ", symtab, 24 * i)
+            if shndx not in by_index or size == 0:
+                continue
+            name = strtab[st_name:strtab.index(b"\0", st_name)].decode()
+            data, addr = by_index[shndx]
+            syms[name] = data[value - addr:value - addr + size]
+        for name, code in syms.items():
+            kd = syms.get(name + ".kd")
+            if kd is not None and len(kd) == 64:
+                # bytes 16..23 of a kernel descriptor hold the distance from it to the code,
+                # which moves when other kernels are added; everything else is the kernel's
+                h = hashlib.sha256(code)
+                h.update(kd[:16] + bytes(8) + kd[24:])
+                out[name] = h.hexdigest()[:16]
+    return out
+
+
+def kernel_code_hash(symbol: str, lib_path: str = LIB_PATH):
+    """Hash of one kernel's gfx950 machine code in the built library, or None when the
+    library is not built or holds no such kernel."""
+    return kernel_symbols(lib_path).get(symbol)
 
 
 def measured_traffic(workload: str, variant: str):
     """HBM bytes per launch from the committed counter summary, if it was taken on the
-    machine code that runs now and on the variant the plan picks now."""
+    machine code of the kernel that runs now and on the variant the plan picks now."""
     try:
         with open(TRAFFIC_FILE) as f:
             data = json.load(f)
     except (OSError, ValueError):
         return None
     entry = data.get(workload)
-    if (not entry or entry.get("kernel_code_sha") != kernel_code_hash()
-            or entry.get("variant") != variant):
+    if (not entry or entry.get("variant") != variant
+            or kernel_code_hash(entry.get("kernel_symbol", "")) != entry.get("kernel_code_sha")
+            or entry.get("kernel_code_sha") is None):
         return None
     return entry.get("bytes_per_launch")
 
@@ -196,7 +229,7 @@ def main() -> int:
     ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5", "sk"])
     ap.add_argument("--variant", type=int, default=-1, help="force a hot-kernel tile variant")
     ap.add_argument("--kernel", default="auto",
-                    choices=["auto", "splitk", "naive", "tiled16", "tiled32", "tiled32p", "regtiled41",
+                    choices=["auto", "splitk", "streamk", "naive", "tiled16", "tiled32", "tiled32p", "regtiled41",
                              "regtiled44", "regtiled88", "transpose32p0", "transpose32p1",
                              "transpose64p0", "transpose64p1"],
                     help="the entry point a step calls (default: the hot path sgemm_f32); the "
@@ -250,7 +283,18 @@ def main() -> int:
         plan["splits"] = ws_bytes // (4 * M * N) if ws_bytes else 1
         plan["name"] = f"splitk{plan['splits']}+reduce"
         plan["BM"] = plan["BN"] = plan["BK"] = plan["grid"] = None   # chosen per split count
-    if kern not in ("auto", "splitk"):
+    if kern == "streamk":
+        sk_plan = g.sgemm_f32_streamk_describe(M, N, K, args.variant)
+        ws_bytes = lib.sgemm_f32_streamk_workspace_size(M, N, K, args.variant)
+        ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device=dev)
+        plan["streamk_workspace_bytes"] = ws_bytes
+        plan["streamk_plan"] = sk_plan
+        plan["name"] = (f"streamk_{sk_plan['name']}" if sk_plan["streamk"] else sk_plan["name"])
+        plan["BM"], plan["BN"], plan["BK"] = sk_plan["BM"], sk_plan["BN"], sk_plan["BK"]
+        plan["grid"] = (sk_plan["tiles_dp"] + sk_plan["G"] if sk_plan["streamk"]
+                        else sk_plan["tiles"])
+        log(f"bench: stream-K plan {sk_plan}")
+    if kern not in ("auto", "splitk", "streamk"):
         plan["name"] = {"naive": "naive", "tiled16": "lds_tiled_16", "tiled32": "lds_tiled_32",
                         "tiled32p": "lds_tiled_32_padded", "regtiled41": "regtiled_4x1",
                         "regtiled44": "regtiled_4x4", "regtiled88": "regtiled_8x8"}[kern]
@@ -262,6 +306,9 @@ def main() -> int:
                   else lib.sgemm_f32_variant(args.variant, *call_args))
         elif kern == "splitk":
             rc = lib.sgemm_f32_splitk(*gemm, 0, ws.data_ptr(), plan["splitk_workspace_bytes"], sp)
+        elif kern == "streamk":
+            rc = lib.sgemm_f32_streamk(*gemm, args.variant, ws.data_ptr(),
+                                       plan["streamk_workspace_bytes"], sp)
         elif kern == "naive":
             rc = lib.sgemm_f32_naive(*call_args)
         elif kern.startswith("tiled"):
@@ -293,7 +340,7 @@ def main() -> int:
     compulsory = 4.0 * (M * K + K * N + M * N)
     t_mfma = flop / (PEAK_FP32_MFMA_TFLOPS * 1e12)
     t_hbm = compulsory / (PEAK_HBM_GBS * 1e9)
-    if kern not in ("auto", "splitk"):
+    if kern not in ("auto", "splitk", "streamk"):
         # the scalar rungs run on the vector ALUs without packed FP32: 256 CUs x 4 SIMDs x
         # 16 lanes x 2 FLOP x 2.4 GHz
         achieved = flop / (ms / 1e3) / 1e12

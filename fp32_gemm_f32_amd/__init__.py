@@ -9,6 +9,9 @@ Raw layer (same names and arguments as the C ABI; pointers are integers):
     sgemm_f32_naive(...), sgemm_f32_tiled(..., tile=32, pad=0, stream=0)
     sgemm_f32_splitk(..., splits, workspace, workspace_bytes, stream=0)
     sgemm_f32_splitk_workspace_size(M, N, K, splits) -> int
+    sgemm_f32_streamk(..., variant, workspace, workspace_bytes, stream=0)
+    sgemm_f32_streamk_workspace_size(M, N, K, variant=-1) -> int
+    sgemm_f32_streamk_describe(M, N, K, variant=-1, num_cus=0) -> dict
     sgemm_f32_regtiled(..., tm=4, tn=4, stream=0)
     sgemm_f32_lds_transpose(rows, cols, src, ldi, dst, ldo, tile=32, pad=0, stream=0)
     sgemm_f32_variant(variant, M, N, K, A, lda, B, ldb, C, ldc, stream=0)
@@ -59,6 +62,12 @@ def _load():
         lib.sgemm_f32_splitk.restype = i
         lib.sgemm_f32_splitk_workspace_size.argtypes = [i, i, i, i]
         lib.sgemm_f32_splitk_workspace_size.restype = ctypes.c_size_t
+        lib.sgemm_f32_streamk.argtypes = gemm + [i, p, ctypes.c_size_t, p]
+        lib.sgemm_f32_streamk.restype = i
+        lib.sgemm_f32_streamk_workspace_size.argtypes = [i, i, i, i]
+        lib.sgemm_f32_streamk_workspace_size.restype = ctypes.c_size_t
+        lib.sgemm_f32_streamk_describe.argtypes = [i, i, i, i, i, ctypes.c_char_p, i]
+        lib.sgemm_f32_streamk_describe.restype = i
         lib.sgemm_f32_regtiled.argtypes = gemm + [i, i, p]
         lib.sgemm_f32_regtiled.restype = i
         lib.sgemm_f32_lds_transpose.argtypes = [i, i, p, i, p, i, i, i, p]
@@ -115,6 +124,25 @@ def sgemm_f32_splitk_workspace_size(M, N, K, splits) -> int:
     return _load().sgemm_f32_splitk_workspace_size(M, N, K, splits)
 
 
+def sgemm_f32_streamk(M, N, K, A, lda, B, ldb, C, ldc, variant, workspace, workspace_bytes,
+                      stream=0) -> None:
+    _check(_load().sgemm_f32_streamk(M, N, K, A, lda, B, ldb, C, ldc, variant,
+                                     workspace or None, workspace_bytes, stream or None),
+           "sgemm_f32_streamk")
+
+
+def sgemm_f32_streamk_workspace_size(M, N, K, variant=-1) -> int:
+    return _load().sgemm_f32_streamk_workspace_size(M, N, K, variant)
+
+
+def sgemm_f32_streamk_describe(M, N, K, variant=-1, num_cus=0) -> dict:
+    buf = ctypes.create_string_buffer(1024)
+    rc = _load().sgemm_f32_streamk_describe(M, N, K, variant, num_cus, buf, len(buf))
+    if rc < 0:
+        raise SgemmError(rc, "sgemm_f32_streamk_describe")
+    return json.loads(buf.value.decode())
+
+
 def sgemm_f32_regtiled(M, N, K, A, lda, B, ldb, C, ldc, tm=4, tn=4, stream=0) -> None:
     _check(_load().sgemm_f32_regtiled(M, N, K, A, lda, B, ldb, C, ldc, tm, tn, stream or None),
            "sgemm_f32_regtiled")
@@ -167,8 +195,10 @@ def matmul(A, B, out=None, kernel: str = "auto", variant: int = -1, tile=32, pad
     """C = A x B for float32 CUDA/HIP tensors, on torch's current stream.
 
     kernel: "auto" (the hot path, or the given variant), "naive", "tiled", "regtiled"
-    (tile = (tm, tn)) or "splitk" (variant = number of splits, -1 for automatic; the
-    workspace is a torch allocation made here).
+    (tile = (tm, tn)), "splitk" (variant = number of splits, -1 for automatic) or
+    "streamk" (variant = tile variant forced into stream-K, -1 for the automatic choice
+    between the plain and the stream-K form). The split-K and stream-K workspaces are
+    torch allocations made here.
     """
     import torch
 
@@ -201,6 +231,10 @@ def matmul(A, B, out=None, kernel: str = "auto", variant: int = -1, tile=32, pad
             ws_bytes = sgemm_f32_splitk_workspace_size(M, N, K, splits)
             ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device=A.device)
             sgemm_f32_splitk(*args, splits, ws.data_ptr(), ws_bytes, stream=stream)
+        elif kernel == "streamk":
+            ws_bytes = sgemm_f32_streamk_workspace_size(M, N, K, variant)
+            ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device=A.device)
+            sgemm_f32_streamk(*args, variant, ws.data_ptr(), ws_bytes, stream=stream)
         elif kernel == "regtiled":
             tm, tn = tile if isinstance(tile, tuple) else (4, 4)
             sgemm_f32_regtiled(*args, tm=tm, tn=tn, stream=stream)

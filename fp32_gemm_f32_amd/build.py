@@ -60,10 +60,17 @@ def build(asm: bool = False, verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}); see {report}")
     os.replace(OUT + ".tmp", OUT)
     if asm:
-        s = os.path.join(BUILD_DIR, "sgemm_f32.s")
-        subprocess.run([hipcc(), *flags(), "--cuda-device-only", "-S", *SOURCES, "-o", s],
-                       check=True)
+        assemble()
     return OUT
+
+
+def assemble(out: str | None = None) -> str:
+    """Write the gfx950 assembly of the library's device code (same flags as the build)."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    s = out or os.path.join(BUILD_DIR, "sgemm_f32.s")
+    subprocess.run([hipcc(), *flags(), "--cuda-device-only", "-S", *SOURCES, "-o", s],
+                   check=True)
+    return s
 
 
 def main() -> None:

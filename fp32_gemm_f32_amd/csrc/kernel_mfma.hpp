@@ -59,6 +59,8 @@
 #include <cstdint>
 #include <type_traits>
 
+#include "streamk.hpp"
+
 namespace sgemm {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -108,6 +110,10 @@ struct GemmArgs {
     int splits, k_chunk;
     int64_t c_split_stride;
     int64_t c_bytes;   // bytes from C to the end of its last row
+    // Stream-K (the SK kernels only): the partition of streamk.hpp and the workspace of
+    // 2 * sk.G partial tiles of BM x BN floats.
+    SkGeom sk;
+    float *W;
 };
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const float *base, int64_t bytes)
@@ -157,6 +163,22 @@ __device__ inline void store_vec(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32
     }
 }
 
+// A vector store wider than 64 bits reads its data registers after it issues; a VALU
+// write to those registers right behind it corrupts lanes of the stored data on gfx950
+// (measured: the last four lanes of each 16-lane quarter). The compiler's hazard model
+// skips stores whose soffset is an SGPR, as every epilogue store here is, so kernels whose
+// register pressure lets it reuse a store's data registers immediately (the stream-K
+// forms) pin two wait states behind each store.
+template <bool GUARD>
+__device__ inline void store_data_guard()
+{
+    if constexpr (GUARD) {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_nop 1");
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 // Physical 16-byte chunk slot of logical chunk q in A-tile row r (CPR chunks per row).
 // The 4-chunk form (64-byte rows) was chosen by measurement on gfx950: of seven XOR
 // swizzles, those whose low bit follows row bit 3 alone (((r >> 1) ^ (r >> 3)) & 3 and
@@ -182,14 +204,19 @@ __host__ __device__ constexpr int a_swizzle_period()
     return CPR == 4 ? 8 : 16;
 }
 
-// Tile coordinates of workgroup bid: a contiguous range of tiles per XCD, then groups of
-// kGroupM tile rows walked column by column.
-__device__ inline void tile_coords(int bid, int tiles_m, int tiles_n, int &tm, int &tn)
+// Position in the tile order of workgroup bid out of `total`: workgroups are dispatched
+// round-robin over the XCDs, so bid % kXcds is the XCD; each XCD gets a contiguous range.
+__device__ inline int xcd_contiguous(int bid, int total)
 {
-    const int total = tiles_m * tiles_n;
     const int q = total / kXcds, r = total % kXcds;
     const int x = bid % kXcds, l = bid / kXcds;
-    const int t = x < r ? x * (q + 1) + l : r * (q + 1) + (x - r) * q + l;
+    return x < r ? x * (q + 1) + l : r * (q + 1) + (x - r) * q + l;
+}
+
+// Tile t of the tile order: groups of kGroupM tile rows, walked column by column, so
+// tiles close in the order share A rows and B columns.
+__device__ inline void grouped_tile(int t, int tiles_m, int tiles_n, int &tm, int &tn)
+{
     const int per_group = kGroupM * tiles_n;
     const int g = t / per_group;
     const int first = g * kGroupM;
@@ -197,6 +224,12 @@ __device__ inline void tile_coords(int bid, int tiles_m, int tiles_n, int &tm, i
     const int w = t - g * per_group;
     tm = first + w % rows;
     tn = w / rows;
+}
+
+// Tile coordinates of workgroup bid when every tile has its own workgroup.
+__device__ inline void tile_coords(int bid, int tiles_m, int tiles_n, int &tm, int &tn)
+{
+    grouped_tile(xcd_contiguous(bid, tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
 }
 
 template <int BM, int BN, int BK, int WGM, int WGN, int KACC = 1, int KG = 1>
@@ -243,9 +276,12 @@ struct MfmaTile {
 // cleaned on its way into LDS, so in the panel that holds the end of the K range each lane
 // zeroes the elements past K of its own chunks once they have landed, before the barrier.
 //
-// One workgroup computes one item (a tile, or a tile's K range under split-K); the grid
-// has one workgroup per item.
-template <int BM, int BN, int BK, int WGM, int WGN, int KACC, int KG, bool DL>
+// Without SK one workgroup computes one item (a tile, or a tile's K range under split-K)
+// and the grid has one workgroup per item. With SK the grid is sk.tiles_dp workgroups of
+// one tile each followed by sk.G stream-K workgroups, each walking the segments of its
+// range of K-panel units (streamk.hpp): whole tiles go to C, partial ones to its two
+// workspace slots.
+template <int BM, int BN, int BK, int WGM, int WGN, int KACC, int KG, bool DL, bool SK = false>
 __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
 {
     using T = MfmaTile<BM, BN, BK, WGM, WGN, KACC, KG>;
@@ -297,9 +333,13 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
 
     // This workgroup's item: split ls of tile item % tiles, i.e. tile origin (lm0, ln0) and
     // K range [lkb, lkb + lK). All wave-uniform: keep them (and the loops they bound) on
-    // the scalar unit.
-    int lm0, ln0, lkb, lK, ls;
-    {
+    // the scalar unit. Stream-K workgroups set them per segment (below).
+    int lm0 = 0, ln0 = 0, lkb = 0, lK = 0, ls = 0;
+    // stream-K: this workgroup's index g, its next unit and the end of its range
+    int sk_g = 0;
+    int64_t sk_i = 0, sk_end = 0;
+    bool sk_mode = false;
+    if constexpr (!SK) {
         int tm, tn;
         const int item = blockIdx.x;
         ls = item / ntiles;
@@ -309,8 +349,24 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
         lkb = __builtin_amdgcn_readfirstlane(ls * p.k_chunk);
         lK = __builtin_amdgcn_readfirstlane(min(K - lkb, p.k_chunk));
         ls = __builtin_amdgcn_readfirstlane(ls);
+    } else {
+        const int bid = blockIdx.x;
+        if (bid < p.sk.tiles_dp) {
+            int tm, tn;
+            grouped_tile(xcd_contiguous(bid, p.sk.tiles_dp), p.tiles_m, p.tiles_n, tm, tn);
+            lm0 = __builtin_amdgcn_readfirstlane(tm * BM);
+            ln0 = __builtin_amdgcn_readfirstlane(tn * BN);
+            lK = K;
+        } else {
+            // consecutive ranges on one XCD, so neighbouring segments share its L2
+            sk_mode = true;
+            sk_g = __builtin_amdgcn_readfirstlane(xcd_contiguous(bid - p.sk.tiles_dp, p.sk.G));
+            sk_i = sk_start(p.sk, sk_g);
+            sk_end = sk_start(p.sk, sk_g + 1);
+        }
     }
-    const bool b_col_ok = ln0 + b_c0 < N;
+    // B columns of this thread's chunks inside the tile (per segment under stream-K)
+    bool b_col_ok = ln0 + b_c0 < N;
 
     // ---- global -> register staging of one panel ----
     f32x4 ra[A_CH], rb[B_CH];
@@ -563,16 +619,15 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
         }
     };
 
-    auto epilogue = [&](int m0, int n0, int split) {
+    // Stores the tile through resource rsc (its first element at offset 0, rows ldc4 bytes
+    // apart), rows_left x cols_left of it inside the destination.
+    auto epilogue = [&](__amdgpu_buffer_rsrc_t rsc, uint32_t ldc4, int rows_left,
+                        int cols_left) {
         // Lane (lo, hi) owns rows lrow + dr (dr = 8 (v / 4) + v % 4 for accumulator v) and
         // columns col .. col + CI - 1 of each of its blocks. The row step dr * ldc goes in
         // the scalar offset; rows past M and chunks that cross N get voffset kOob (the
         // hardware drops those stores), and only a tile on the N edge stores the partial
         // chunks element by element.
-        const int64_t ec = split * p.c_split_stride + int64_t(m0) * ldc + n0;
-        const __amdgpu_buffer_rsrc_t rsc = make_rsrc(p.C + ec, p.c_bytes - ec * 4);
-        const uint32_t ldc4 = uint32_t(ldc) * 4u;
-        const int rows_left = M - m0, cols_left = N - n0;
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
             const int lrow = wm * WM + r * 32 + 4 * hi;
@@ -592,6 +647,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
                     }
                     const bool ok = col_full && lrow + dr < rows_left;
                     store_vec<CI>(rsc, ok ? vbase : kOob, uint32_t(dr) * ldc4, out);
+                    store_data_guard<SK && CI >= 4>();
                 }
             }
         }
@@ -618,33 +674,79 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
         }
     };
 
-    // ---- K loop; group kg takes panels kg, kg + KG, ... ----
-    set_panel(kg * BK);
-    if constexpr (DL) {
+    // one pass per item: once, or once per segment of a stream-K range
+    for (;;) {
+        bool to_workspace = false;
+        int slot = 0;
+        if constexpr (SK) {
+            if (sk_mode) {
+                if (sk_i >= sk_end) break;
+                const int P = p.sk.panels;
+                const int t = int(sk_i / P);
+                const int kb = int(sk_i - int64_t(t) * P);
+                const int ke = int(min(int64_t(P), kb + (sk_end - sk_i)));
+                to_workspace = kb != 0 || ke != P;
+                slot = 2 * sk_g + (sk_i == sk_start(p.sk, sk_g) ? 0 : 1);
+                int tm, tn;
+                grouped_tile(p.sk.tiles_dp + t, p.tiles_m, p.tiles_n, tm, tn);
+                lm0 = __builtin_amdgcn_readfirstlane(tm * BM);
+                ln0 = __builtin_amdgcn_readfirstlane(tn * BN);
+                lkb = __builtin_amdgcn_readfirstlane(kb * BK);
+                lK = __builtin_amdgcn_readfirstlane(min(K, ke * BK) - kb * BK);
+                sk_i += ke - kb;
+                b_col_ok = ln0 + b_c0 < N;
 #pragma unroll
-        for (int l = 0; l < NL; ++l) load_direct(smem, l);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        fix_k_tail(smem);
-    } else {
+                for (int h = 0; h < KACC; ++h)
 #pragma unroll
-        for (int l = 0; l < NL; ++l) load_slot(l);
+                    for (int i = 0; i < RB; ++i)
 #pragma unroll
-        for (int l = 0; l < NL; ++l) write_slot(smem, l);
-    }
-    __syncthreads();
-    read_a(smem, 0, a[0]);
-    read_b(smem + T::A_TILE, 0, b[0]);
+                        for (int j = 0; j < CI * CG; ++j) acc[h][i][j] = f32x16{};
+                // every wave is done with the previous segment's LDS (operands and K-group
+                // sums) before this one's first loads overwrite it
+                __syncthreads();
+            }
+        }
 
-    // the last round stages nothing; a group whose last panel lies past the K range loads
-    // only zeros for it
-    const int rounds = ((lK + BK - 1) / BK + KG - 1) / KG;
-    for (int r = 0; r + 1 < rounds; ++r) {
-        set_panel(((r + 1) * KG + kg) * BK);
-        panel(r & 1, std::true_type{});
+        // ---- the item: the K loop of group kg (panels kg, kg + KG, ...), the K-group sums
+        // and the epilogue, into C or (a partial stream-K tile) into workspace slot `slot`
+        set_panel(kg * BK);
+        if constexpr (DL) {
+#pragma unroll
+            for (int l = 0; l < NL; ++l) load_direct(smem, l);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            fix_k_tail(smem);
+        } else {
+#pragma unroll
+            for (int l = 0; l < NL; ++l) load_slot(l);
+#pragma unroll
+            for (int l = 0; l < NL; ++l) write_slot(smem, l);
+        }
+        __syncthreads();
+        read_a(smem, 0, a[0]);
+        read_b(smem + T::A_TILE, 0, b[0]);
+
+        // the last round stages nothing; a group whose last panel lies past the K range loads
+        // only zeros for it
+        const int rounds = ((lK + BK - 1) / BK + KG - 1) / KG;
+        for (int r = 0; r + 1 < rounds; ++r) {
+            set_panel(((r + 1) * KG + kg) * BK);
+            panel(r & 1, std::true_type{});
+        }
+        panel((rounds - 1) & 1, std::false_type{});
+        finish();
+        if (kg == 0) {
+            if (!to_workspace) {
+                const int64_t ec = ls * p.c_split_stride + int64_t(lm0) * ldc + ln0;
+                epilogue(make_rsrc(p.C + ec, p.c_bytes - ec * 4), uint32_t(ldc) * 4u, M - lm0,
+                         N - ln0);
+            } else {
+                // a partial tile: all BM x BN sums, packed rows of BN floats
+                epilogue(make_rsrc(p.W + int64_t(slot) * BM * BN, int64_t(BM) * BN * 4),
+                         uint32_t(BN) * 4u, BM, BN);
+            }
+        }
+        if (!SK || !sk_mode) break;
     }
-    panel((rounds - 1) & 1, std::false_type{});
-    finish();
-    if (kg == 0) epilogue(lm0, ln0, ls);
 }
 
 // C[i][j] = sum over s of W[s * stride + i * N + j], in ascending s: the second pass of
@@ -686,6 +788,75 @@ __global__ __launch_bounds__(64) void k_splitk_reduce(int M, int N, int splits,
             }
         } else {
             *dst = acc;
+        }
+    }
+}
+
+// Stream-K fixup: every shared tile (streamk.hpp) gets the sum of its workgroups' partial
+// tiles, added in ascending workgroup order, i.e. ascending K, so repeated runs give
+// identical bits. One workgroup of 256 threads per shared tile; a tile that one workgroup
+// covered whole was written to C by it and is skipped. A pass gives each thread
+// kFixupChunks 16-byte chunks of the tile; the partial sums of kFixupBatch contributors
+// are loaded together (kFixupChunks x kFixupBatch loads in flight) and then added in
+// order. W must be 16-byte aligned; C's rows are stored 16 bytes at a time when ldc and C
+// allow it, else element by element.
+constexpr int kFixupChunks = 4;
+
+template <int BM, int BN>
+__global__ __launch_bounds__(256) void k_streamk_fixup(GemmArgs p)
+{
+    const SkGeom s = p.sk;
+    const int t = blockIdx.x;
+    const int64_t u0 = int64_t(t) * s.panels;
+    const int g0 = sk_owner(s, u0), g1 = sk_owner(s, u0 + s.panels - 1);
+    if (g0 == g1) return;
+    int tm, tn;
+    grouped_tile(s.tiles_dp + t, p.tiles_m, p.tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const bool c_vec = (p.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(p.C) & 15) == 0;
+    constexpr int CH = BM * BN / 4;                 // chunks per tile
+    constexpr int PASS = 256 * kFixupChunks;        // chunks per pass
+    static_assert(CH % PASS == 0, "passes cover the tile");
+    const int tid = threadIdx.x;
+    for (int c0 = 0; c0 < CH; c0 += PASS) {
+        f32x4 acc[kFixupChunks];
+        {
+            const float *w = p.W + int64_t(sk_fixup_slot(s, g0, g0, t)) * (BM * BN);
+#pragma unroll
+            for (int q = 0; q < kFixupChunks; ++q)
+                acc[q] = *reinterpret_cast<const f32x4 *>(w + 4 * (c0 + q * 256 + tid));
+        }
+        for (int g = g0 + 1; g <= g1; g += kFixupBatch) {
+            f32x4 v[kFixupBatch][kFixupChunks];
+#pragma unroll
+            for (int u = 0; u < kFixupBatch; ++u) {
+                if (g + u > g1) break;
+                const float *w = p.W + int64_t(sk_fixup_slot(s, g + u, g0, t)) * (BM * BN);
+#pragma unroll
+                for (int q = 0; q < kFixupChunks; ++q)
+                    v[u][q] = *reinterpret_cast<const f32x4 *>(w + 4 * (c0 + q * 256 + tid));
+            }
+#pragma unroll
+            for (int u = 0; u < kFixupBatch; ++u) {
+                if (g + u > g1) break;
+#pragma unroll
+                for (int q = 0; q < kFixupChunks; ++q) acc[q] += v[u][q];
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < kFixupChunks; ++q) {
+            const int c = c0 + q * 256 + tid;
+            const int r = c / (BN / 4), col = 4 * (c % (BN / 4));
+            const int row = m0 + r, left = p.N - (n0 + col);
+            if (row >= p.M || left <= 0) continue;
+            float *dst = p.C + int64_t(row) * p.ldc + n0 + col;
+            if (c_vec && left >= 4) {
+                *reinterpret_cast<f32x4 *>(dst) = acc[q];
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (j < left) dst[j] = acc[q][j];
+            }
         }
     }
 }

@@ -16,6 +16,8 @@
 #include <cstdint>
 #include <cstdio>
 
+#include "streamk.hpp"
+
 namespace sgemm {
 
 struct Variant {
@@ -57,6 +59,35 @@ inline double variant_cost(const Variant &v, const Operands &o, int cus)
     const double k = o.K > 0 ? double(o.K) / o.splits : 1;
     const double rate = per_cu >= v.wg_per_cu ? v.rate : v.rate * v.solo;
     return double(per_cu) * double(v.BM) * v.BN * (k / rate + v.overhead);
+}
+
+// Cost units: one multiply-add on one CU at rate 1 (140 TFLOP/s over 256 CUs).
+constexpr double kUnitsPerUs = 140e12 / 2 / 256 * 1e-6;
+// Stream-K's fixed price: the fixup kernel's launch and latency, in microseconds, the rate
+// at which partial tiles are written and read back, in bytes per microsecond, and the
+// latency of each batch of partial-tile loads the fixup waits for in turn.
+constexpr double kFixupUs = 3.0;
+constexpr double kPartialBytesPerUs = 4e6;
+constexpr double kFixupBatchUs = 0.7;
+
+// Busiest-CU estimate for variant v run as stream-K with partition g (streamk.hpp), in the
+// units of variant_cost: every CU gets the same share of the K-panel units, plus its
+// plain tiles, plus a per-segment overhead (each stream-K workgroup starts one segment
+// more than the whole tiles its range holds), plus the fixup and the partial tiles'
+// round trip through memory.
+inline double streamk_cost(const Variant &v, const Operands &o, int cus, const SkGeom &g,
+                           size_t ws_bytes)
+{
+    const double tile = double(v.BM) * v.BN;
+    const double dp_tiles = double(g.tiles_dp) / cus;                 // per CU
+    const double sk_k = double(g.iters) * v.BK / cus;                  // K per CU, summed
+    const double segs = double(v.wg_per_cu) * (double(g.iters) / g.G / g.panels + 1.0);
+    const double work = tile * ((dp_tiles * o.K + sk_k) / v.rate + (dp_tiles + segs) * v.overhead);
+    // contributors of the most shared tile: its units over a range's length, plus one
+    const double contrib = double(g.panels) * g.G / double(g.iters) + 2.0;
+    const double batches = contrib / kFixupBatch + 1.0;
+    return work + (kFixupUs + batches * kFixupBatchUs + double(ws_bytes) / kPartialBytesPerUs) *
+                      kUnitsPerUs;
 }
 
 template <int NV>

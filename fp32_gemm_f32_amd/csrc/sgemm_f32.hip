@@ -10,6 +10,8 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
+#include <vector>
 
 #include "sgemm_f32.h"
 #include "sgemm_validate.hpp"
@@ -51,16 +53,25 @@ typedef void (*MfmaKernel)(GemmArgs);
 struct VariantEntry {
     Variant v;
     MfmaKernel kern;
+    MfmaKernel kern_sk;     // stream-K form (NULL for variants that are never planned)
+    MfmaKernel fixup;       // its fixup kernel
     int threads;
 };
 
-template <int BM, int BN, int BK, int WGM, int WGN, int KACC, int KG, bool DL>
+// PLANNED variants also get a stream-K form and its fixup kernel; the others are never
+// planned and are instantiated in their plain form only.
+template <int BM, int BN, int BK, int WGM, int WGN, int KACC, int KG, bool DL, bool PLANNED>
 constexpr VariantEntry entry(const char *name, int wg_per_cu, double rate, double overhead,
-                             double solo, bool planned = true)
+                             double solo)
 {
+    MfmaKernel sk = nullptr, fix = nullptr;
+    if constexpr (PLANNED) {
+        sk = &k_sgemm_mfma<BM, BN, BK, WGM, WGN, KACC, KG, DL, true>;
+        fix = &k_streamk_fixup<BM, BN>;
+    }
     return VariantEntry{
-        Variant{name, BM, BN, BK, WGM, WGN, wg_per_cu, rate, overhead, solo, DL, planned},
-        &k_sgemm_mfma<BM, BN, BK, WGM, WGN, KACC, KG, DL>, 64 * WGM * WGN * KG};
+        Variant{name, BM, BN, BK, WGM, WGN, wg_per_cu, rate, overhead, solo, DL, PLANNED},
+        &k_sgemm_mfma<BM, BN, BK, WGM, WGN, KACC, KG, DL>, sk, fix, 64 * WGM * WGN * KG};
 }
 
 // Rates (throughput at 8192^3 relative to 140 TFLOP/s), per-tile overheads (in units of K)
@@ -80,12 +91,12 @@ constexpr VariantEntry entry(const char *name, int wg_per_cu, double rate, doubl
 // The last entry stages through registers; it is never planned and stays as the measured
 // comparison for the direct loads (forced through sgemm_f32_variant).
 const VariantEntry kVariants[] = {
-    entry<256, 256, 32, 4, 2, 1, 1, true>("mfma_256x256x32_w4x2_dl", 1, 1.055, 40, 1.0),
-    entry<128, 256, 16, 2, 2, 1, 1, true>("mfma_128x256x16_w2x2_dl", 2, 1.02, 24, 0.94),
-    entry<128, 128, 32, 2, 2, 1, 1, true>("mfma_128x128x32_w2x2_dl", 2, 1.01, 32, 0.90),
-    entry<64, 64, 32, 2, 1, 2, 4, true>("mfma_64x64x32_w2x1_acc2_kg4_dl", 1, 0.89, 212, 1.0),
-    entry<64, 64, 32, 2, 1, 1, 2, true>("mfma_64x64x32_w2x1_kg2_dl", 2, 0.915, 64, 0.80),
-    entry<256, 256, 32, 4, 2, 1, 1, false>("mfma_256x256x32_w4x2", 1, 1.045, 52, 1.0, false),
+    entry<256, 256, 32, 4, 2, 1, 1, true, true>("mfma_256x256x32_w4x2_dl", 1, 1.055, 40, 1.0),
+    entry<128, 256, 16, 2, 2, 1, 1, true, true>("mfma_128x256x16_w2x2_dl", 2, 1.02, 24, 0.94),
+    entry<128, 128, 32, 2, 2, 1, 1, true, true>("mfma_128x128x32_w2x2_dl", 2, 1.01, 32, 0.90),
+    entry<64, 64, 32, 2, 1, 2, 4, true, true>("mfma_64x64x32_w2x1_acc2_kg4_dl", 1, 0.89, 212, 1.0),
+    entry<64, 64, 32, 2, 1, 1, 2, true, true>("mfma_64x64x32_w2x1_kg2_dl", 2, 0.915, 64, 0.80),
+    entry<256, 256, 32, 4, 2, 1, 1, false, false>("mfma_256x256x32_w4x2", 1, 1.045, 52, 1.0),
 };
 constexpr int kNumVariants = int(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -120,12 +131,11 @@ int device_cus(int *out)
     return SGEMM_OK;
 }
 
-// One workgroup per tile.
-int run_variant(int vi, const Operands &o, const float *A, const float *B, float *C,
-                void *stream)
+// Kernel arguments of the plain product with variant e.
+GemmArgs plain_args(const VariantEntry &e, const Operands &o, const float *A, const float *B,
+                    float *C)
 {
-    const VariantEntry &e = kVariants[vi];
-    GemmArgs p;
+    GemmArgs p{};
     p.A = A; p.B = B; p.C = C;
     p.a_bytes = span_elems(o.M, o.K, o.lda) * 4;
     p.b_bytes = span_elems(o.K, o.N, o.ldb) * 4;
@@ -136,6 +146,48 @@ int run_variant(int vi, const Operands &o, const float *A, const float *B, float
     p.splits = 1;
     p.k_chunk = o.K;
     p.c_split_stride = 0;
+    return p;
+}
+
+// Stream-K with variant vi: the partition for this shape, with G = CUs x the variant's
+// resident workgroups per CU.
+SkGeom streamk_geometry(const Variant &v, const Operands &o, int cus)
+{
+    const int64_t tiles = ((int64_t(o.M) + v.BM - 1) / v.BM) * ((int64_t(o.N) + v.BN - 1) / v.BN);
+    return sk_geometry(tiles, (o.K + v.BK - 1) / v.BK, cus * v.wg_per_cu);
+}
+
+size_t streamk_workspace_bytes(const Variant &v, const SkGeom &g)
+{
+    return g.tiles_sk > 0 ? size_t(2) * size_t(g.G) * size_t(v.BM) * size_t(v.BN) * 4u : 0;
+}
+
+// The stream-K entry's choice: the cheapest of every planned variant run plainly or as
+// stream-K (streamk_cost in plan.hpp). Returns the variant index and sets *sk.
+int choose_streamk(const Operands &o, int cus, bool *sk)
+{
+    int best = -1;
+    double best_cost = 0.0;
+    *sk = false;
+    for (int i = 0; i < kNumVariants; ++i) {
+        const Variant &v = g_table[i];
+        if (!v.planned || !variant_allowed(v, o)) continue;
+        const double c_dp = variant_cost(v, o, cus);
+        if (best < 0 || c_dp < best_cost) { best = i; best_cost = c_dp; *sk = false; }
+        const SkGeom g = streamk_geometry(v, o, cus);
+        if (g.tiles_sk == 0) continue;
+        const double c_sk = streamk_cost(v, o, cus, g, streamk_workspace_bytes(v, g));
+        if (c_sk < best_cost) { best = i; best_cost = c_sk; *sk = true; }
+    }
+    return best;
+}
+
+// One workgroup per tile.
+int run_variant(int vi, const Operands &o, const float *A, const float *B, float *C,
+                void *stream)
+{
+    const VariantEntry &e = kVariants[vi];
+    const GemmArgs p = plain_args(e, o, A, B, C);
     const int64_t tiles = int64_t(p.tiles_m) * p.tiles_n;
     if (tiles > INT32_MAX) return SGEMM_ETOO_LARGE;
     return launch(e.kern, dim3(unsigned(tiles)), dim3(e.threads), stream, p);
@@ -176,7 +228,7 @@ int run_splitk(int splits, const Operands &o0, const float *A, const float *B, f
     splitk_geometry(o.K, e.v.BK, splits, &eff, &k_chunk);
     const int64_t mn = int64_t(o.M) * o.N;
     if (w_bytes < size_t(eff) * size_t(mn) * 4u) return SGEMM_EINVAL_ARG;
-    GemmArgs p;
+    GemmArgs p{};
     p.A = A; p.B = B; p.C = W;
     p.a_bytes = span_elems(o.M, o.K, o.lda) * 4;
     p.b_bytes = span_elems(o.K, o.N, o.ldb) * 4;
@@ -201,6 +253,39 @@ int run_splitk(int splits, const Operands &o0, const float *A, const float *B, f
                           eff, Wc, mn, C, o.ldc, c_vec)
                  : launch(k_splitk_reduce<1>, dim3(unsigned(blocks)), dim3(64), stream, o.M, o.N,
                           eff, Wc, mn, C, o.ldc, c_vec);
+}
+
+// Stream-K with variant vi (the partition may leave nothing to share: then it is the plain
+// launch). W holds 2 G partial tiles.
+int run_streamk(int vi, const Operands &o, const float *A, const float *B, float *C, float *W,
+                size_t w_bytes, void *stream, int cus)
+{
+    const VariantEntry &e = kVariants[vi];
+    GemmArgs p = plain_args(e, o, A, B, C);
+    p.sk = streamk_geometry(e.v, o, cus);
+    if (p.sk.tiles_sk == 0) return run_variant(vi, o, A, B, C, stream);
+    if (w_bytes < streamk_workspace_bytes(e.v, p.sk)) return SGEMM_EINVAL_ARG;
+    p.W = W;
+    const int64_t grid = int64_t(p.sk.tiles_dp) + p.sk.G;
+    if (grid > INT32_MAX) return SGEMM_ETOO_LARGE;
+    const int st = launch(e.kern_sk, dim3(unsigned(grid)), dim3(e.threads), stream, p);
+    if (st != SGEMM_OK) return st;
+    return launch(e.fixup, dim3(unsigned(p.sk.tiles_sk)), dim3(256), stream, p);
+}
+
+// The stream-K entry's plan: variant index (or a negative status) and whether it shares
+// tiles. variant >= 0 forces stream-K with that variant.
+int plan_streamk(int variant, const Operands &o, int cus, bool *sk)
+{
+    if (variant >= kNumVariants || (variant >= 0 && !kVariants[variant].kern_sk))
+        return SGEMM_EINVAL_ARG;
+    if (variant >= 0) {
+        if (!offsets_fit(kVariants[variant].v, o)) return SGEMM_ETOO_LARGE;
+        *sk = streamk_geometry(kVariants[variant].v, o, cus).tiles_sk > 0;
+        return variant;
+    }
+    const int vi = choose_streamk(o, cus, sk);
+    return vi < 0 ? SGEMM_ETOO_LARGE : vi;
 }
 
 int run_hot(int variant, int M, int N, int K, const float *A, int lda, const float *B, int ldb,
@@ -282,6 +367,124 @@ extern "C" int sgemm_f32_splitk(int M, int N, int K, const float *A, int lda, co
         if (qs != SGEMM_OK) return qs;
     }
     return run_splitk(splits, o, A, B, C, workspace, workspace_bytes, stream, cus);
+}
+
+extern "C" size_t sgemm_f32_streamk_workspace_size(int M, int N, int K, int variant)
+{
+    if (M <= 0 || N <= 0 || K <= 0) return 0;
+    int cus = 0;
+    if (device_cus(&cus) != SGEMM_OK) return 0;
+    const Operands o = make_operands(M, N, K, K, N, N);
+    bool sk = false;
+    const int vi = plan_streamk(variant < 0 ? -1 : variant, o, cus, &sk);
+    if (vi < 0 || !sk) return 0;
+    return streamk_workspace_bytes(kVariants[vi].v, streamk_geometry(kVariants[vi].v, o, cus));
+}
+
+extern "C" int sgemm_f32_streamk(int M, int N, int K, const float *A, int lda, const float *B,
+                                 int ldb, float *C, int ldc, int variant, float *workspace,
+                                 size_t workspace_bytes, void *stream)
+{
+    const int st = validate(M, N, K, A, lda, B, ldb, C, ldc);
+    if (st != SGEMM_OK) return st;
+    if (variant >= kNumVariants || (variant >= 0 && !kVariants[variant].kern_sk))
+        return SGEMM_EINVAL_ARG;
+    // the workspace, when one is given, is checked before any HIP call
+    const int64_t w_elems = int64_t(workspace_bytes / 4);
+    if (workspace_bytes > 0) {
+        if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 15u) != 0)
+            return SGEMM_EINVAL_PTR;
+        if (overlap(workspace, w_elems, A, span_elems(M, K, lda)) ||
+            overlap(workspace, w_elems, B, span_elems(K, N, ldb)) ||
+            overlap(workspace, w_elems, C, span_elems(M, N, ldc)))
+            return SGEMM_EALIAS;
+    }
+    if (M == 0 || N == 0) return SGEMM_OK;
+    if (K == 0) return fill_zero(M, N, C, ldc, stream);
+    const Operands o = make_operands(M, N, K, lda, ldb, ldc);
+    int cus = 0;
+    const int qs = device_cus(&cus);
+    if (qs != SGEMM_OK) return qs;
+    bool sk = false;
+    const int vi = plan_streamk(variant < 0 ? -1 : variant, o, cus, &sk);
+    if (vi < 0) return vi;
+    if (!sk) return run_variant(vi, o, A, B, C, stream);
+    return run_streamk(vi, o, A, B, C, workspace, workspace_bytes, stream, cus);
+}
+
+extern "C" int sgemm_f32_streamk_describe(int M, int N, int K, int variant, int num_cus,
+                                          char *buf, int buflen)
+{
+    if (!buf || buflen <= 0) return SGEMM_EINVAL_ARG;
+    if (M < 0 || N < 0 || K < 0) return SGEMM_EINVAL_DIM;
+    if (M == 0 || N == 0 || K == 0) return SGEMM_EINVAL_DIM;
+    int cus = num_cus;
+    if (cus <= 0) {
+        const int qs = device_cus(&cus);
+        if (qs != SGEMM_OK) return qs;
+    }
+    const Operands o = make_operands(M, N, K, K, N, N);
+    bool sk = false;
+    const int vi = plan_streamk(variant < 0 ? -1 : variant, o, cus, &sk);
+    if (vi < 0) return vi;
+    const Variant &v = kVariants[vi].v;
+    const SkGeom g = streamk_geometry(v, o, cus);
+    // walk every stream-K range with the kernels' own functions: each unit must belong to
+    // exactly one range, each shared tile's partial slots must be distinct and written by
+    // the segment that the fixup reads them for
+    int64_t shared = 0, max_contrib = 0, max_segments = 0;
+    bool ok = true;
+    if (sk) {
+        int64_t next = 0;
+        std::vector<int> written(size_t(2) * g.G, -1);
+        for (int wg = 0; wg < g.G && ok; ++wg) {
+            const int64_t a = sk_start(g, wg), b = sk_start(g, wg + 1);
+            ok = a == next && b >= a;
+            next = b;
+            int64_t segs = 0;
+            for (int64_t i = a; i < b && ok;) {
+                const int t = int(i / g.panels);
+                const int kb = int(i - int64_t(t) * g.panels);
+                const int ke = int(std::min<int64_t>(g.panels, kb + (b - i)));
+                if (kb != 0 || ke != g.panels) {
+                    const int slot = 2 * wg + (i == a ? 0 : 1);
+                    ok = written[size_t(slot)] < 0 && sk_slot(g, wg, t) == slot &&
+                         sk_owner(g, i) == wg;
+                    written[size_t(slot)] = t;
+                }
+                i += ke - kb;
+                ++segs;
+            }
+            max_segments = std::max(max_segments, segs);
+        }
+        ok = ok && next == g.iters;
+        for (int t = 0; t < g.tiles_sk && ok; ++t) {
+            const int64_t u0 = int64_t(t) * g.panels;
+            const int g0 = sk_owner(g, u0), g1 = sk_owner(g, u0 + g.panels - 1);
+            if (g0 == g1) continue;
+            ++shared;
+            max_contrib = std::max<int64_t>(max_contrib, g1 - g0 + 1);
+            for (int wg = g0; wg <= g1 && ok; ++wg)
+                ok = written[size_t(sk_slot(g, wg, t))] == t &&
+                     sk_fixup_slot(g, wg, g0, t) == sk_slot(g, wg, t);
+        }
+    }
+    const int n = snprintf(buf, size_t(buflen),
+                           "{\"variant\": %d, \"name\": \"%s\", \"streamk\": %s, "
+                           "\"BM\": %d, \"BN\": %d, \"BK\": %d, \"cus\": %d, "
+                           "\"G\": %d, \"tiles\": %lld, \"tiles_dp\": %d, "
+                           "\"tiles_sk\": %d, \"panels\": %d, \"units\": %lld, "
+                           "\"shared_tiles\": %lld, \"max_contributors\": %lld, "
+                           "\"max_segments\": %lld, \"workspace_bytes\": %zu, "
+                           "\"partition_ok\": %s}",
+                           vi, v.name, sk ? "true" : "false", v.BM, v.BN, v.BK, cus, g.G,
+                           (long long)(int64_t((M + v.BM - 1) / v.BM) * ((N + v.BN - 1) / v.BN)),
+                           sk ? g.tiles_dp : 0, sk ? g.tiles_sk : 0, g.panels,
+                           (long long)(sk ? g.iters : 0), (long long)shared,
+                           (long long)max_contrib, (long long)max_segments,
+                           sk ? streamk_workspace_bytes(v, g) : size_t(0), ok ? "true" : "false");
+    if (n < 0 || n >= buflen) return SGEMM_EINVAL_ARG;
+    return vi;
 }
 
 extern "C" int sgemm_f32_naive(int M, int N, int K, const float *A, int lda, const float *B,

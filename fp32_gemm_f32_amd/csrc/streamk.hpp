@@ -1,0 +1,96 @@
+// streamk.hpp -- the stream-K work partition, shared by the planner (host), the hot
+// kernel's stream-K mode and the fixup kernel (device).
+//
+// A tile grid that does not divide evenly over the resident workgroups leaves a last,
+// partly filled round of tiles: 272 tiles on 256 compute units take two tile times, with
+// 240 units idle in the second. The pages' own remedy is to pick the tile size ("Shared
+// Memory Tiling", "Choosing a tile size"; "Visual walkthrough - Memory hierarchy",
+// Step 7), which cannot fix a count just past a multiple of the CU count. Stream-K cuts
+// the work finer: the unit is one K-panel of one tile (BM x BN x BK multiply-adds), and
+// every workgroup gets an equal, contiguous range of those units. A range that covers a
+// whole tile writes it to C; a tile shared by several ranges is summed afterwards.
+//
+// Layout of the work:
+//   * tiles are numbered in the tile order (groups of kGroupM tile rows, column by column);
+//   * tiles 0 .. tiles_dp - 1 run one per workgroup, as in the plain kernel;
+//   * the next tiles_sk tiles form iters = tiles_sk * panels units, and stream-K
+//     workgroup g (0 <= g < G) takes units [start(g), start(g + 1)) with
+//     start(g) = floor(g * iters / G);
+//   * inside its range a workgroup visits one segment per tile it touches; a segment that
+//     is not the whole tile stores its partial sums to workspace slot 2g (the first
+//     segment of the range) or 2g + 1 (the last one). A range touches at most one
+//     partial tile at each end, so two slots per workgroup are enough.
+//   * the fixup kernel adds, for each shared tile, the partial sums of its workgroups in
+//     ascending g, which is ascending K; the result does not depend on timing.
+// With q = tiles / G and r = tiles % G: r = 0 needs no stream-K; q = 0 shares every tile;
+// otherwise the last G + r tiles are shared (each stream-K range then holds more than one
+// whole tile's worth of units, so no segment is very short) and the rest run plainly.
+// Every range holds at least one unit (G is lowered to the unit count when needed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace sgemm {
+
+// Contributors whose partial tiles the fixup kernel loads together before adding them.
+constexpr int kFixupBatch = 4;
+
+struct SkGeom {
+    int G = 0;            // stream-K workgroups
+    int tiles_dp = 0;     // tiles run one per workgroup before the shared ones
+    int tiles_sk = 0;     // tiles shared out by K-panel
+    int panels = 0;       // K-panels per tile
+    int64_t iters = 0;    // tiles_sk * panels units
+};
+
+// First unit of stream-K workgroup g (g = G gives the end of the last range).
+__host__ __device__ inline int64_t sk_start(const SkGeom &s, int g)
+{
+    return int64_t(g) * s.iters / s.G;
+}
+
+// The workgroup whose range holds unit i: the largest g with start(g) <= i.
+__host__ __device__ inline int sk_owner(const SkGeom &s, int64_t i)
+{
+    return int(((i + 1) * s.G - 1) / s.iters);
+}
+
+// Workspace slot of workgroup g's partial sums of shared tile t (an index among the
+// shared tiles): 2g if g's range starts inside t, else 2g + 1.
+__host__ __device__ inline int sk_slot(const SkGeom &s, int g, int t)
+{
+    return 2 * g + (sk_start(s, g) / s.panels == t ? 0 : 1);
+}
+
+// The same slot, as the fixup kernel computes it for contributor g of shared tile t whose
+// first contributor is g0: every later contributor's range starts inside t, and g0's does
+// only when it starts at t's first unit (no division per contributor).
+__host__ __device__ inline int sk_fixup_slot(const SkGeom &s, int g, int g0, int t)
+{
+    return g > g0 ? 2 * g : 2 * g + (sk_start(s, g) == int64_t(t) * s.panels ? 0 : 1);
+}
+
+inline SkGeom sk_geometry(int64_t tiles, int panels, int G)
+{
+    SkGeom s;
+    s.G = G;
+    s.panels = panels;
+    const int64_t q = tiles / G, r = tiles % G;
+    if (r == 0) {
+        s.tiles_dp = int(tiles);
+    } else if (q == 0) {
+        s.tiles_sk = int(tiles);
+    } else {
+        s.tiles_dp = int((q - 1) * G);
+        s.tiles_sk = int(G + r);
+    }
+    s.iters = int64_t(s.tiles_sk) * panels;
+    // no empty ranges: a workgroup between two contributors of a tile must have written a
+    // slot for it (only possible to violate when q = 0 and the tiles hold few units)
+    if (s.tiles_sk > 0 && s.iters < G) s.G = int(s.iters);
+    return s;
+}
+
+}  // namespace sgemm

@@ -91,6 +91,54 @@ int sgemm_f32_splitk(int M, int N, int K,
 size_t sgemm_f32_splitk_workspace_size(int M, int N, int K, int splits);
 
 /*
+ * Stream-K for tile grids that do not divide evenly over the GPU (a tile count just past a
+ * multiple of the resident workgroups, such as 272 tiles on 256 compute units): the pages
+ * size tiles against the parallelism they leave ("Shared Memory Tiling", "Choosing a tile
+ * size"; "Visual walkthrough - Memory hierarchy", Step 7), and this entry point goes one
+ * step finer. The unit of work is one K-panel of one tile; the last tiles' units are
+ * shared out evenly over the resident workgroups (CUs x workgroups per CU), each taking a
+ * contiguous range. A range that covers a whole tile writes it to C; a tile shared by
+ * several ranges gets their partial sums, which go through `workspace` and are added by a
+ * second kernel in ascending K order, so repeated calls give identical bits. Results
+ * differ from sgemm_f32's only by the order of the K-sum (exact on small integers).
+ * variant < 0: the library prices every tile variant run plainly and as stream-K and
+ * takes the cheapest; when that is a plain grid this is sgemm_f32 and the workspace is
+ * not touched. variant >= 0 forces stream-K with that tile variant (an index below
+ * sgemm_f32_variant_count() whose name ends in "_dl", else SGEMM_EINVAL_ARG); a grid that
+ * divides evenly still runs plainly.
+ * workspace: caller-owned device memory of sgemm_f32_streamk_workspace_size bytes (2 x
+ * the workgroup count x one tile of floats), 16-byte aligned, not overlapping A, B or C
+ * (SGEMM_EINVAL_PTR, SGEMM_EALIAS; checked before any HIP call whenever workspace_bytes
+ * > 0); too small for the plan is SGEMM_EINVAL_ARG. It needs no initialisation, and
+ * its contents on return are unspecified. Calls that share a workspace must not overlap
+ * in time (same stream, or synchronised). Both kernels run on `stream`.
+ */
+int sgemm_f32_streamk(int M, int N, int K,
+                      const float *A, int lda,
+                      const float *B, int ldb,
+                      float *C, int ldc,
+                      int variant, float *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/* Bytes of workspace sgemm_f32_streamk needs for this shape and variant on the current
+ * device (0 when the plan shares no tile, for empty shapes, or on a bad variant). */
+size_t sgemm_f32_streamk_workspace_size(int M, int N, int K, int variant);
+
+/*
+ * Writes a one-line JSON description of sgemm_f32_streamk's plan for packed operands of
+ * this shape into buf: variant and tile, whether it shares tiles, the workgroup count G,
+ * the plain and shared tile counts, K-panels per tile, the shared units, how many tiles
+ * are shared and by at most how many workgroups, segments per workgroup, workspace bytes,
+ * and "partition_ok": the result of walking every range with the kernels' own partition
+ * functions (every unit in exactly one range, every partial slot the fixup reads written
+ * once for that tile). num_cus > 0 plans for that many compute units (no GPU needed);
+ * num_cus <= 0 queries the current device. M, N and K must be positive (else
+ * SGEMM_EINVAL_DIM). Returns the variant index, or a negative sgemm_status.
+ */
+int sgemm_f32_streamk_describe(int M, int N, int K, int variant, int num_cus,
+                               char *buf, int buflen);
+
+/*
  * The reference kernel: one thread per element of C, a length-K dot product read
  * straight from global memory ("Shared Memory Tiling", "The naive kernel"), with bounds
  * checks so any shape works. Slow on purpose; the pages' 2*M*N*K read count applies.

@@ -160,3 +160,78 @@ def test_splitk_validation_and_workspace_size():
     assert lib.sgemm_f32_splitk(0, 48, 4096, P, 4096, P + 4096, 48, P + 8192, 48, 4, ws, need,
                                 None) == 0
 
+
+
+def test_streamk_validation():
+    lib = g.library()
+    n = lib.sgemm_f32_variant_count()
+    args = (64, 48, 4096, P, 4096, P + (1 << 26), 48, P + (1 << 27), 48)
+    ws = P + (1 << 28)
+    assert lib.sgemm_f32_streamk(*args, n, ws, 1 << 20, None) == -6          # no such variant
+    unplanned = [i for i in range(n) if not g.variant_names()[i].endswith("_dl")]
+    for i in unplanned:                                                     # no stream-K form
+        assert lib.sgemm_f32_streamk(*args, i, ws, 1 << 20, None) == -6
+    assert lib.sgemm_f32_streamk(*args, -1, None, 1 << 20, None) == -3
+    assert lib.sgemm_f32_streamk(*args, -1, ws + 4, 1 << 20, None) == -3    # not 16-byte aligned
+    assert lib.sgemm_f32_streamk(*args, -1, P + 64, 1 << 20, None) == -4    # overlaps A
+    assert lib.sgemm_f32_streamk(*args, 0, P + (1 << 27) - 64, 1 << 20, None) == -4  # overlaps C
+    assert lib.sgemm_f32_streamk(-1, 48, 64, P, 64, P + 4096, 48, P + 8192, 48, -1, ws, 64,
+                                 None) == -1
+    assert lib.sgemm_f32_streamk(64, 48, 64, P, 63, P + 4096, 48, P + 8192, 48, -1, ws, 64,
+                                 None) == -2
+    # empty output: nothing to do, before any device query
+    assert lib.sgemm_f32_streamk(0, 48, 64, P, 64, P + 4096, 48, P + 8192, 48, -1, ws, 64,
+                                 None) == 0
+
+
+def _shapes(n, seed):
+    import random
+    rnd = random.Random(seed)
+    out = [(1023, 1025, 1027), (256, 256, 32768), (1, 1, 1), (64, 64, 32), (65, 65, 33),
+           (5000, 5000, 1000), (3000, 3000, 3000), (2107, 2107, 100), (1, 4000, 7)]
+    out += [(rnd.randint(1, 3000), rnd.randint(1, 3000), rnd.randint(1, 5000)) for _ in range(n)]
+    return out
+
+
+def test_streamk_partition_self_check():
+    """The library walks every stream-K range with the kernels' own partition functions:
+    each K-panel unit belongs to exactly one range, each range holds at least one unit,
+    and every partial slot the fixup reads for a shared tile was written for that tile by
+    exactly one segment. Checked over random shapes, every variant and several CU counts."""
+    nv = len(g.variant_names())
+    planned = [i for i in range(nv) if g.variant_names()[i].endswith("_dl")]
+    seen_sk = seen_dp_and_sk = seen_tiny = 0
+    for M, N, K in _shapes(60, 7):
+        for v in [-1] + planned:
+            for cus in (256, 80, 7, 1):
+                d = g.sgemm_f32_streamk_describe(M, N, K, v, cus)
+                assert d["partition_ok"], (M, N, K, v, cus, d)
+                assert d["G"] >= 1 and d["max_segments"] <= 3, d
+                if not d["streamk"]:
+                    assert d["workspace_bytes"] == 0 and d["tiles_sk"] == 0
+                    continue
+                seen_sk += 1
+                tiles = d["tiles"]
+                assert d["tiles_dp"] + d["tiles_sk"] == tiles
+                assert d["tiles_dp"] % d["G"] == 0 and d["tiles_sk"] > 0
+                assert d["units"] == d["tiles_sk"] * d["panels"] >= d["G"]
+                assert d["panels"] == -(-K // d["BK"])
+                assert d["workspace_bytes"] == 2 * d["G"] * d["BM"] * d["BN"] * 4
+                assert d["shared_tiles"] <= d["tiles_sk"]
+                seen_dp_and_sk += d["tiles_dp"] > 0
+                seen_tiny += d["units"] < cus
+    assert seen_sk and seen_dp_and_sk and seen_tiny
+
+
+def test_streamk_plan_choices():
+    """The automatic choice shares tiles where a plain grid leaves a mostly idle last round
+    (272 tiles on 256 CUs) and keeps the plain grid where tiles divide evenly."""
+    c3 = g.sgemm_f32_streamk_describe(1023, 1025, 1027, -1, 256)
+    assert c3["streamk"] and c3["shared_tiles"] > 0 and c3["tiles"] == 272
+    for shape in [(8192, 8192, 8192), (1024, 1024, 1024), (16384, 16384, 64)]:
+        d = g.sgemm_f32_streamk_describe(*shape, -1, 256)
+        assert not d["streamk"], d
+        assert d["name"] == g.sgemm_f32_plan_describe(*shape, num_cus=256)["name"]
+    # forced stream-K with a variant whose tiles divide evenly is the plain grid
+    d = g.sgemm_f32_streamk_describe(8192, 8192, 8192, 0, 256)
+    assert not d["streamk"] and d["tiles"] == 1024

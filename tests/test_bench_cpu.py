@@ -11,14 +11,20 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def test_kernel_code_hash(tmp_path):
-    """The hash covers the gfx950 code object inside the built library, is stable, and is
-    None for a file that is not such a library."""
-    h = bench.kernel_code_hash()
-    assert h is not None and len(h) == 16 and h == bench.kernel_code_hash()
+    """Every kernel of the built library gets a hash of its own gfx950 machine code; the
+    hashes are stable, differ between kernels, and are None for a file that is not such a
+    library or a kernel that is not in it."""
+    syms = bench.kernel_symbols()
+    mfma = [s for s in syms if "k_sgemm_mfma" in s]
+    assert len(mfma) >= 5 and any("k_splitk_reduce" in s for s in syms)
+    assert all(len(h) == 16 for h in syms.values())
+    assert len(set(syms[s] for s in mfma)) == len(mfma)
+    assert bench.kernel_code_hash(mfma[0]) == syms[mfma[0]] == bench.kernel_symbols()[mfma[0]]
+    assert bench.kernel_code_hash("no_such_kernel") is None
     junk = tmp_path / "not_a_library.so"
     junk.write_bytes(b"not an ELF file at all" * 10)
-    assert bench.kernel_code_hash(str(junk)) is None
-    assert bench.kernel_code_hash(str(tmp_path / "missing.so")) is None
+    assert bench.kernel_symbols(str(junk)) == {}
+    assert bench.kernel_code_hash(mfma[0], str(tmp_path / "missing.so")) is None
 
 
 def test_traffic_needs_matching_variant():
@@ -39,6 +45,7 @@ def test_committed_traffic_entries_are_well_formed():
             continue
         assert entry["bytes_per_launch"] >= entry["compulsory_bytes"] * 0.9, name
         assert len(entry["kernel_code_sha"]) == 16 and entry["variant"].startswith("mfma_")
+        assert entry["kernel_symbol"].startswith("_ZN5sgemm12k_sgemm_mfma")
 
 
 def test_more_than_one_gpu_is_refused():
