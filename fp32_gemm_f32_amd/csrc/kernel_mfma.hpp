@@ -145,21 +145,27 @@ __device__ inline void static_for(F &&f)
 // once and not read again by the kernel, so the stores carry the non-temporal hint (cache
 // policy bit 1 on gfx950), which measurably speeds up the store-heavy low-K shapes.
 constexpr int kStoreNonTemporal = 2;
-template <int W>
+// Stream-K partial tiles are read back by the fixup kernel right after, so they are stored
+// with the default policy.
+#ifndef SGEMM_PARTIAL_STORE_POLICY
+#define SGEMM_PARTIAL_STORE_POLICY 0
+#endif
+constexpr int kStorePartial = SGEMM_PARTIAL_STORE_POLICY;
+template <int W, int POLICY = kStoreNonTemporal>
 __device__ inline void store_vec(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
                                  typename fvec<W>::type v)
 {
     if constexpr (W == 4) {
         typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, soff,
-                                               kStoreNonTemporal);
+                                               POLICY);
     } else if constexpr (W == 2) {
         typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, voff, soff,
-                                              kStoreNonTemporal);
+                                              POLICY);
     } else {
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, v), r, voff, soff,
-                                              kStoreNonTemporal);
+                                              POLICY);
     }
 }
 
@@ -336,8 +342,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     // the scalar unit. Stream-K workgroups set them per segment (below).
     int lm0 = 0, ln0 = 0, lkb = 0, lK = 0, ls = 0;
     // stream-K: this workgroup's index g, its next unit and the end of its range
-    int sk_g = 0;
-    int64_t sk_i = 0, sk_end = 0;
+    int sk_g = 0, sk_i = 0, sk_end = 0;
     bool sk_mode = false;
     if constexpr (!SK) {
         int tm, tn;
@@ -620,9 +625,10 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     };
 
     // Stores the tile through resource rsc (its first element at offset 0, rows ldc4 bytes
-    // apart), rows_left x cols_left of it inside the destination.
+    // apart), rows_left x cols_left of it inside the destination, with cache policy POLICY.
     auto epilogue = [&](__amdgpu_buffer_rsrc_t rsc, uint32_t ldc4, int rows_left,
-                        int cols_left) {
+                        int cols_left, auto policy_tag) {
+        constexpr int POLICY = decltype(policy_tag)::value;
         // Lane (lo, hi) owns rows lrow + dr (dr = 8 (v / 4) + v % 4 for accumulator v) and
         // columns col .. col + CI - 1 of each of its blocks. The row step dr * ldc goes in
         // the scalar offset; rows past M and chunks that cross N get voffset kOob (the
@@ -646,7 +652,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
                         else out[j] = acc[0][r][g * CI + j][v];
                     }
                     const bool ok = col_full && lrow + dr < rows_left;
-                    store_vec<CI>(rsc, ok ? vbase : kOob, uint32_t(dr) * ldc4, out);
+                    store_vec<CI, POLICY>(rsc, ok ? vbase : kOob, uint32_t(dr) * ldc4, out);
                     store_data_guard<SK && CI >= 4>();
                 }
             }
@@ -666,8 +672,9 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
                         const bool ok = partial && lrow + dr < rows_left;
 #pragma unroll
                         for (int j = 0; j < CI; ++j)
-                            store_vec<1>(rsc, ok && col + j < cols_left ? vbase + 4u * j : kOob,
-                                         uint32_t(dr) * ldc4, acc[0][r][g * CI + j][v]);
+                            store_vec<1, POLICY>(rsc,
+                                                 ok && col + j < cols_left ? vbase + 4u * j : kOob,
+                                                 uint32_t(dr) * ldc4, acc[0][r][g * CI + j][v]);
                     }
                 }
             }
@@ -682,9 +689,9 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
             if (sk_mode) {
                 if (sk_i >= sk_end) break;
                 const int P = p.sk.panels;
-                const int t = int(sk_i / P);
-                const int kb = int(sk_i - int64_t(t) * P);
-                const int ke = int(min(int64_t(P), kb + (sk_end - sk_i)));
+                const int t = sk_i / P;
+                const int kb = sk_i - t * P;
+                const int ke = min(P, kb + (sk_end - sk_i));
                 to_workspace = kb != 0 || ke != P;
                 slot = 2 * sk_g + (sk_i == sk_start(p.sk, sk_g) ? 0 : 1);
                 int tm, tn;
@@ -738,11 +745,11 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
             if (!to_workspace) {
                 const int64_t ec = ls * p.c_split_stride + int64_t(lm0) * ldc + ln0;
                 epilogue(make_rsrc(p.C + ec, p.c_bytes - ec * 4), uint32_t(ldc) * 4u, M - lm0,
-                         N - ln0);
+                         N - ln0, std::integral_constant<int, kStoreNonTemporal>{});
             } else {
                 // a partial tile: all BM x BN sums, packed rows of BN floats
                 epilogue(make_rsrc(p.W + int64_t(slot) * BM * BN, int64_t(BM) * BN * 4),
-                         uint32_t(BN) * 4u, BM, BN);
+                         uint32_t(BN) * 4u, BM, BN, std::integral_constant<int, kStorePartial>{});
             }
         }
         if (!SK || !sk_mode) break;
@@ -795,11 +802,11 @@ __global__ __launch_bounds__(64) void k_splitk_reduce(int M, int N, int splits,
 // Stream-K fixup: every shared tile (streamk.hpp) gets the sum of its workgroups' partial
 // tiles, added in ascending workgroup order, i.e. ascending K, so repeated runs give
 // identical bits. One workgroup of 256 threads per shared tile; a tile that one workgroup
-// covered whole was written to C by it and is skipped. A pass gives each thread
-// kFixupChunks 16-byte chunks of the tile; the partial sums of kFixupBatch contributors
-// are loaded together (kFixupChunks x kFixupBatch loads in flight) and then added in
-// order. W must be 16-byte aligned; C's rows are stored 16 bytes at a time when ldc and C
-// allow it, else element by element.
+// covered whole was written to C by it and is skipped. Each thread owns kFixupChunks
+// 16-byte chunks per pass and loads them from up to kFixupBatch contributors at once
+// (the first batch includes the first contributor, so a tile shared by a few workgroups
+// costs one memory latency), then adds them in order. W must be 16-byte aligned; C's rows
+// are stored 16 bytes at a time when ldc and C allow it, else element by element.
 constexpr int kFixupChunks = 4;
 
 template <int BM, int BN>
@@ -807,7 +814,7 @@ __global__ __launch_bounds__(256) void k_streamk_fixup(GemmArgs p)
 {
     const SkGeom s = p.sk;
     const int t = blockIdx.x;
-    const int64_t u0 = int64_t(t) * s.panels;
+    const int u0 = t * s.panels;
     const int g0 = sk_owner(s, u0), g1 = sk_owner(s, u0 + s.panels - 1);
     if (g0 == g1) return;
     int tm, tn;
@@ -820,13 +827,7 @@ __global__ __launch_bounds__(256) void k_streamk_fixup(GemmArgs p)
     const int tid = threadIdx.x;
     for (int c0 = 0; c0 < CH; c0 += PASS) {
         f32x4 acc[kFixupChunks];
-        {
-            const float *w = p.W + int64_t(sk_fixup_slot(s, g0, g0, t)) * (BM * BN);
-#pragma unroll
-            for (int q = 0; q < kFixupChunks; ++q)
-                acc[q] = *reinterpret_cast<const f32x4 *>(w + 4 * (c0 + q * 256 + tid));
-        }
-        for (int g = g0 + 1; g <= g1; g += kFixupBatch) {
+        for (int g = g0; g <= g1; g += kFixupBatch) {
             f32x4 v[kFixupBatch][kFixupChunks];
 #pragma unroll
             for (int u = 0; u < kFixupBatch; ++u) {
@@ -840,7 +841,8 @@ __global__ __launch_bounds__(256) void k_streamk_fixup(GemmArgs p)
             for (int u = 0; u < kFixupBatch; ++u) {
                 if (g + u > g1) break;
 #pragma unroll
-                for (int q = 0; q < kFixupChunks; ++q) acc[q] += v[u][q];
+                for (int q = 0; q < kFixupChunks; ++q)
+                    acc[q] = (g + u == g0) ? v[u][q] : acc[q] + v[u][q];
             }
         }
 #pragma unroll

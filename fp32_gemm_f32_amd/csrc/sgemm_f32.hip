@@ -435,17 +435,17 @@ extern "C" int sgemm_f32_streamk_describe(int M, int N, int K, int variant, int 
     int64_t shared = 0, max_contrib = 0, max_segments = 0;
     bool ok = true;
     if (sk) {
-        int64_t next = 0;
+        int next = 0;
         std::vector<int> written(size_t(2) * g.G, -1);
         for (int wg = 0; wg < g.G && ok; ++wg) {
-            const int64_t a = sk_start(g, wg), b = sk_start(g, wg + 1);
-            ok = a == next && b >= a;
+            const int a = sk_start(g, wg), b = sk_start(g, wg + 1);
+            ok = a == next && b > a;
             next = b;
             int64_t segs = 0;
-            for (int64_t i = a; i < b && ok;) {
-                const int t = int(i / g.panels);
-                const int kb = int(i - int64_t(t) * g.panels);
-                const int ke = int(std::min<int64_t>(g.panels, kb + (b - i)));
+            for (int i = a; i < b && ok;) {
+                const int t = i / g.panels;
+                const int kb = i - t * g.panels;
+                const int ke = std::min(g.panels, kb + (b - i));
                 if (kb != 0 || ke != g.panels) {
                     const int slot = 2 * wg + (i == a ? 0 : 1);
                     ok = written[size_t(slot)] < 0 && sk_slot(g, wg, t) == slot &&
@@ -459,7 +459,7 @@ extern "C" int sgemm_f32_streamk_describe(int M, int N, int K, int variant, int 
         }
         ok = ok && next == g.iters;
         for (int t = 0; t < g.tiles_sk && ok; ++t) {
-            const int64_t u0 = int64_t(t) * g.panels;
+            const int u0 = t * g.panels;
             const int g0 = sk_owner(g, u0), g1 = sk_owner(g, u0 + g.panels - 1);
             if (g0 == g1) continue;
             ++shared;

@@ -14,8 +14,8 @@
 //   * tiles are numbered in the tile order (groups of kGroupM tile rows, column by column);
 //   * tiles 0 .. tiles_dp - 1 run one per workgroup, as in the plain kernel;
 //   * the next tiles_sk tiles form iters = tiles_sk * panels units, and stream-K
-//     workgroup g (0 <= g < G) takes units [start(g), start(g + 1)) with
-//     start(g) = floor(g * iters / G);
+//     workgroup g (0 <= g < G) takes units [start(g), start(g + 1)): with iters = q G + r,
+//     start(g) = g q + min(g, r), so the first r ranges hold q + 1 units and the rest q;
 //   * inside its range a workgroup visits one segment per tile it touches; a segment that
 //     is not the whole tile stores its partial sums to workspace slot 2g (the first
 //     segment of the range) or 2g + 1 (the last one). A range touches at most one
@@ -35,26 +35,28 @@
 namespace sgemm {
 
 // Contributors whose partial tiles the fixup kernel loads together before adding them.
-constexpr int kFixupBatch = 4;
+constexpr int kFixupBatch = 8;
 
 struct SkGeom {
     int G = 0;            // stream-K workgroups
     int tiles_dp = 0;     // tiles run one per workgroup before the shared ones
     int tiles_sk = 0;     // tiles shared out by K-panel
     int panels = 0;       // K-panels per tile
-    int64_t iters = 0;    // tiles_sk * panels units
+    int iters = 0;        // tiles_sk * panels units
+    int q = 0, r = 0;     // iters = q G + r: the first r ranges hold q + 1 units, the rest q
 };
 
 // First unit of stream-K workgroup g (g = G gives the end of the last range).
-__host__ __device__ inline int64_t sk_start(const SkGeom &s, int g)
+__host__ __device__ inline int sk_start(const SkGeom &s, int g)
 {
-    return int64_t(g) * s.iters / s.G;
+    return g * s.q + (g < s.r ? g : s.r);
 }
 
 // The workgroup whose range holds unit i: the largest g with start(g) <= i.
-__host__ __device__ inline int sk_owner(const SkGeom &s, int64_t i)
+__host__ __device__ inline int sk_owner(const SkGeom &s, int i)
 {
-    return int(((i + 1) * s.G - 1) / s.iters);
+    const int long_units = s.r * (s.q + 1);
+    return i < long_units ? i / (s.q + 1) : s.r + (i - long_units) / s.q;
 }
 
 // Workspace slot of workgroup g's partial sums of shared tile t (an index among the
@@ -69,27 +71,37 @@ __host__ __device__ inline int sk_slot(const SkGeom &s, int g, int t)
 // only when it starts at t's first unit (no division per contributor).
 __host__ __device__ inline int sk_fixup_slot(const SkGeom &s, int g, int g0, int t)
 {
-    return g > g0 ? 2 * g : 2 * g + (sk_start(s, g) == int64_t(t) * s.panels ? 0 : 1);
+    return g > g0 ? 2 * g : 2 * g + (sk_start(s, g) == t * s.panels ? 0 : 1);
 }
 
+// The partition for `tiles` tiles of `panels` K-panels over G resident workgroups. Shares
+// nothing (tiles_sk = 0) when the tiles divide evenly or the shared units would not fit in
+// 31 bits.
 inline SkGeom sk_geometry(int64_t tiles, int panels, int G)
 {
     SkGeom s;
     s.G = G;
     s.panels = panels;
     const int64_t q = tiles / G, r = tiles % G;
-    if (r == 0) {
-        s.tiles_dp = int(tiles);
-    } else if (q == 0) {
-        s.tiles_sk = int(tiles);
-    } else {
-        s.tiles_dp = int((q - 1) * G);
-        s.tiles_sk = int(G + r);
+    int64_t dp = tiles, sk = 0;
+    if (r != 0) {
+        dp = q == 0 ? 0 : (q - 1) * G;
+        sk = tiles - dp;
     }
-    s.iters = int64_t(s.tiles_sk) * panels;
+    if (sk * panels > INT32_MAX || dp > INT32_MAX) {
+        dp = tiles;
+        sk = 0;
+    }
+    s.tiles_dp = int(dp);
+    s.tiles_sk = int(sk);
+    s.iters = int(sk * panels);
     // no empty ranges: a workgroup between two contributors of a tile must have written a
     // slot for it (only possible to violate when q = 0 and the tiles hold few units)
-    if (s.tiles_sk > 0 && s.iters < G) s.G = int(s.iters);
+    if (s.tiles_sk > 0 && s.iters < G) s.G = s.iters;
+    if (s.tiles_sk > 0) {
+        s.q = s.iters / s.G;
+        s.r = s.iters % s.G;
+    }
     return s;
 }
 

@@ -1,8 +1,9 @@
 """The C ABI under HIP graph capture and from several host threads at once.
 
 Graph capture: the hot path launches kernels only (no memset, no allocation, no host
-synchronisation), so a captured call, and split-K's two kernels, replay correctly; every
-replay is checked against the oracle, with eager work and synchronisation between replays.
+synchronisation), so a captured call replays correctly, as do split-K's two kernels and
+stream-K's main and fixup kernels; every replay is checked against the oracle, with eager
+work and synchronisation between replays.
 Threads: the library keeps no mutable state beyond a per-device CU-count cache, so four host
 threads, each on its own stream, get correct results at the same time."""
 import threading
@@ -32,7 +33,9 @@ def int_operands(M, N, K, seed):
 
 
 @pytest.mark.parametrize("M,N,K,kernel", [(1000, 700, 300, "auto"), (257, 259, 1031, "auto"),
-                                          (256, 256, 8192, "splitk"), (64, 96, 0, "auto")])
+                                          (256, 256, 8192, "splitk"), (64, 96, 0, "auto"),
+                                          (1023, 1025, 1027, "streamk"),
+                                          (256, 256, 8192, "streamk")])
 def test_graph_capture_and_replay(gpu, M, N, K, kernel):
     torch = gpu
     A, B = int_operands(M, N, K, M + N + K)
@@ -43,6 +46,10 @@ def test_graph_capture_and_replay(gpu, M, N, K, kernel):
     if kernel == "splitk":
         ws_bytes = g.sgemm_f32_splitk_workspace_size(M, N, K, 4)
         ws = torch.empty(ws_bytes // 4, device="cuda")
+    if kernel == "streamk":
+        ws_bytes = g.sgemm_f32_streamk_workspace_size(M, N, K, -1)
+        assert ws_bytes > 0 and g.sgemm_f32_streamk_describe(M, N, K)["streamk"]
+        ws = torch.empty(ws_bytes // 4, device="cuda")
     args = (M, N, K, dA.data_ptr(), max(K, 1), dB.data_ptr(), N, dC.data_ptr(), N)
     stream = torch.cuda.Stream()
     graph = torch.cuda.CUDAGraph()
@@ -52,6 +59,8 @@ def test_graph_capture_and_replay(gpu, M, N, K, kernel):
             s = torch.cuda.current_stream().cuda_stream
             if kernel == "splitk":
                 g.sgemm_f32_splitk(*args, 4, ws.data_ptr(), ws.numel() * 4, stream=s)
+            elif kernel == "streamk":
+                g.sgemm_f32_streamk(*args, -1, ws.data_ptr(), ws.numel() * 4, stream=s)
             else:
                 g.sgemm_f32(*args, stream=s)
     torch.cuda.synchronize()
