@@ -149,17 +149,28 @@ GemmArgs plain_args(const VariantEntry &e, const Operands &o, const float *A, co
     return p;
 }
 
-// Stream-K with variant vi: the partition for this shape, with G = CUs x the variant's
-// resident workgroups per CU.
-SkGeom streamk_geometry(const Variant &v, const Operands &o, int cus)
-{
-    const int64_t tiles = ((int64_t(o.M) + v.BM - 1) / v.BM) * ((int64_t(o.N) + v.BN - 1) / v.BN);
-    return sk_geometry(tiles, (o.K + v.BK - 1) / v.BK, cus * v.wg_per_cu);
-}
-
 size_t streamk_workspace_bytes(const Variant &v, const SkGeom &g)
 {
     return g.tiles_sk > 0 ? size_t(2) * size_t(g.G) * size_t(v.BM) * size_t(v.BN) * 4u : 0;
+}
+
+// Stream-K with variant v: the partition for this shape, with G = CUs x the variant's
+// resident workgroups per CU; of the two ways to pick the shared tiles (streamk.hpp), the
+// one streamk_cost prices lower. *cost receives that price when non-null.
+SkGeom streamk_geometry(const Variant &v, const Operands &o, int cus, double *cost = nullptr)
+{
+    const int64_t tiles = ((int64_t(o.M) + v.BM - 1) / v.BM) * ((int64_t(o.N) + v.BN - 1) / v.BN);
+    const int panels = (o.K + v.BK - 1) / v.BK;
+    SkGeom best = sk_geometry(tiles, panels, cus * v.wg_per_cu, false);
+    double best_cost = best.tiles_sk ? streamk_cost(v, o, cus, best,
+                                                    streamk_workspace_bytes(v, best)) : 0.0;
+    const SkGeom alt = sk_geometry(tiles, panels, cus * v.wg_per_cu, true);
+    if (alt.tiles_sk > 0 && alt.tiles_dp != best.tiles_dp) {
+        const double c = streamk_cost(v, o, cus, alt, streamk_workspace_bytes(v, alt));
+        if (c < best_cost) { best = alt; best_cost = c; }
+    }
+    if (cost) *cost = best_cost;
+    return best;
 }
 
 // The stream-K entry's choice: the cheapest of every planned variant run plainly or as
@@ -174,9 +185,9 @@ int choose_streamk(const Operands &o, int cus, bool *sk)
         if (!v.planned || !variant_allowed(v, o)) continue;
         const double c_dp = variant_cost(v, o, cus);
         if (best < 0 || c_dp < best_cost) { best = i; best_cost = c_dp; *sk = false; }
-        const SkGeom g = streamk_geometry(v, o, cus);
+        double c_sk = 0.0;
+        const SkGeom g = streamk_geometry(v, o, cus, &c_sk);
         if (g.tiles_sk == 0) continue;
-        const double c_sk = streamk_cost(v, o, cus, g, streamk_workspace_bytes(v, g));
         if (c_sk < best_cost) { best = i; best_cost = c_sk; *sk = true; }
     }
     return best;

@@ -23,8 +23,10 @@
 //   * the fixup kernel adds, for each shared tile, the partial sums of its workgroups in
 //     ascending g, which is ascending K; the result does not depend on timing.
 // With q = tiles / G and r = tiles % G: r = 0 needs no stream-K; q = 0 shares every tile;
-// otherwise the last G + r tiles are shared (each stream-K range then holds more than one
-// whole tile's worth of units, so no segment is very short) and the rest run plainly.
+// otherwise either the last G + r tiles are shared (each stream-K range then holds more
+// than one whole tile's worth of units, so no segment is very short) or only the last r
+// (fewer partial tiles to write and add up), and the rest run plainly; the planner prices
+// both.
 // Every range holds at least one unit (G is lowered to the unit count when needed).
 #pragma once
 
@@ -74,10 +76,12 @@ __host__ __device__ inline int sk_fixup_slot(const SkGeom &s, int g, int g0, int
     return g > g0 ? 2 * g : 2 * g + (sk_start(s, g) == t * s.panels ? 0 : 1);
 }
 
-// The partition for `tiles` tiles of `panels` K-panels over G resident workgroups. Shares
-// nothing (tiles_sk = 0) when the tiles divide evenly or the shared units would not fit in
-// 31 bits.
-inline SkGeom sk_geometry(int64_t tiles, int panels, int G)
+// The partition for `tiles` tiles of `panels` K-panels over G resident workgroups. With
+// q >= 1 full rounds, `remainder_only` shares just the r leftover tiles (short ranges,
+// little partial-sum traffic) instead of the last G + r (ranges longer than a tile).
+// Shares nothing (tiles_sk = 0) when the tiles divide evenly or the shared units would not
+// fit in 31 bits.
+inline SkGeom sk_geometry(int64_t tiles, int panels, int G, bool remainder_only = false)
 {
     SkGeom s;
     s.G = G;
@@ -85,7 +89,7 @@ inline SkGeom sk_geometry(int64_t tiles, int panels, int G)
     const int64_t q = tiles / G, r = tiles % G;
     int64_t dp = tiles, sk = 0;
     if (r != 0) {
-        dp = q == 0 ? 0 : (q - 1) * G;
+        dp = q == 0 ? 0 : (remainder_only ? q : q - 1) * G;
         sk = tiles - dp;
     }
     if (sk * panels > INT32_MAX || dp > INT32_MAX) {

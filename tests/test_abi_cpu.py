@@ -213,7 +213,9 @@ def test_streamk_partition_self_check():
                 seen_sk += 1
                 tiles = d["tiles"]
                 assert d["tiles_dp"] + d["tiles_sk"] == tiles
-                assert d["tiles_dp"] % d["G"] == 0 and d["tiles_sk"] > 0
+                # plain tiles come in whole rounds of the resident workgroups (G may be
+                # lowered afterwards to the shared unit count)
+                assert d["tiles_sk"] > 0 and d["tiles_dp"] % cus == 0
                 assert d["units"] == d["tiles_sk"] * d["panels"] >= d["G"]
                 assert d["panels"] == -(-K // d["BK"])
                 assert d["workspace_bytes"] == 2 * d["G"] * d["BM"] * d["BN"] * 4
