@@ -238,16 +238,46 @@ __device__ inline void tile_coords(int bid, int tiles_m, int tiles_n, int &tm, i
     grouped_tile(xcd_contiguous(bid, tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, int KACC = 1, int KG = 1>
+// The FP32 MFMA instruction a wave tile is built from: an MB x MB block of C gains an
+// MB x KSTEP by KSTEP x MB outer product per instruction; both shapes have the same
+// throughput (4096 FLOP in 16 passes, 2048 in 8). Lane l supplies A[l % MB][l / MB] and
+// B[l / MB][l % MB]; accumulator register v of lane l holds column l % MB and row
+//  * 32 x 32 x 2 (16 registers): 8 (v / 4) + v % 4 + 4 (l / 32);
+//  * 16 x 16 x 4 (4 registers):  v + 4 (l / 16).
+// H = 64 / MB lane groups each read 4 consecutive k of an A row with one ds_read_b128, so a
+// k-group of 4 H values of k feeds 4 MFMA steps (step s uses element s of every group).
+template <int MB> struct MfmaShape;
+template <> struct MfmaShape<32> {
+    static constexpr int H = 2, KSTEP = 2, ACC = 16;
+    typedef f32x16 acc_t;
+    __device__ static acc_t mfma(float a, float b, const acc_t &c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+    }
+    // row of accumulator register v inside the block, for lane group 0
+    static constexpr int row(int v) { return 8 * (v >> 2) + (v & 3); }
+};
+template <> struct MfmaShape<16> {
+    static constexpr int H = 4, KSTEP = 4, ACC = 4;
+    typedef f32x4 acc_t;
+    __device__ static acc_t mfma(float a, float b, const acc_t &c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+    static constexpr int row(int v) { return v; }
+};
+
+template <int BM, int BN, int BK, int WGM, int WGN, int KACC = 1, int KG = 1, int MB = 32>
 struct MfmaTile {
     static constexpr int kGroupThreads = 64 * WGM * WGN;   // one K-group of waves
     static constexpr int kThreads = kGroupThreads * KG;
     static constexpr int WM = BM / WGM;          // wave tile rows
     static constexpr int WN = BN / WGN;          // wave tile columns
-    static constexpr int RB = WM / 32;           // 32-row MFMA blocks per wave
-    static constexpr int CI = WN >= 128 ? 4 : WN / 32;   // column interleave
-    static constexpr int CG = WN / (32 * CI);    // interleaved column groups
-    static constexpr int NACC = RB * CI * CG;    // 32 x 32 accumulator blocks per wave
+    static constexpr int RB = WM / MB;           // MB-row MFMA blocks per wave
+    static constexpr int CI = WN >= 4 * MB ? 4 : WN / MB;   // column interleave
+    static constexpr int CG = WN / (MB * CI);    // interleaved column groups
+    static constexpr int NACC = RB * CI * CG;    // MB x MB accumulator blocks per wave
+    static constexpr int ACC = MfmaShape<MB>::ACC;   // registers per accumulator block
     static constexpr int CPR = BK / 4;           // 16-byte chunks per A-tile row
     static constexpr int A_CH = BM * BK / 4 / kGroupThreads;  // A chunks per thread per panel
     static constexpr int B_CH = BK * BN / 4 / kGroupThreads;  // B chunks per thread per panel
@@ -256,12 +286,12 @@ struct MfmaTile {
     static constexpr int STAGE = A_TILE + B_TILE;
     // partial sums of K-groups 1 .. KG-1, handed to group 0 after the last panel; they reuse
     // the stages' memory
-    static constexpr int RED = (KG - 1) * kGroupThreads * NACC * 16;
+    static constexpr int RED = (KG - 1) * kGroupThreads * NACC * ACC;
     static constexpr int LDS_FLOATS = 2 * KG * STAGE > RED ? 2 * KG * STAGE : RED;
     static constexpr int LDS_BYTES = LDS_FLOATS * 4;
-    static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile is made of 32 x 32 blocks");
-    static_assert(WN % (32 * CI) == 0, "column groups");
-    static_assert(BK % 8 == 0, "four MFMA k-steps consume 8 k values");
+    static_assert(WM % MB == 0 && WN % MB == 0, "wave tile is made of MB x MB blocks");
+    static_assert(WN % (MB * CI) == 0, "column groups");
+    static_assert(BK % (4 * MfmaShape<MB>::KSTEP) == 0, "panels hold whole k-groups");
     static_assert((BM * BK / 4) % kGroupThreads == 0 && (BK * BN / 4) % kGroupThreads == 0,
                   "panel chunks divide evenly over a K-group");
     static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS holds 160 KiB per workgroup");
@@ -287,10 +317,13 @@ struct MfmaTile {
 // one tile each followed by sk.G stream-K workgroups, each walking the segments of its
 // range of K-panel units (streamk.hpp): whole tiles go to C, partial ones to its two
 // workspace slots.
-template <int BM, int BN, int BK, int WGM, int WGN, int KACC, int KG, bool DL, bool SK = false>
+template <int BM, int BN, int BK, int WGM, int WGN, int KACC, int KG, bool DL, bool SK = false,
+          int MB = 32>
 __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
 {
-    using T = MfmaTile<BM, BN, BK, WGM, WGN, KACC, KG>;
+    using T = MfmaTile<BM, BN, BK, WGM, WGN, KACC, KG, MB>;
+    using S = MfmaShape<MB>;
+    typedef typename S::acc_t acc_t;
     constexpr int NT = T::kGroupThreads, WM = T::WM, WN = T::WN, RB = T::RB, CI = T::CI,
                   CG = T::CG, CPR = T::CPR, A_CH = T::A_CH, B_CH = T::B_CH;
     typedef typename fvec<CI>::type bvec;
@@ -302,7 +335,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     const int kg = KG == 1 ? 0 : __builtin_amdgcn_readfirstlane(int(threadIdx.x) / NT);
     const int tid = threadIdx.x % NT;         // thread index inside the K-group
     const int lane = tid & 63;
-    const int lo = lane & 31, hi = lane >> 5;
+    const int lo = lane % MB, hi = lane / MB;   // operand row / column, lane group
     const int wave = tid >> 6;
     const int wm = wave / WGN, wn = wave % WGN;
     // this group's stages: stage s at smem + s * KG * STAGE
@@ -323,7 +356,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     static_assert(NT % CPR == 0 && A_RSTEP % a_swizzle_period<CPR>() == 0 &&
                       NT % (BN / 4) == 0,
                   "chunk assignment strides");
-    static_assert(32 % a_swizzle_period<CPR>() == 0, "a lane's A rows share one swizzle");
+    static_assert(MB % a_swizzle_period<CPR>() == 0, "a lane's A rows share one swizzle");
     // A register-staged lane loads logical chunk tid % CPR of its row and stores it at the
     // swizzled slot; a direct-loading lane owns LDS slot tid % CPR and loads the logical
     // chunk that belongs there.
@@ -452,13 +485,13 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
 
     // KACC accumulator sets take the k-steps in turn (KACC > 1 gives a wave with few MFMA
     // blocks independent accumulation chains); they are summed before the epilogue.
-    f32x16 acc[KACC][RB][CI * CG];
+    acc_t acc[KACC][RB][CI * CG];
 #pragma unroll
     for (int h = 0; h < KACC; ++h)
 #pragma unroll
         for (int i = 0; i < RB; ++i)
 #pragma unroll
-            for (int j = 0; j < CI * CG; ++j) acc[h][i][j] = f32x16{};
+            for (int j = 0; j < CI * CG; ++j) acc[h][i][j] = acc_t{};
 
     // A-operand LDS rows of this lane: row wm*WM + rb*32 + lo, whose swizzle depends on
     // lo only (wm*WM + rb*32 is a multiple of 32).
@@ -469,13 +502,13 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     auto read_a = [&](const float *As, int kb, f32x4 (&a)[RB]) {
 #pragma unroll
         for (int r = 0; r < RB; ++r)
-            a[r] = *reinterpret_cast<const f32x4 *>(As + a_row0 + r * 32 * BK +
-                                                    4 * ((2 * kb + hi) ^ a_sw));
+            a[r] = *reinterpret_cast<const f32x4 *>(As + a_row0 + r * MB * BK +
+                                                    4 * ((S::H * kb + hi) ^ a_sw));
     };
     auto read_b = [&](const float *Bs, int t, bvec (&b)[CG]) {
-        const float *brow = Bs + (8 * (t >> 2) + (t & 3) + 4 * hi) * BN + b_col0;
+        const float *brow = Bs + (4 * S::H * (t >> 2) + (t & 3) + 4 * hi) * BN + b_col0;
 #pragma unroll
-        for (int g = 0; g < CG; ++g) b[g] = *reinterpret_cast<const bvec *>(brow + g * 32 * CI);
+        for (int g = 0; g < CG; ++g) b[g] = *reinterpret_cast<const bvec *>(brow + g * MB * CI);
     };
 
     // Operand registers: a[kb & 1] holds the A values of k-group kb, b[t & 1] the B values
@@ -497,7 +530,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     // panel's barrier, and this panel's reads of `cur` all precede this barrier. With
     // direct loads there are no LDS write steps; the wave waits for its loads before the
     // barrier instead.
-    constexpr int STEPS = BK / 2;
+    constexpr int STEPS = BK / S::KSTEP;
     constexpr int NL = A_CH + B_CH;                     // staging slots per panel
     constexpr int LS = SGEMM_LOAD_STEPS;
     constexpr int WS = SGEMM_WRITE_STEPS;
@@ -514,7 +547,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
             constexpr int t = decltype(tc)::value;
             constexpr int kb = t >> 2, s = t & 3;
             constexpr bool next_b = t + 1 < STEPS;
-            constexpr bool next_a = s == 0 && kb + 1 < BK / 8;
+            constexpr bool next_a = s == 0 && kb + 1 < BK / (4 * S::KSTEP);
             constexpr int w0 = t - (STEPS - 1 - WS);            // write group of this step
             constexpr int l_first = t * PER_LOAD;
             constexpr int n_load = (NEXT && t < LS)
@@ -570,13 +603,13 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
                         float bj;
                         if constexpr (CI == 1) bj = b[t & 1][g]; else bj = b[t & 1][g][j];
                         constexpr int h = t % KACC;
-                        acc[h][r][g * CI + j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                            a[kb & 1][r][s], bj, acc[h][r][g * CI + j], 0, 0, 0);
+                        acc[h][r][g * CI + j] =
+                            S::mfma(a[kb & 1][r][s], bj, acc[h][r][g * CI + j]);
                     }
         });
     };
 
-    static_assert((BK / 2) % KACC == 0, "accumulator sets divide the k-steps of a panel");
+    static_assert(STEPS % KACC == 0, "accumulator sets divide the k-steps of a panel");
 
     // ---- epilogue of one tile: accumulators to C through a buffer resource ----
     const int ldc = p.ldc;
@@ -590,7 +623,8 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
                 for (int j = 0; j < CI * CG; ++j) acc[0][i][j] += acc[h][i][j];
         if constexpr (KG > 1) {
             // every group has read its stages for the last time before red overwrites them;
-            // then group g > 0 writes quad q of its sums at red[((g-1) * NACC * 4 + q) * NT + tid]
+            // then group g > 0 writes quad q of its sums at
+            // red[((g-1) * NACC * ACC / 4 + q) * NT + tid]
             __syncthreads();
             if (kg > 0) {
 #pragma unroll
@@ -598,10 +632,11 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
 #pragma unroll
                     for (int j = 0; j < CI * CG; ++j)
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const f32x16 &x = acc[0][i][j];
+                        for (int q = 0; q < T::ACC / 4; ++q) {
+                            const acc_t &x = acc[0][i][j];
                             const f32x4 v = {x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
-                            const int quad = ((kg - 1) * T::NACC + i * CI * CG + j) * 4 + q;
+                            const int quad =
+                                ((kg - 1) * T::NACC + i * CI * CG + j) * (T::ACC / 4) + q;
                             *reinterpret_cast<f32x4 *>(red + (quad * NT + tid) * 4) = v;
                         }
             }
@@ -613,8 +648,9 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
 #pragma unroll
                         for (int j = 0; j < CI * CG; ++j)
 #pragma unroll
-                            for (int q = 0; q < 4; ++q) {
-                                const int quad = ((g - 1) * T::NACC + i * CI * CG + j) * 4 + q;
+                            for (int q = 0; q < T::ACC / 4; ++q) {
+                                const int quad =
+                                    ((g - 1) * T::NACC + i * CI * CG + j) * (T::ACC / 4) + q;
                                 const f32x4 v =
                                     *reinterpret_cast<const f32x4 *>(red + (quad * NT + tid) * 4);
 #pragma unroll
@@ -636,15 +672,15 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
         // chunks element by element.
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
-            const int lrow = wm * WM + r * 32 + 4 * hi;
+            const int lrow = wm * WM + r * MB + 4 * hi;
 #pragma unroll
             for (int g = 0; g < CG; ++g) {
-                const int col = wn * WN + g * 32 * CI + CI * lo;
+                const int col = wn * WN + g * MB * CI + CI * lo;
                 const uint32_t vbase = uint32_t(lrow) * ldc4 + uint32_t(col) * 4u;
                 const bool col_full = col + CI <= cols_left;
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int dr = 8 * (v >> 2) + (v & 3);
+                for (int v = 0; v < T::ACC; ++v) {
+                    const int dr = S::row(v);
                     bvec out;
 #pragma unroll
                     for (int j = 0; j < CI; ++j) {
@@ -660,15 +696,15 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
         if (cols_left < BN) {
 #pragma unroll
             for (int r = 0; r < RB; ++r) {
-                const int lrow = wm * WM + r * 32 + 4 * hi;
+                const int lrow = wm * WM + r * MB + 4 * hi;
 #pragma unroll
                 for (int g = 0; g < CG; ++g) {
-                    const int col = wn * WN + g * 32 * CI + CI * lo;
+                    const int col = wn * WN + g * MB * CI + CI * lo;
                     const uint32_t vbase = uint32_t(lrow) * ldc4 + uint32_t(col) * 4u;
                     const bool partial = col < cols_left && col + CI > cols_left;
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int dr = 8 * (v >> 2) + (v & 3);
+                    for (int v = 0; v < T::ACC; ++v) {
+                        const int dr = S::row(v);
                         const bool ok = partial && lrow + dr < rows_left;
 #pragma unroll
                         for (int j = 0; j < CI; ++j)
@@ -707,7 +743,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
 #pragma unroll
                     for (int i = 0; i < RB; ++i)
 #pragma unroll
-                        for (int j = 0; j < CI * CG; ++j) acc[h][i][j] = f32x16{};
+                        for (int j = 0; j < CI * CG; ++j) acc[h][i][j] = acc_t{};
                 // every wave is done with the previous segment's LDS (operands and K-group
                 // sums) before this one's first loads overwrite it
                 __syncthreads();
@@ -803,7 +839,8 @@ __global__ __launch_bounds__(64) void k_splitk_reduce(int M, int N, int splits,
 // tiles, added in ascending workgroup order, i.e. ascending K, so repeated runs give
 // identical bits. One workgroup of 256 threads per shared tile; a tile that one workgroup
 // covered whole was written to C by it and is skipped. Each thread owns kFixupChunks
-// 16-byte chunks per pass and loads them from up to kFixupBatch contributors at once
+// 16-byte chunks per pass (fewer in a last, partial pass) and loads them from up to
+// kFixupBatch contributors at once
 // (the first batch includes the first contributor, so a tile shared by a few workgroups
 // costs one memory latency), then adds them in order. W must be 16-byte aligned; C's rows
 // are stored 16 bytes at a time when ldc and C allow it, else element by element.
@@ -822,31 +859,33 @@ __global__ __launch_bounds__(256) void k_streamk_fixup(GemmArgs p)
     const int m0 = tm * BM, n0 = tn * BN;
     const bool c_vec = (p.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(p.C) & 15) == 0;
     constexpr int CH = BM * BN / 4;                 // chunks per tile
-    constexpr int PASS = 256 * kFixupChunks;        // chunks per pass
-    static_assert(CH % PASS == 0, "passes cover the tile");
+    static_assert(CH % 256 == 0, "chunks divide over the workgroup");
+    constexpr int PASS = 256 * kFixupChunks;        // chunks per full pass
     const int tid = threadIdx.x;
-    for (int c0 = 0; c0 < CH; c0 += PASS) {
-        f32x4 acc[kFixupChunks];
+    // one pass over chunks c0 + q 256 + tid, q < NQ
+    auto pass = [&](int c0, auto nq_tag) {
+        constexpr int NQ = decltype(nq_tag)::value;
+        f32x4 acc[NQ];
         for (int g = g0; g <= g1; g += kFixupBatch) {
-            f32x4 v[kFixupBatch][kFixupChunks];
+            f32x4 v[kFixupBatch][NQ];
 #pragma unroll
             for (int u = 0; u < kFixupBatch; ++u) {
                 if (g + u > g1) break;
                 const float *w = p.W + int64_t(sk_fixup_slot(s, g + u, g0, t)) * (BM * BN);
 #pragma unroll
-                for (int q = 0; q < kFixupChunks; ++q)
+                for (int q = 0; q < NQ; ++q)
                     v[u][q] = *reinterpret_cast<const f32x4 *>(w + 4 * (c0 + q * 256 + tid));
             }
 #pragma unroll
             for (int u = 0; u < kFixupBatch; ++u) {
                 if (g + u > g1) break;
 #pragma unroll
-                for (int q = 0; q < kFixupChunks; ++q)
+                for (int q = 0; q < NQ; ++q)
                     acc[q] = (g + u == g0) ? v[u][q] : acc[q] + v[u][q];
             }
         }
 #pragma unroll
-        for (int q = 0; q < kFixupChunks; ++q) {
+        for (int q = 0; q < NQ; ++q) {
             const int c = c0 + q * 256 + tid;
             const int r = c / (BN / 4), col = 4 * (c % (BN / 4));
             const int row = m0 + r, left = p.N - (n0 + col);
@@ -860,7 +899,11 @@ __global__ __launch_bounds__(256) void k_streamk_fixup(GemmArgs p)
                     if (j < left) dst[j] = acc[q][j];
             }
         }
-    }
+    };
+    for (int c0 = 0; c0 + PASS <= CH; c0 += PASS)
+        pass(c0, std::integral_constant<int, kFixupChunks>{});
+    if constexpr (CH % PASS != 0)
+        pass(CH - CH % PASS, std::integral_constant<int, (CH % PASS) / 256>{});
 }
 
 }  // namespace sgemm

@@ -60,18 +60,20 @@ struct VariantEntry {
 
 // PLANNED variants also get a stream-K form and its fixup kernel; the others are never
 // planned and are instantiated in their plain form only.
-template <int BM, int BN, int BK, int WGM, int WGN, int KACC, int KG, bool DL, bool PLANNED>
+template <int BM, int BN, int BK, int WGM, int WGN, int KACC, int KG, bool DL, bool PLANNED,
+          int MB = 32>
 constexpr VariantEntry entry(const char *name, int wg_per_cu, double rate, double overhead,
                              double solo)
 {
     MfmaKernel sk = nullptr, fix = nullptr;
     if constexpr (PLANNED) {
-        sk = &k_sgemm_mfma<BM, BN, BK, WGM, WGN, KACC, KG, DL, true>;
+        sk = &k_sgemm_mfma<BM, BN, BK, WGM, WGN, KACC, KG, DL, true, MB>;
         fix = &k_streamk_fixup<BM, BN>;
     }
     return VariantEntry{
         Variant{name, BM, BN, BK, WGM, WGN, wg_per_cu, rate, overhead, solo, DL, PLANNED},
-        &k_sgemm_mfma<BM, BN, BK, WGM, WGN, KACC, KG, DL>, sk, fix, 64 * WGM * WGN * KG};
+        &k_sgemm_mfma<BM, BN, BK, WGM, WGN, KACC, KG, DL, false, MB>, sk, fix,
+        64 * WGM * WGN * KG};
 }
 
 // Rates (throughput at 8192^3 relative to 140 TFLOP/s), per-tile overheads (in units of K)
@@ -91,12 +93,15 @@ constexpr VariantEntry entry(const char *name, int wg_per_cu, double rate, doubl
 // The last entry stages through registers; it is never planned and stays as the measured
 // comparison for the direct loads (forced through sgemm_f32_variant).
 const VariantEntry kVariants[] = {
-    entry<256, 256, 32, 4, 2, 1, 1, true, true>("mfma_256x256x32_w4x2_dl", 1, 1.055, 40, 1.0),
-    entry<128, 256, 16, 2, 2, 1, 1, true, true>("mfma_128x256x16_w2x2_dl", 2, 1.02, 24, 0.94),
-    entry<128, 128, 32, 2, 2, 1, 1, true, true>("mfma_128x128x32_w2x2_dl", 2, 1.01, 32, 0.90),
-    entry<64, 64, 32, 2, 1, 2, 4, true, true>("mfma_64x64x32_w2x1_acc2_kg4_dl", 1, 0.89, 212, 1.0),
-    entry<64, 64, 32, 2, 1, 1, 2, true, true>("mfma_64x64x32_w2x1_kg2_dl", 2, 0.915, 64, 0.80),
+    entry<256, 256, 32, 4, 2, 1, 1, true, true>("mfma_256x256x32_w4x2_dl", 1, 1.060, 40, 1.0),
+    entry<128, 256, 16, 2, 2, 1, 1, true, true>("mfma_128x256x16_w2x2_dl", 2, 1.020, 24, 0.94),
+    entry<128, 128, 32, 2, 2, 1, 1, true, true>("mfma_128x128x32_w2x2_dl", 2, 1.015, 28, 0.90),
+    entry<64, 64, 32, 2, 1, 2, 4, true, true>("mfma_64x64x32_w2x1_acc2_kg4_dl", 1, 0.880, 212, 1.0),
+    entry<64, 64, 32, 2, 1, 1, 2, true, true>("mfma_64x64x32_w2x1_kg2_dl", 2, 0.905, 60, 0.82),
     entry<256, 256, 32, 4, 2, 1, 1, false, false>("mfma_256x256x32_w4x2", 1, 1.045, 52, 1.0),
+    entry<80, 64, 32, 1, 2, 1, 4, true, true, 16>("mfma16_80x64x32_w1x2_kg4_dl", 1, 0.925, 192, 1.0),
+    entry<80, 64, 32, 1, 2, 1, 2, true, true, 16>("mfma16_80x64x32_w1x2_kg2_dl", 2, 0.935, 56, 0.82),
+    entry<48, 64, 32, 1, 2, 1, 4, true, true, 16>("mfma16_48x64x32_w1x2_kg4_dl", 1, 0.865, 236, 1.0),
 };
 constexpr int kNumVariants = int(sizeof(kVariants) / sizeof(kVariants[0]));
 

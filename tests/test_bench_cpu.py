@@ -44,7 +44,7 @@ def test_committed_traffic_entries_are_well_formed():
         if name.startswith("_"):
             continue
         assert entry["bytes_per_launch"] >= entry["compulsory_bytes"] * 0.9, name
-        assert len(entry["kernel_code_sha"]) == 16 and entry["variant"].startswith("mfma_")
+        assert len(entry["kernel_code_sha"]) == 16 and entry["variant"].startswith("mfma")
         assert entry["kernel_symbol"].startswith("_ZN5sgemm12k_sgemm_mfma")
 
 

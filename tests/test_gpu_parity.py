@@ -90,8 +90,11 @@ def test_every_variant_on_configs(gpu, name):
         assert rep["n_inexact"] == 0 and rep["n_nonfinite"] == 0, (vname, rep)
 
 
-@pytest.mark.parametrize("M,N,K", [(2048, 2048, 2048), (3000, 3000, 3000), (16384, 16384, 256),
-                                   (4096, 4096, 4096)])
+AT_SCALE = [(2048, 2048, 2048), (3000, 3000, 3000), (16384, 16384, 256), (4096, 4096, 4096),
+            (1200, 1200, 500), (1279, 1279, 2000), (1100, 1100, 1100)]
+
+
+@pytest.mark.parametrize("M,N,K", AT_SCALE)
 def test_planned_variants_at_scale(gpu, M, N, K):
     """Every tile variant the plan picks, at a size where it picks it (the mid-size shapes
     of the plan's fit), on small-integer inputs: exact on sampled rows at tile edges."""
@@ -111,8 +114,7 @@ def test_planned_variants_at_scale(gpu, M, N, K):
 
 def test_plan_covers_every_planned_variant(gpu):
     """The shapes above, with the five workloads, reach every variant the plan can pick."""
-    shapes = [(2048, 2048, 2048), (3000, 3000, 3000), (16384, 16384, 256), (4096, 4096, 4096)]
-    shapes += [(w.M, w.N, w.K) for w in wl.WORKLOADS.values()]
+    shapes = AT_SCALE + [(w.M, w.N, w.K) for w in wl.WORKLOADS.values()]
     picked = {g.sgemm_f32_plan_describe(*s)["name"] for s in shapes}
     planned = {n for n in g.variant_names() if n.endswith("_dl")}
     assert planned <= picked, planned - picked

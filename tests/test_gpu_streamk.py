@@ -31,6 +31,12 @@ def planned_variants():
     return [i for i, n in enumerate(g.variant_names()) if n.endswith("_dl")]
 
 
+def shared_c3_variant():
+    """A variant whose stream-K form shares every tile of the ragged 1023x1025x1027 shape
+    (64 x 64 tiles, two workgroups per CU: 272 tiles, fewer than the 512 workgroups)."""
+    return g.variant_names().index("mfma_64x64x32_w2x1_kg2_dl")
+
+
 def run_streamk(torch, A, B, variant=-1, ldc=None, lda=None, ldb=None, ws_fill=float("nan")):
     M, K = A.shape
     N = B.shape[1]
@@ -58,7 +64,11 @@ def hybrid_shape(variant):
     return side * BM - 3, side * BN - 5, 3 * BK + 5
 
 
-@pytest.mark.parametrize("variant", [-1] + list(range(5)))
+# indices past the table's end are skipped at run time
+VARIANT_SLOTS = list(range(12))
+
+
+@pytest.mark.parametrize("variant", [-1] + VARIANT_SLOTS)
 @pytest.mark.parametrize("M,N,K", [(1023, 1025, 1027), (300, 257, 129), (65, 65, 33),
                                    (1, 1, 300), (130, 70, 1000)])
 def test_streamk_exact_integers(gpu, variant, M, N, K):
@@ -74,7 +84,7 @@ def test_streamk_exact_integers(gpu, variant, M, N, K):
     assert rep["n_inexact"] == 0 and rep["n_nonfinite"] == 0, rep
 
 
-@pytest.mark.parametrize("variant", list(range(5)))
+@pytest.mark.parametrize("variant", VARIANT_SLOTS)
 def test_streamk_plain_then_shared_tiles(gpu, variant):
     if variant not in planned_variants():
         pytest.skip("variant has no stream-K form")
@@ -92,7 +102,7 @@ def test_streamk_plain_then_shared_tiles(gpu, variant):
 def test_streamk_workloads_float(gpu, name):
     A, B = wl.operands(name)
     C, d = run_streamk(gpu, A, B)
-    if name == "c3":
+    if name == "sk":
         assert d["streamk"]
     rep = oracle.check(A, B, C)
     assert rep["max_err"] <= TOL and rep["n_nonfinite"] == 0, rep
@@ -100,11 +110,14 @@ def test_streamk_workloads_float(gpu, name):
 
 def test_streamk_deterministic(gpu):
     A, B = wl.operands("c3")
-    first, d = run_streamk(gpu, A, B)
+    v = shared_c3_variant()
+    first, d = run_streamk(gpu, A, B, v)
     first = first.copy()
     assert d["streamk"] and d["shared_tiles"] > 0
+    rep = oracle.check(A, B, first)
+    assert rep["max_err"] <= TOL and rep["n_nonfinite"] == 0, rep
     for fill in (0.0, 1e30, float("nan")):
-        again, _ = run_streamk(gpu, A, B, ws_fill=fill)
+        again, _ = run_streamk(gpu, A, B, v, ws_fill=fill)
         assert np.array_equal(first.view(np.uint32), again.view(np.uint32))
 
 
@@ -133,13 +146,14 @@ def test_streamk_edges(gpu):
     assert (c.result() == 0).all()
     # a workspace smaller than the plan needs is refused before anything runs
     M, N, K = 1023, 1025, 1027
-    need = g.sgemm_f32_streamk_workspace_size(M, N, K, -1)
+    v = shared_c3_variant()
+    need = g.sgemm_f32_streamk_workspace_size(M, N, K, v)
     assert need > 0
     big = torch.zeros(need // 4 + 64, device="cuda")
     _, dA, _ = device_matrix(np.ones((M, K), np.float32))
     _, dB, _ = device_matrix(np.ones((K, N), np.float32))
     c = GuardedC(M, N)
-    rc = lib.sgemm_f32_streamk(M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, c.ptr, N, -1,
+    rc = lib.sgemm_f32_streamk(M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, c.ptr, N, v,
                                big.data_ptr(), need - 4, None)
     assert rc == -6
     torch.cuda.synchronize()

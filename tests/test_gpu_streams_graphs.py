@@ -46,9 +46,12 @@ def test_graph_capture_and_replay(gpu, M, N, K, kernel):
     if kernel == "splitk":
         ws_bytes = g.sgemm_f32_splitk_workspace_size(M, N, K, 4)
         ws = torch.empty(ws_bytes // 4, device="cuda")
+    sk_variant = -1
     if kernel == "streamk":
-        ws_bytes = g.sgemm_f32_streamk_workspace_size(M, N, K, -1)
-        assert ws_bytes > 0 and g.sgemm_f32_streamk_describe(M, N, K)["streamk"]
+        # the 64 x 64 tile with two workgroups per CU shares tiles on both shapes
+        sk_variant = g.variant_names().index("mfma_64x64x32_w2x1_kg2_dl")
+        ws_bytes = g.sgemm_f32_streamk_workspace_size(M, N, K, sk_variant)
+        assert ws_bytes > 0 and g.sgemm_f32_streamk_describe(M, N, K, sk_variant)["streamk"]
         ws = torch.empty(ws_bytes // 4, device="cuda")
     args = (M, N, K, dA.data_ptr(), max(K, 1), dB.data_ptr(), N, dC.data_ptr(), N)
     stream = torch.cuda.Stream()
@@ -60,7 +63,7 @@ def test_graph_capture_and_replay(gpu, M, N, K, kernel):
             if kernel == "splitk":
                 g.sgemm_f32_splitk(*args, 4, ws.data_ptr(), ws.numel() * 4, stream=s)
             elif kernel == "streamk":
-                g.sgemm_f32_streamk(*args, -1, ws.data_ptr(), ws.numel() * 4, stream=s)
+                g.sgemm_f32_streamk(*args, sk_variant, ws.data_ptr(), ws.numel() * 4, stream=s)
             else:
                 g.sgemm_f32(*args, stream=s)
     torch.cuda.synchronize()
