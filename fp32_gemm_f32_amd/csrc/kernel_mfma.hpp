@@ -210,6 +210,16 @@ __host__ __device__ constexpr int a_swizzle_period()
     return CPR == 4 ? 8 : 16;
 }
 
+// Physical 16-byte chunk slot of logical chunk q in B-tile row r. The 32-wide blocks read
+// B rows whole and need none. With 16-wide blocks one read phase covers lane groups 0 and
+// 1, which read rows r and r + 4 of the panel: BN-float rows put those 1 KiB (or 2 KiB)
+// apart, on the same banks, so rows with bit 2 set are moved by half of a 64-bank line.
+template <int MB>
+__host__ __device__ constexpr int b_swizzle(int r)
+{
+    return MB == 16 ? ((r >> 2) & 1) << 3 : 0;
+}
+
 // Position in the tile order of workgroup bid out of `total`: workgroups are dispatched
 // round-robin over the XCDs, so bid % kXcds is the XCD; each XCD gets a contiguous range.
 __device__ inline int xcd_contiguous(int bid, int total)
@@ -365,10 +375,17 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     const uint32_t a_off0 = uint32_t(a_r0) * uint32_t(lda) * 4u + uint32_t(a_q) * 16u;
     const uint32_t a_stride = uint32_t(A_RSTEP) * uint32_t(lda) * 4u;
     const int a_lds0 = a_r0 * BK + 4 * (a_q ^ a_swizzle<CPR>(a_r0));
-    const int b_k0 = tid / (BN / 4), b_c0 = 4 * (tid % (BN / 4));
+    // B: a register-staged lane loads logical chunk tid % (BN/4) of its row and stores it at
+    // the swizzled slot; a direct-loading lane owns slot tid % (BN/4) and loads the logical
+    // chunk that belongs there (the swizzle is one per thread: its rows lie B_KSTEP apart)
+    const int b_k0 = tid / (BN / 4);
+    const int b_q = DL ? (tid % (BN / 4)) ^ b_swizzle<MB>(b_k0) : tid % (BN / 4);
+    const int b_c0 = 4 * b_q;
+    static_assert(MB == 32 || (B_KSTEP % 8 == 0 && BN / 4 >= 16),
+                  "a thread's B rows share one swizzle, which stays inside the row");
     const uint32_t b_off0 = uint32_t(b_k0) * uint32_t(ldb) * 4u + uint32_t(b_c0) * 4u;
     const uint32_t b_stride = uint32_t(B_KSTEP) * uint32_t(ldb) * 4u;
-    const int b_lds0 = b_k0 * BN + b_c0;
+    const int b_lds0 = b_k0 * BN + (MB == 32 ? b_c0 : 4 * (b_q ^ b_swizzle<MB>(b_k0)));
 
     // This workgroup's item: split ls of tile item % tiles, i.e. tile origin (lm0, ln0) and
     // K range [lkb, lkb + lK). All wave-uniform: keep them (and the loops they bound) on
@@ -506,9 +523,21 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
                                                     4 * ((S::H * kb + hi) ^ a_sw));
     };
     auto read_b = [&](const float *Bs, int t, bvec (&b)[CG]) {
-        const float *brow = Bs + (4 * S::H * (t >> 2) + (t & 3) + 4 * hi) * BN + b_col0;
+        if constexpr (MB == 32) {
+            const float *brow = Bs + (4 * S::H * (t >> 2) + (t & 3) + 4 * hi) * BN + b_col0;
 #pragma unroll
-        for (int g = 0; g < CG; ++g) b[g] = *reinterpret_cast<const bvec *>(brow + g * MB * CI);
+            for (int g = 0; g < CG; ++g)
+                b[g] = *reinterpret_cast<const bvec *>(brow + g * MB * CI);
+        } else {
+            // the row's bit 2 is bit 0 of the lane group, so the swizzle is per lane
+            const float *brow = Bs + (4 * S::H * (t >> 2) + (t & 3) + 4 * hi) * BN;
+            const int sw = b_swizzle<MB>(4 * hi);
+#pragma unroll
+            for (int g = 0; g < CG; ++g) {
+                const int col = b_col0 + g * MB * CI;
+                b[g] = *reinterpret_cast<const bvec *>(brow + 4 * ((col >> 2) ^ sw) + (col & 3));
+            }
+        }
     };
 
     // Operand registers: a[kb & 1] holds the A values of k-group kb, b[t & 1] the B values
