@@ -13,10 +13,11 @@
 //    Dominates"): each wavefront owns a WM x WN sub-tile and forms outer products of a
 //    column of A-values and a row of B-values. On gfx950 the outer product is one
 //    instruction: v_mfma_f32_32x32x2_f32 adds a 32 x 2 by 2 x 32 product into a 32 x 32
-//    FP32 accumulator block spread over 16 registers per lane. A wave holds
-//    (WM/32) x (WN/32) such blocks; per k-pair it reads WM/32 A-registers and WN/32
-//    B-registers from LDS and issues (WM/32)(WN/32) MFMAs, the hardware form of the
-//    pages' (TM + TN) reads per TM * TN multiply-adds.
+//    FP32 accumulator block spread over 16 registers per lane (v_mfma_f32_16x16x4_f32, a
+//    16 x 4 by 4 x 16 product into 4 registers, for tiles of 16-row granularity; MB below
+//    is the block size). A wave holds (WM/MB) x (WN/MB) such blocks; per k-step it reads
+//    WM/MB A-values and WN/MB B-values from LDS and issues (WM/MB)(WN/MB) MFMAs, the
+//    hardware form of the pages' (TM + TN) reads per TM * TN multiply-adds.
 //  * Software pipelining ("Shared Memory Tiling", "What tiling does not fix"): two LDS
 //    stages; the global loads of panel p+1 are in flight while the MFMAs consume panel
 //    p, so each panel costs one barrier instead of two.
@@ -37,10 +38,11 @@
 //    element.
 //  * MFMA operand layout (32x32x2): lane l supplies A[l % 32][l / 32] and
 //    B[l / 32][l % 32]; accumulator register v of lane l holds
-//    D[8 (v / 4) + 4 (l / 32) + v % 4][l % 32].
+//    D[8 (v / 4) + 4 (l / 32) + v % 4][l % 32]. For 16x16x4 see MfmaShape<16>.
 //  * K permutation: lanes 0-31 read 4 consecutive k of a row of A with one ds_read_b128
 //    and lanes 32-63 the next 4, so four MFMAs consume 8 k values; the B operand of step
-//    s is read from LDS row 8 kb + s + 4 (l / 32), which pairs the same k on both sides.
+//    s is read from LDS row 8 kb + s + 4 (l / 32), which pairs the same k on both sides
+//    (four lane groups and 16 k values per four steps for 16x16x4).
 //  * Column interleave: a lane reads CI consecutive columns of a B row with one LDS load
 //    and feeds them to CI different MFMA blocks, so MFMA column c of block j is column
 //    CI c + j of the wave tile. In the epilogue each lane then owns CI consecutive
