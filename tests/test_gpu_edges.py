@@ -22,7 +22,7 @@ def gpu():
     return torch
 
 
-SIZES = [1, 2, 3, 5, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 257]
+SIZES = [1, 2, 3, 5, 31, 32, 33, 47, 48, 49, 63, 64, 65, 79, 80, 81, 127, 128, 129, 255, 257]
 SHAPES = sorted({(s, 65, 33) for s in SIZES} | {(65, s, 33) for s in SIZES} |
                 {(65, 33, s) for s in SIZES} |
                 {(257, 255, 129), (129, 257, 255), (300, 520, 9), (7, 600, 600),
