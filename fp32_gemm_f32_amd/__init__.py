@@ -16,6 +16,7 @@ Raw layer (same names and arguments as the C ABI; pointers are integers):
     sgemm_f32_lds_transpose(rows, cols, src, ldi, dst, ldo, tile=32, pad=0, stream=0)
     sgemm_f32_variant(variant, M, N, K, A, lda, B, ldb, C, ldc, stream=0)
     sgemm_f32_plan_describe(M, N, K, A, lda, B, ldb, C, ldc, num_cus=0) -> dict
+    sgemm_f32_variant_info(variant) -> dict, planned_variants() -> [index]
 Tensor layer (torch tensors on the GPU, launched on torch's current stream):
     matmul(A, B, out=None, kernel="auto", variant=-1) -> C
 """
@@ -78,6 +79,8 @@ def _load():
         lib.sgemm_f32_variant_count.restype = i
         lib.sgemm_f32_variant_name.argtypes = [i]
         lib.sgemm_f32_variant_name.restype = ctypes.c_char_p
+        lib.sgemm_f32_variant_info.argtypes = [i, ctypes.c_char_p, i]
+        lib.sgemm_f32_variant_info.restype = i
         lib.sgemm_f32_status_string.argtypes = [i]
         lib.sgemm_f32_status_string.restype = ctypes.c_char_p
         lib.sgemm_f32_plan_describe.argtypes = gemm + [i, ctypes.c_char_p, i]
@@ -161,6 +164,19 @@ def sgemm_f32_variant(variant, M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> Non
 def variant_names() -> list[str]:
     lib = _load()
     return [lib.sgemm_f32_variant_name(i).decode() for i in range(lib.sgemm_f32_variant_count())]
+
+
+def sgemm_f32_variant_info(variant) -> dict:
+    buf = ctypes.create_string_buffer(1024)
+    rc = _load().sgemm_f32_variant_info(variant, buf, len(buf))
+    if rc < 0:
+        raise SgemmError(rc, "sgemm_f32_variant_info")
+    return json.loads(buf.value.decode())
+
+
+def planned_variants() -> list[int]:
+    """Indices of the variants the automatic plan may pick (each has a stream-K form)."""
+    return [i for i in range(len(variant_names())) if sgemm_f32_variant_info(i)["planned"]]
 
 
 def sgemm_f32_plan_describe(M, N, K, A=0, lda=None, B=0, ldb=None, C=0, ldc=None,

@@ -56,6 +56,8 @@ struct VariantEntry {
     MfmaKernel kern_sk;     // stream-K form (NULL for variants that are never planned)
     MfmaKernel fixup;       // its fixup kernel
     int threads;
+    int mb;                 // MFMA block size (32: 32x32x2, 16: 16x16x4)
+    int kg;                 // K-groups
 };
 
 // PLANNED variants also get a stream-K form and its fixup kernel; the others are never
@@ -73,7 +75,7 @@ constexpr VariantEntry entry(const char *name, int wg_per_cu, double rate, doubl
     return VariantEntry{
         Variant{name, BM, BN, BK, WGM, WGN, wg_per_cu, rate, overhead, solo, DL, PLANNED},
         &k_sgemm_mfma<BM, BN, BK, WGM, WGN, KACC, KG, DL, false, MB>, sk, fix,
-        64 * WGM * WGN * KG};
+        64 * WGM * WGN * KG, MB, KG};
 }
 
 // Rates (throughput at 8192^3 relative to 140 TFLOP/s), per-tile overheads (in units of K)
@@ -95,13 +97,14 @@ constexpr VariantEntry entry(const char *name, int wg_per_cu, double rate, doubl
 const VariantEntry kVariants[] = {
     entry<256, 256, 32, 4, 2, 1, 1, true, true>("mfma_256x256x32_w4x2_dl", 1, 1.060, 40, 1.0),
     entry<128, 256, 16, 2, 2, 1, 1, true, true>("mfma_128x256x16_w2x2_dl", 2, 1.020, 24, 0.94),
-    entry<128, 128, 32, 2, 2, 1, 1, true, true>("mfma_128x128x32_w2x2_dl", 2, 1.015, 28, 0.90),
-    entry<64, 64, 32, 2, 1, 2, 4, true, true>("mfma_64x64x32_w2x1_acc2_kg4_dl", 1, 0.880, 212, 1.0),
+    entry<128, 128, 32, 2, 2, 1, 1, true, true>("mfma_128x128x32_w2x2_dl", 2, 1.020, 32, 0.90),
+    entry<64, 64, 32, 2, 1, 2, 4, true, false>("mfma_64x64x32_w2x1_acc2_kg4_dl", 1, 0.880, 212, 1.0),
     entry<64, 64, 32, 2, 1, 1, 2, true, true>("mfma_64x64x32_w2x1_kg2_dl", 2, 0.905, 60, 0.82),
     entry<256, 256, 32, 4, 2, 1, 1, false, false>("mfma_256x256x32_w4x2", 1, 1.045, 52, 1.0),
     entry<80, 64, 32, 1, 2, 1, 4, true, true, 16>("mfma16_80x64x32_w1x2_kg4_dl", 1, 0.925, 192, 1.0),
-    entry<80, 64, 32, 1, 2, 1, 2, true, true, 16>("mfma16_80x64x32_w1x2_kg2_dl", 2, 0.935, 56, 0.82),
-    entry<48, 64, 32, 1, 2, 1, 4, true, true, 16>("mfma16_48x64x32_w1x2_kg4_dl", 1, 0.865, 236, 1.0),
+    entry<80, 64, 32, 1, 2, 1, 2, true, true, 16>("mfma16_80x64x32_w1x2_kg2_dl", 2, 0.930, 56, 0.82),
+    entry<48, 64, 32, 1, 2, 1, 4, true, true, 16>("mfma16_48x64x32_w1x2_kg4_dl", 1, 0.820, 150, 1.0),
+    entry<64, 64, 64, 2, 2, 1, 2, true, true, 16>("mfma16_64x64x64_w2x2_kg2_dl", 1, 0.895, 172, 1.0),
 };
 constexpr int kNumVariants = int(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -587,6 +590,25 @@ extern "C" int sgemm_f32_variant_count(void) { return kNumVariants; }
 extern "C" const char *sgemm_f32_variant_name(int variant)
 {
     return (variant >= 0 && variant < kNumVariants) ? kVariants[variant].v.name : nullptr;
+}
+
+extern "C" int sgemm_f32_variant_info(int variant, char *buf, int buflen)
+{
+    if (!buf || buflen <= 0 || variant < 0 || variant >= kNumVariants) return SGEMM_EINVAL_ARG;
+    const VariantEntry &e = kVariants[variant];
+    const Variant &v = e.v;
+    const int n = snprintf(buf, size_t(buflen),
+                           "{\"variant\": %d, \"name\": \"%s\", \"BM\": %d, \"BN\": %d, "
+                           "\"BK\": %d, \"waves\": [%d, %d], \"k_groups\": %d, "
+                           "\"threads\": %d, \"mfma\": \"%dx%dx%d\", \"wg_per_cu\": %d, "
+                           "\"direct_loads\": %s, \"planned\": %s, \"streamk\": %s, "
+                           "\"rate\": %.3f, \"overhead\": %.1f, \"solo\": %.2f}",
+                           variant, v.name, v.BM, v.BN, v.BK, v.wgm, v.wgn, e.kg, e.threads, e.mb,
+                           e.mb, e.mb == 32 ? 2 : 4, v.wg_per_cu, v.direct ? "true" : "false",
+                           v.planned ? "true" : "false", e.kern_sk ? "true" : "false", v.rate,
+                           v.overhead, v.solo);
+    if (n < 0 || n >= buflen) return SGEMM_EINVAL_ARG;
+    return SGEMM_OK;
 }
 
 extern "C" const char *sgemm_f32_status_string(int status)

@@ -214,6 +214,16 @@ int sgemm_f32_variant(int variant, int M, int N, int K,
 int sgemm_f32_variant_count(void);
 const char *sgemm_f32_variant_name(int variant);
 
+/*
+ * Writes a one-line JSON description of tile variant `variant` into buf (at most buflen
+ * bytes including the NUL): name, tile (BM, BN, BK), waves along M and N, K-groups,
+ * threads, the MFMA instruction shape ("32x32x2" or "16x16x4"), resident workgroups per
+ * CU, direct loads, whether the automatic plan may pick it, whether it has a stream-K
+ * form, and the plan's cost-model parameters (rate, overhead, solo) for it. Host-only, no
+ * GPU needed. Returns SGEMM_OK, or SGEMM_EINVAL_ARG for a bad index or a buffer too small.
+ */
+int sgemm_f32_variant_info(int variant, char *buf, int buflen);
+
 /* A static, NUL-terminated description of a status code. */
 const char *sgemm_f32_status_string(int status);
 

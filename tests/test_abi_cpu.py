@@ -168,7 +168,8 @@ def test_streamk_validation():
     args = (64, 48, 4096, P, 4096, P + (1 << 26), 48, P + (1 << 27), 48)
     ws = P + (1 << 28)
     assert lib.sgemm_f32_streamk(*args, n, ws, 1 << 20, None) == -6          # no such variant
-    unplanned = [i for i in range(n) if not g.variant_names()[i].endswith("_dl")]
+    unplanned = [i for i in range(n) if i not in g.planned_variants()]
+    assert unplanned
     for i in unplanned:                                                     # no stream-K form
         assert lib.sgemm_f32_streamk(*args, i, ws, 1 << 20, None) == -6
     assert lib.sgemm_f32_streamk(*args, -1, None, 1 << 20, None) == -3
@@ -198,8 +199,7 @@ def test_streamk_partition_self_check():
     each K-panel unit belongs to exactly one range, each range holds at least one unit,
     and every partial slot the fixup reads for a shared tile was written for that tile by
     exactly one segment. Checked over random shapes, every variant and several CU counts."""
-    nv = len(g.variant_names())
-    planned = [i for i in range(nv) if g.variant_names()[i].endswith("_dl")]
+    planned = g.planned_variants()
     seen_sk = seen_dp_and_sk = seen_tiny = 0
     for M, N, K in _shapes(60, 7):
         for v in [-1] + planned:
@@ -240,3 +240,23 @@ def test_streamk_plan_choices():
     # forced stream-K with a variant whose tiles divide evenly is the plain grid
     d = g.sgemm_f32_streamk_describe(8192, 8192, 8192, 0, 256)
     assert not d["streamk"] and d["tiles"] == 1024
+
+
+def test_variant_info():
+    names = g.variant_names()
+    planned = g.planned_variants()
+    assert 0 in planned and len(planned) >= 5
+    for i, name in enumerate(names):
+        info = g.sgemm_f32_variant_info(i)
+        assert info["name"] == name and info["variant"] == i
+        assert info["mfma"] in ("32x32x2", "16x16x4")
+        assert name.startswith("mfma16_") == (info["mfma"] == "16x16x4")
+        w0, w1 = info["waves"]
+        assert info["threads"] == 64 * w0 * w1 * info["k_groups"]
+        assert info["streamk"] == info["planned"]          # planned variants have a stream-K form
+        assert info["direct_loads"] == name.endswith("_dl")
+        assert f"{info['BM']}x{info['BN']}x{info['BK']}" in name
+    with pytest.raises(g.SgemmError):
+        g.sgemm_f32_variant_info(len(names))
+    buf = ctypes.create_string_buffer(8)
+    assert g.library().sgemm_f32_variant_info(0, buf, 8) == -6

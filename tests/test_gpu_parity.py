@@ -116,5 +116,5 @@ def test_plan_covers_every_planned_variant(gpu):
     """The shapes above, with the five workloads, reach every variant the plan can pick."""
     shapes = AT_SCALE + [(w.M, w.N, w.K) for w in wl.WORKLOADS.values()]
     picked = {g.sgemm_f32_plan_describe(*s)["name"] for s in shapes}
-    planned = {n for n in g.variant_names() if n.endswith("_dl")}
+    planned = {g.variant_names()[i] for i in g.planned_variants()}
     assert planned <= picked, planned - picked

@@ -28,7 +28,7 @@ def gpu():
 
 
 def planned_variants():
-    return [i for i, n in enumerate(g.variant_names()) if n.endswith("_dl")]
+    return g.planned_variants()
 
 
 def shared_c3_variant():
