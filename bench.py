@@ -61,25 +61,28 @@ def _elf_sections(data: bytes) -> dict:
 
 
 def _gfx950_code_objects(lib_path: str):
-    """The gfx950 device code objects inside the library's offload bundle (empty when the
-    file is missing or is not such a library)."""
+    """The gfx950 device code objects inside the library's offload bundles, one bundle per
+    translation unit (empty when the file is missing or is not such a library)."""
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
     try:
         with open(lib_path, "rb") as f:
             fat = _elf_sections(f.read())[".hip_fatbin"][0]
     except (OSError, KeyError, struct.error, ValueError):
         return []
-    if not fat.startswith(b"__CLANG_OFFLOAD_BUNDLE__"):
-        return []
     out = []
-    n, = struct.unpack_from("<Q", fat, 24)
-    off = 32
-    for _ in range(n):
-        o, size, tlen = struct.unpack_from("<QQQ", fat, off)
-        off += 24
-        triple = fat[off:off + tlen].decode()
-        off += tlen
-        if "gfx950" in triple:
-            out.append(fat[o:o + size])
+    start = fat.find(magic)
+    while start >= 0:
+        n, = struct.unpack_from("<Q", fat, start + 24)
+        off, end = start + 32, start + 32
+        for _ in range(n):
+            o, size, tlen = struct.unpack_from("<QQQ", fat, off)
+            off += 24
+            triple = fat[off:off + tlen].decode()
+            off += tlen
+            end = max(end, start + o + size)
+            if "gfx950" in triple:
+                out.append(fat[start + o:start + o + size])
+        start = fat.find(magic, max(end, start + 1))
     return out
 
 

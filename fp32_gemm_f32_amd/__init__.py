@@ -16,7 +16,8 @@ Raw layer (same names and arguments as the C ABI; pointers are integers):
     sgemm_f32_lds_transpose(rows, cols, src, ldi, dst, ldo, tile=32, pad=0, stream=0)
     sgemm_f32_variant(variant, M, N, K, A, lda, B, ldb, C, ldc, stream=0)
     sgemm_f32_plan_describe(M, N, K, A, lda, B, ldb, C, ldc, num_cus=0) -> dict
-    sgemm_f32_variant_info(variant) -> dict, planned_variants() -> [index]
+    sgemm_f32_variant_info(variant) -> dict, planned_variants() -> [index],
+    streamk_variants() -> [index]
 Tensor layer (torch tensors on the GPU, launched on torch's current stream):
     matmul(A, B, out=None, kernel="auto", variant=-1) -> C
 """
@@ -175,8 +176,13 @@ def sgemm_f32_variant_info(variant) -> dict:
 
 
 def planned_variants() -> list[int]:
-    """Indices of the variants the automatic plan may pick (each has a stream-K form)."""
+    """Indices of the variants the automatic plan may pick."""
     return [i for i in range(len(variant_names())) if sgemm_f32_variant_info(i)["planned"]]
+
+
+def streamk_variants() -> list[int]:
+    """Indices of the variants with a stream-K form (those sgemm_f32_streamk accepts)."""
+    return [i for i in range(len(variant_names())) if sgemm_f32_variant_info(i)["streamk"]]
 
 
 def sgemm_f32_plan_describe(M, N, K, A=0, lda=None, B=0, ldb=None, C=0, ldc=None,

@@ -20,7 +20,11 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libsgemm_f32.so")
 BUILD_DIR = os.path.join(PKG, "_build")
-SOURCES = [os.path.join(CSRC, "sgemm_f32.hip")]
+# Translation units and whether their MFMA accumulators are held in VGPRs (see flags()).
+# The one-wave-per-SIMD kernel keeps 256 accumulators per lane in AGPRs, so it is compiled
+# on its own, without that option.
+SOURCES = [(os.path.join(CSRC, "sgemm_f32.hip"), True),
+           (os.path.join(CSRC, "sgemm_regpanel.hip"), False)]
 ARCH = "gfx950"
 
 
@@ -31,33 +35,49 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the library)")
 
 
-def flags() -> list[str]:
-    return [
+def flags(vgpr_form: bool = True) -> list[str]:
+    f = [
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         # packed FP32 instructions stay off: the compiler must not form them from float2
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        # MFMA accumulators stay in VGPRs (every kernel fits in 256 registers); left to its
-        # heuristics the register allocator moves them between AGPRs and VGPRs on each
-        # iteration of the persistent tile loop
-        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-Wall", "-Wno-unused-command-line-argument",
         f"-I{INCLUDE}", f"-I{CSRC}",
     ]
+    if vgpr_form:
+        # MFMA accumulators stay in VGPRs (every kernel of the unit fits in 256 registers);
+        # left to its heuristics the register allocator moves them between AGPRs and VGPRs
+        # on each iteration of the persistent stream-K tile loop
+        f += ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+    return f
 
 
 def build(asm: bool = False, verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     report = os.path.join(BUILD_DIR, "resource_usage.txt")
-    cmd = [hipcc(), *flags(), "-shared", *SOURCES, "-o", OUT + ".tmp",
-           "-Rpass-analysis=kernel-resource-usage"]
+    objs, log = [], []
+    for src, vgpr_form in SOURCES:
+        obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+        cmd = [hipcc(), *flags(vgpr_form), "-c", src, "-o", obj,
+               "-Rpass-analysis=kernel-resource-usage"]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        log.append(r.stderr)
+        if r.returncode != 0:
+            with open(report, "w") as f:
+                f.write("".join(log))
+            sys.stderr.write(r.stderr[-8000:])
+            raise RuntimeError(f"hipcc failed ({r.returncode}) on {src}; see {report}")
+        objs.append(obj)
+    with open(report, "w") as f:
+        f.write("".join(log))
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-fPIC", "-shared", *objs, "-o", OUT + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
-    with open(report, "w") as f:
-        f.write(r.stderr)
     if r.returncode != 0:
         sys.stderr.write(r.stderr[-8000:])
-        raise RuntimeError(f"hipcc failed ({r.returncode}); see {report}")
+        raise RuntimeError(f"hipcc link failed ({r.returncode})")
     os.replace(OUT + ".tmp", OUT)
     if asm:
         assemble()
@@ -65,11 +85,20 @@ def build(asm: bool = False, verbose: bool = False) -> str:
 
 
 def assemble(out: str | None = None) -> str:
-    """Write the gfx950 assembly of the library's device code (same flags as the build)."""
+    """Write the gfx950 assembly of the library's device code (same flags as the build),
+    all translation units into one file."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     s = out or os.path.join(BUILD_DIR, "sgemm_f32.s")
-    subprocess.run([hipcc(), *flags(), "--cuda-device-only", "-S", *SOURCES, "-o", s],
-                   check=True)
+    parts = []
+    for src, vgpr_form in SOURCES:
+        part = s + "." + os.path.basename(src) + ".s"
+        subprocess.run([hipcc(), *flags(vgpr_form), "--cuda-device-only", "-S", src, "-o", part],
+                       check=True)
+        with open(part) as f:
+            parts.append(f.read())
+        os.remove(part)
+    with open(s, "w") as f:
+        f.write("\n".join(parts))
     return s
 
 

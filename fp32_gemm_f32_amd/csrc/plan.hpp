@@ -30,6 +30,7 @@ struct Variant {
     double solo;            // rate factor when a CU holds fewer than wg_per_cu tiles
     bool direct;            // direct global -> LDS loads
     bool planned;           // candidate for the automatic choice (else forced use only)
+    bool splitk = true;     // candidate for split-K items too
 };
 
 struct Operands {
@@ -97,7 +98,7 @@ inline int choose_variant(const Variant (&table)[NV], const Operands &o, int cus
     double best_cost = 0.0;
     for (int i = 0; i < NV; ++i) {
         const Variant &v = table[i];
-        if (!v.planned || !variant_allowed(v, o)) continue;
+        if (!v.planned || !variant_allowed(v, o) || (o.splits > 1 && !v.splitk)) continue;
         const double c = variant_cost(v, o, cus);
         if (best < 0 || c < best_cost) { best = i; best_cost = c; }
     }

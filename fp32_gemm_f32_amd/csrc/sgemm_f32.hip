@@ -50,14 +50,20 @@ int fill_zero(int M, int N, float *C, int ldc, void *stream)
 
 typedef void (*MfmaKernel)(GemmArgs);
 
+}  // namespace
+// k_sgemm_regpanel lives in sgemm_regpanel.hip (a translation unit built with other options)
+MfmaKernel regpanel_kernel();
+namespace {
+
 struct VariantEntry {
     Variant v;
     MfmaKernel kern;
-    MfmaKernel kern_sk;     // stream-K form (NULL for variants that are never planned)
+    MfmaKernel kern_sk;     // stream-K form (NULL for variants without one)
     MfmaKernel fixup;       // its fixup kernel
     int threads;
     int mb;                 // MFMA block size (32: 32x32x2, 16: 16x16x4)
     int kg;                 // K-groups
+    const char *kernel;     // kernel family: "mfma" (kernel_mfma.hpp) or "regpanel"
 };
 
 // PLANNED variants also get a stream-K form and its fixup kernel; the others are never
@@ -75,16 +81,29 @@ constexpr VariantEntry entry(const char *name, int wg_per_cu, double rate, doubl
     return VariantEntry{
         Variant{name, BM, BN, BK, WGM, WGN, wg_per_cu, rate, overhead, solo, DL, PLANNED},
         &k_sgemm_mfma<BM, BN, BK, WGM, WGN, KACC, KG, DL, false, MB>, sk, fix,
-        64 * WGM * WGN * KG, MB, KG};
+        64 * WGM * WGN * KG, MB, KG, "mfma"};
+}
+
+// The one-wave-per-SIMD kernel (kernel_regpanel.hpp): 256 x 256 tiles of four 128 x 128
+// waves. It is planned for the plain product only: split-K and stream-K serve shapes with
+// few tiles, where the smaller tiles win.
+VariantEntry regpanel_entry(const char *name, double rate, double overhead)
+{
+    return VariantEntry{
+        Variant{name, 256, 256, 32, 2, 2, 1, rate, overhead, 1.0, false, true, false},
+        regpanel_kernel(), nullptr, nullptr, 256, 32, 1, "regpanel"};
 }
 
 // Rates (throughput at 8192^3 relative to 140 TFLOP/s), per-tile overheads (in units of K)
-// and solo factors are fitted on MI355X to one run that timed every variant on twelve
-// shapes from 1024^3 to 16384^2 x 64; the plan then picks the measured best on nine of
-// them and a variant within 0.7 % of it on the other three. All planned variants load
-// their panels straight into LDS ("_dl"), which measured as fast as or faster than staging
-// through registers on every one of those shapes.
-//  * 256 x 256 (8 waves of 64 x 128): long K and many tiles.
+// and solo factors are fitted on MI355X to runs that timed every variant on 19 shapes from
+// 1023 x 1025 x 1027 to 16384^2 x 64; the plan then picks a variant within 1 % of the
+// measured best on all of them. The template kernel's planned variants load their panels
+// straight into LDS ("_dl"), which measured as fast as or faster than staging through
+// registers on every one of those shapes.
+//  * 256 x 256, one wave per SIMD ("_rp", kernel_regpanel.hpp): long K and many tiles
+//    (8192^3, 4096^3, 8192^2 x 1024); plain product only.
+//  * 256 x 256 (8 waves of 64 x 128): dominated by "_rp" in the plain product; planned for
+//    its stream-K form, which shares the tiles of large ragged tile counts.
 //  * 128 x 256 (4 waves, 48 KiB of LDS): two workgroups per CU, so one stores while the
 //    other computes; best when K is short and C's stores weigh as much as the MFMAs.
 //  * 128 x 128 (4 waves, two per CU): shapes with about one 256 x 256 tile per CU or fewer.
@@ -105,6 +124,7 @@ const VariantEntry kVariants[] = {
     entry<80, 64, 32, 1, 2, 1, 2, true, true, 16>("mfma16_80x64x32_w1x2_kg2_dl", 2, 0.930, 56, 0.82),
     entry<48, 64, 32, 1, 2, 1, 4, true, true, 16>("mfma16_48x64x32_w1x2_kg4_dl", 1, 0.820, 150, 1.0),
     entry<64, 64, 64, 2, 2, 1, 2, true, true, 16>("mfma16_64x64x64_w2x2_kg2_dl", 1, 0.895, 172, 1.0),
+    regpanel_entry("mfma_256x256x32_w2x2_rp", 1.085, 44),
 };
 constexpr int kNumVariants = int(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -193,6 +213,7 @@ int choose_streamk(const Operands &o, int cus, bool *sk)
         if (!v.planned || !variant_allowed(v, o)) continue;
         const double c_dp = variant_cost(v, o, cus);
         if (best < 0 || c_dp < best_cost) { best = i; best_cost = c_dp; *sk = false; }
+        if (!kVariants[i].kern_sk) continue;
         double c_sk = 0.0;
         const SkGeom g = streamk_geometry(v, o, cus, &c_sk);
         if (g.tiles_sk == 0) continue;
@@ -602,11 +623,12 @@ extern "C" int sgemm_f32_variant_info(int variant, char *buf, int buflen)
                            "\"BK\": %d, \"waves\": [%d, %d], \"k_groups\": %d, "
                            "\"threads\": %d, \"mfma\": \"%dx%dx%d\", \"wg_per_cu\": %d, "
                            "\"direct_loads\": %s, \"planned\": %s, \"streamk\": %s, "
-                           "\"rate\": %.3f, \"overhead\": %.1f, \"solo\": %.2f}",
+                           "\"rate\": %.3f, \"overhead\": %.1f, \"solo\": %.2f, "
+                           "\"kernel\": \"%s\", \"splitk\": %s}",
                            variant, v.name, v.BM, v.BN, v.BK, v.wgm, v.wgn, e.kg, e.threads, e.mb,
                            e.mb, e.mb == 32 ? 2 : 4, v.wg_per_cu, v.direct ? "true" : "false",
                            v.planned ? "true" : "false", e.kern_sk ? "true" : "false", v.rate,
-                           v.overhead, v.solo);
+                           v.overhead, v.solo, e.kernel, v.splitk ? "true" : "false");
     if (n < 0 || n >= buflen) return SGEMM_EINVAL_ARG;
     return SGEMM_OK;
 }

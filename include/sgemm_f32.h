@@ -200,7 +200,8 @@ int sgemm_f32_lds_transpose(int rows, int cols,
  * index below sgemm_f32_variant_count(), else SGEMM_EINVAL_ARG. Every variant computes
  * the same product for every shape; they differ in tile shape, waves and how panels reach
  * LDS (names ending in "_dl" load straight from global memory into LDS, the others stage
- * through registers), and some are never chosen automatically (kept for comparison). A
+ * through registers; "_rp" is the one-wave-per-SIMD kernel that holds a whole K-panel's
+ * operands in registers), and some are never chosen automatically (kept for comparison). A
  * variant whose 31-bit buffer offsets cannot span one workgroup's rows of A or C or one
  * K-panel of B returns SGEMM_ETOO_LARGE.
  */
@@ -219,8 +220,10 @@ const char *sgemm_f32_variant_name(int variant);
  * bytes including the NUL): name, tile (BM, BN, BK), waves along M and N, K-groups,
  * threads, the MFMA instruction shape ("32x32x2" or "16x16x4"), resident workgroups per
  * CU, direct loads, whether the automatic plan may pick it, whether it has a stream-K
- * form, and the plan's cost-model parameters (rate, overhead, solo) for it. Host-only, no
- * GPU needed. Returns SGEMM_OK, or SGEMM_EINVAL_ARG for a bad index or a buffer too small.
+ * form, the plan's cost-model parameters (rate, overhead, solo) for it, the kernel family
+ * ("mfma": the LDS-double-buffered template; "regpanel": the one-wave-per-SIMD kernel) and
+ * whether split-K may use it. Host-only, no GPU needed. Returns SGEMM_OK, or
+ * SGEMM_EINVAL_ARG for a bad index or a buffer too small.
  */
 int sgemm_f32_variant_info(int variant, char *buf, int buflen);
 

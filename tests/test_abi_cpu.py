@@ -168,9 +168,9 @@ def test_streamk_validation():
     args = (64, 48, 4096, P, 4096, P + (1 << 26), 48, P + (1 << 27), 48)
     ws = P + (1 << 28)
     assert lib.sgemm_f32_streamk(*args, n, ws, 1 << 20, None) == -6          # no such variant
-    unplanned = [i for i in range(n) if i not in g.planned_variants()]
-    assert unplanned
-    for i in unplanned:                                                     # no stream-K form
+    without = [i for i in range(n) if i not in g.streamk_variants()]
+    assert without
+    for i in without:                                                       # no stream-K form
         assert lib.sgemm_f32_streamk(*args, i, ws, 1 << 20, None) == -6
     assert lib.sgemm_f32_streamk(*args, -1, None, 1 << 20, None) == -3
     assert lib.sgemm_f32_streamk(*args, -1, ws + 4, 1 << 20, None) == -3    # not 16-byte aligned
@@ -199,7 +199,7 @@ def test_streamk_partition_self_check():
     each K-panel unit belongs to exactly one range, each range holds at least one unit,
     and every partial slot the fixup reads for a shared tile was written for that tile by
     exactly one segment. Checked over random shapes, every variant and several CU counts."""
-    planned = g.planned_variants()
+    planned = g.streamk_variants()
     seen_sk = seen_dp_and_sk = seen_tiny = 0
     for M, N, K in _shapes(60, 7):
         for v in [-1] + planned:
@@ -253,7 +253,10 @@ def test_variant_info():
         assert name.startswith("mfma16_") == (info["mfma"] == "16x16x4")
         w0, w1 = info["waves"]
         assert info["threads"] == 64 * w0 * w1 * info["k_groups"]
-        assert info["streamk"] == info["planned"]          # planned variants have a stream-K form
+        assert info["kernel"] in ("mfma", "regpanel")
+        # planned variants of the template kernel have a stream-K form; the regpanel kernel
+        # has none
+        assert info["streamk"] == (info["planned"] and info["kernel"] == "mfma")
         assert info["direct_loads"] == name.endswith("_dl")
         assert f"{info['BM']}x{info['BN']}x{info['BK']}" in name
     with pytest.raises(g.SgemmError):

@@ -112,9 +112,19 @@ def test_planned_variants_at_scale(gpu, M, N, K):
     assert rep["n_nonfinite"] == 0 and rep["n_inexact"] == 0, (plan["name"], rep)
 
 
+# large shapes whose tile counts fall just past a whole round of 256 x 256 tiles
+STREAMK_PLAN_SHAPES = [(4500, 4500, 8192), (5000, 5000, 2048)]
+
+
 def test_plan_covers_every_planned_variant(gpu):
-    """The shapes above, with the five workloads, reach every variant the plan can pick."""
+    """The shapes above, with the five workloads, reach every variant the plan can pick:
+    through the plain product's plan, or through the stream-K entry's plan (the 8-wave
+    256 x 256 variant is planned for its stream-K form)."""
     shapes = AT_SCALE + [(w.M, w.N, w.K) for w in wl.WORKLOADS.values()]
     picked = {g.sgemm_f32_plan_describe(*s)["name"] for s in shapes}
+    for s in shapes + STREAMK_PLAN_SHAPES:
+        d = g.sgemm_f32_streamk_describe(*s)
+        if d["streamk"]:
+            picked.add(d["name"])
     planned = {g.variant_names()[i] for i in g.planned_variants()}
     assert planned <= picked, planned - picked

@@ -27,8 +27,8 @@ def gpu():
     return torch
 
 
-def planned_variants():
-    return g.planned_variants()
+def streamk_variants():
+    return g.streamk_variants()
 
 
 def shared_c3_variant():
@@ -72,7 +72,7 @@ VARIANT_SLOTS = list(range(12))
 @pytest.mark.parametrize("M,N,K", [(1023, 1025, 1027), (300, 257, 129), (65, 65, 33),
                                    (1, 1, 300), (130, 70, 1000)])
 def test_streamk_exact_integers(gpu, variant, M, N, K):
-    if variant >= 0 and variant not in planned_variants():
+    if variant >= 0 and variant not in streamk_variants():
         pytest.skip("variant has no stream-K form")
     rng = np.random.default_rng(M + 7 * N + 13 * K + variant)
     A = wl.draw(rng, (M, K), "int")
@@ -86,7 +86,7 @@ def test_streamk_exact_integers(gpu, variant, M, N, K):
 
 @pytest.mark.parametrize("variant", VARIANT_SLOTS)
 def test_streamk_plain_then_shared_tiles(gpu, variant):
-    if variant not in planned_variants():
+    if variant not in streamk_variants():
         pytest.skip("variant has no stream-K form")
     M, N, K = hybrid_shape(variant)
     rng = np.random.default_rng(variant + 101)
