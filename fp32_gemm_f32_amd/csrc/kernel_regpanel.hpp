@@ -54,13 +54,14 @@ constexpr int STEPS = 16;                       // k-steps of 2 per panel
 constexpr int LOAD_STEPS = 8;                   // steps 4 .. 11 carry the global loads
 static_assert(LDS_FLOATS * 4 <= 160 * 1024, "LDS");
 
-// A buffer resource over bytes [0, rem) from base, rem clamped to what the offsets can reach.
-__device__ inline __amdgpu_buffer_rsrc_t rsrc(const float *base, int64_t rem)
+// Size of a buffer resource that reaches every offset a load can use (all offsets stay
+// below 2^31 - 64: the host checks BM * lda and BK * ldb against it).
+constexpr uint32_t kFullRange = kOob - 64u;
+
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(const float *base, uint32_t bytes)
 {
-    int32_t n = 0;
-    if (rem > 0) n = rem >= int64_t(kOob) ? int32_t(kOob - 64) : int32_t(rem);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0, n,
-                                             kBufferWord3);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0,
+                                             int32_t(bytes), kBufferWord3);
 }
 
 // Release/acquire of LDS only around the barrier: the wave waits for its own LDS accesses,
@@ -95,8 +96,15 @@ void k_sgemm_regpanel(GemmArgs p)
     const int kb = __builtin_amdgcn_readfirstlane(ls * p.k_chunk);
     const int ke = __builtin_amdgcn_readfirstlane(min(p.K, kb + p.k_chunk));
     const int M = p.M, N = p.N, lda = p.lda, ldb = p.ldb;
-    // bytes from B to the end of row ke - 1: rows of later splits read as zero
-    const int64_t b_end = (int64_t(ke - 1) * ldb + N) * 4;
+    // Resource sizes, in 32-bit scalar min/select chains (the panel loop must not need the
+    // vector ALU, nor branch, for them). A panel's A resource starts at (m0, k0): when the
+    // tile holds A's last row it ends at A's end, a_end - 4 k0 bytes on; otherwise a_end is
+    // all ones and the size saturates to the full range (4 K < 2^31). A panel's B resource
+    // starts at (k0, n0) and ends at the end of row ke - 1, so rows of later splits read as
+    // zero; with more than BK rows left, BK + 1 rows cover every offset the loads use. The
+    // host's offset check keeps these products below 2^31.
+    const uint32_t a_end =
+        M - m0 <= BM ? uint32_t((M - 1 - m0) * lda + p.K) * 4u : 0xffffffffu;
 
     // ---- staging: thread tid loads A rows a_r + 32 i (16-byte chunk a_q of the panel's
     // 32 columns) and B rows b_r + 4 i (chunk b_q of the tile's 256 columns), i < 8
@@ -122,8 +130,14 @@ void k_sgemm_regpanel(GemmArgs p)
         if (lo_j == 0) {
             kp = k0;
             const int64_t ea = int64_t(m0) * lda + k0, eb = int64_t(k0) * ldb + n0;
-            ra = rsrc(p.A + ea, k0 < ke ? p.a_bytes - ea * 4 : 0);
-            rb = rsrc(p.B + eb, k0 < ke ? b_end - eb * 4 : 0);
+            const int rows = ke - k0;
+            const uint32_t na = min(a_end - 4u * uint32_t(k0), kFullRange);
+            const uint32_t nb =
+                min(uint32_t((min(rows, BK + 1) - 1) * ldb + (N - n0)) * 4u, kFullRange);
+            // a panel past the K range reads zeros (selects, not a branch: the panel loop
+            // stays one block)
+            ra = rsrc(p.A + ea, rows > 0 ? na : 0u);
+            rb = rsrc(p.B + eb, rows > 0 ? nb : 0u);
         }
 #pragma unroll
         for (int j = lo_j; j < hi_j; ++j) {
