@@ -38,8 +38,12 @@
 //    floats with the 16-byte chunk swizzle a_swizzle<8>, B rows of 256 floats as they are;
 //    both read phases and both write phases are conflict-free.
 //
-// Items are kernel_mfma.hpp's: workgroup i computes tile i % tiles over split i / tiles of
-// K (one split for the plain product), so the kernel also serves split-K.
+// Items are kernel_mfma.hpp's: without SK, workgroup i computes tile i % tiles over split
+// i / tiles of K (one split for the plain product; the plan gives this kernel whole tiles).
+// With SK the grid is sk.tiles_dp workgroups of one whole tile each followed by sk.G
+// stream-K workgroups, each walking the segments of its range of K-panel units
+// (streamk.hpp): a segment that covers its whole tile stores it to C, any other stores its
+// partial sums to the workgroup's workspace slot for k_streamk_fixup<256, 256> to add.
 #pragma once
 
 #include "kernel_mfma.hpp"
@@ -74,27 +78,21 @@ __device__ inline void lds_barrier()
 }
 }  // namespace regpanel
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void k_sgemm_regpanel(GemmArgs p)
+// One item: the tile at (m0, n0) over K range [kb, ke), stored to C (at element offset
+// c_off, the split's slice) or, for a partial stream-K tile (TO_WS), to workspace slot
+// `slot`. Force-inlined into the kernels, so the plain kernel sees constant arguments and
+// the stream-K kernel holds no accumulators or staging registers across its segments.
+template <bool SK>
+__device__ __forceinline__ void regpanel_item(const GemmArgs &p, float *lds, int m0, int n0,
+                                              int kb, int ke, int64_t c_off, bool to_workspace,
+                                              int slot)
 {
     using namespace regpanel;
-    __shared__ __attribute__((aligned(16))) float lds[LDS_FLOATS];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lo = lane & 31, h = lane >> 5;
     const int wm = wave >> 1, wn = wave & 1;
-
-    // ---- the item: tile (m0, n0), K range [kb, ke)
-    const int ntiles = p.tiles_m * p.tiles_n;
-    const int item = blockIdx.x;
-    const int ls = item / ntiles;
-    int tm, tn;
-    tile_coords(item - ls * ntiles, p.tiles_m, p.tiles_n, tm, tn);
-    const int m0 = __builtin_amdgcn_readfirstlane(tm * BM);
-    const int n0 = __builtin_amdgcn_readfirstlane(tn * BN);
-    const int kb = __builtin_amdgcn_readfirstlane(ls * p.k_chunk);
-    const int ke = __builtin_amdgcn_readfirstlane(min(p.K, kb + p.k_chunk));
     const int M = p.M, N = p.N, lda = p.lda, ldb = p.ldb;
     // Resource sizes, in 32-bit scalar min/select chains (the panel loop must not need the
     // vector ALU, nor branch, for them). A panel's A resource starts at (m0, k0): when the
@@ -258,14 +256,29 @@ void k_sgemm_regpanel(GemmArgs p)
     panel(std::false_type{}, std::false_type{});
 
     // ---- epilogue: lane (lo, h) holds rows 8 (v / 4) + v % 4 + 4 h of row block r and
-    // columns 4 lo .. 4 lo + 3 of the wave tile (element c from column block c)
-    const int row0 = m0 + wm * WT, col0 = n0 + wn * WT;
-    const int ldc = p.ldc;
-    const int64_t ec = ls * p.c_split_stride + int64_t(row0) * ldc + col0;
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.C + ec, p.c_bytes - ec * 4);
-    const int rows_left = M - row0, cols_left = N - col0;
+    // columns 4 lo .. 4 lo + 3 of the wave tile (element c from column block c). A partial
+    // stream-K tile goes to its workspace slot as all BM x BN sums, packed rows of BN
+    // floats (the wave's 128 x 128 quarter of it). One store sequence serves both
+    // destinations (a second copy of it costs the stream-K form its registers), so partial
+    // tiles carry the same non-temporal hint as C.
     const int col = 4 * lo;
-    const uint32_t ldc4 = uint32_t(ldc) * 4u;
+    __amdgpu_buffer_rsrc_t rc;
+    uint32_t ldc4;
+    int rows_left, cols_left;
+    if (!to_workspace) {
+        const int row0 = m0 + wm * WT, col0 = n0 + wn * WT;
+        const int64_t ec = c_off + int64_t(row0) * p.ldc + col0;
+        rc = make_rsrc(p.C + ec, p.c_bytes - ec * 4);
+        ldc4 = uint32_t(p.ldc) * 4u;
+        rows_left = M - row0;
+        cols_left = N - col0;
+    } else {
+        const int64_t ew = int64_t(slot) * BM * BN + int64_t(wm * WT) * BN + wn * WT;
+        rc = make_rsrc(p.W + ew, (int64_t(BM) * BN - (int64_t(wm * WT) * BN + wn * WT)) * 4);
+        ldc4 = uint32_t(BN) * 4u;
+        rows_left = WT;
+        cols_left = WT;
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
 #pragma unroll
@@ -275,6 +288,7 @@ void k_sgemm_regpanel(GemmArgs p)
             const bool ok = lr < rows_left && col + 4 <= cols_left;
             store_vec<4, kStoreNonTemporal>(rc, ok ? uint32_t(lr) * ldc4 + 16u * lo : kOob, 0u,
                                             out);
+            store_data_guard<SK>();
         }
     }
     if (cols_left < WT) {
@@ -292,6 +306,63 @@ void k_sgemm_regpanel(GemmArgs p)
                                                            : kOob,
                         0u, acc[r][c][v]);
             }
+    }
+}
+
+template <bool SK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_sgemm_regpanel(GemmArgs p)
+{
+    using namespace regpanel;
+    __shared__ __attribute__((aligned(16))) float lds[LDS_FLOATS];
+    if constexpr (!SK) {
+        // one item per workgroup: tile item % tiles over split item / tiles
+        const int ntiles = p.tiles_m * p.tiles_n;
+        const int item = blockIdx.x;
+        const int ls = item / ntiles;
+        int tm, tn;
+        tile_coords(item - ls * ntiles, p.tiles_m, p.tiles_n, tm, tn);
+        const int m0 = __builtin_amdgcn_readfirstlane(tm * BM);
+        const int n0 = __builtin_amdgcn_readfirstlane(tn * BN);
+        const int kb = __builtin_amdgcn_readfirstlane(ls * p.k_chunk);
+        const int ke = __builtin_amdgcn_readfirstlane(min(p.K, kb + p.k_chunk));
+        regpanel_item<false>(p, lds, m0, n0, kb, ke, ls * p.c_split_stride, false, 0);
+    } else {
+        // workgroups below tiles_dp own one whole tile; the others walk a stream-K range,
+        // laid out contiguously per XCD so neighbouring segments share its L2. One call
+        // site for both (one inlined copy of the item).
+        const int bid = blockIdx.x;
+        const bool dp = bid < p.sk.tiles_dp;
+        const int g = dp ? 0
+                         : __builtin_amdgcn_readfirstlane(
+                               xcd_contiguous(bid - p.sk.tiles_dp, p.sk.G));
+        const int first = dp ? 0 : sk_start(p.sk, g);
+        const int end = dp ? 1 : sk_start(p.sk, g + 1);
+        const int P = p.sk.panels;
+        for (int i = first; i < end;) {
+            int t, kbp, kep;
+            if (dp) {
+                t = xcd_contiguous(bid, p.sk.tiles_dp);
+                kbp = 0;
+                kep = P;
+            } else {
+                const int u = i / P;
+                t = p.sk.tiles_dp + u;
+                kbp = i - u * P;
+                kep = min(P, kbp + (end - i));
+            }
+            int tm, tn;
+            grouped_tile(t, p.tiles_m, p.tiles_n, tm, tn);
+            // every wave is done with the previous segment's LDS before this one's prologue
+            // overwrites it
+            if (i != first) lds_barrier();
+            regpanel_item<true>(p, lds, __builtin_amdgcn_readfirstlane(tm * BM),
+                                __builtin_amdgcn_readfirstlane(tn * BN),
+                                __builtin_amdgcn_readfirstlane(kbp * BK),
+                                __builtin_amdgcn_readfirstlane(min(p.K, kep * BK)), 0,
+                                kbp != 0 || kep != P, 2 * g + (i == first ? 0 : 1));
+            i = dp ? end : i + (kep - kbp);
+        }
     }
 }
 

@@ -53,6 +53,7 @@ typedef void (*MfmaKernel)(GemmArgs);
 }  // namespace
 // k_sgemm_regpanel lives in sgemm_regpanel.hip (a translation unit built with other options)
 MfmaKernel regpanel_kernel();
+MfmaKernel regpanel_streamk_kernel();
 namespace {
 
 struct VariantEntry {
@@ -85,13 +86,14 @@ constexpr VariantEntry entry(const char *name, int wg_per_cu, double rate, doubl
 }
 
 // The one-wave-per-SIMD kernel (kernel_regpanel.hpp): 256 x 256 tiles of four 128 x 128
-// waves. It is planned for the plain product only: split-K and stream-K serve shapes with
-// few tiles, where the smaller tiles win.
+// waves, with a stream-K form. Split-K does not plan it: its shapes have few tiles, where
+// the smaller tiles win.
 VariantEntry regpanel_entry(const char *name, double rate, double overhead)
 {
     return VariantEntry{
         Variant{name, 256, 256, 32, 2, 2, 1, rate, overhead, 1.0, false, true, false},
-        regpanel_kernel(), nullptr, nullptr, 256, 32, 1, "regpanel"};
+        regpanel_kernel(), regpanel_streamk_kernel(), &k_streamk_fixup<256, 256>, 256, 32, 1,
+        "regpanel"};
 }
 
 // Rates (throughput at 8192^3 relative to 140 TFLOP/s), per-tile overheads (in units of K)
@@ -101,9 +103,9 @@ VariantEntry regpanel_entry(const char *name, double rate, double overhead)
 // straight into LDS ("_dl"), which measured as fast as or faster than staging through
 // registers on every one of those shapes.
 //  * 256 x 256, one wave per SIMD ("_rp", kernel_regpanel.hpp): long K and many tiles
-//    (8192^3, 4096^3, 8192^2 x 1024); plain product only.
-//  * 256 x 256 (8 waves of 64 x 128): dominated by "_rp" in the plain product; planned for
-//    its stream-K form, which shares the tiles of large ragged tile counts.
+//    (8192^3, 4096^3, 8192^2 x 1024), and as stream-K large ragged tile counts.
+//  * 256 x 256 (8 waves of 64 x 128): the same tile in the template kernel; "_rp" is faster
+//    on every measured shape, so it is no longer planned (forced use only).
 //  * 128 x 256 (4 waves, 48 KiB of LDS): two workgroups per CU, so one stores while the
 //    other computes; best when K is short and C's stores weigh as much as the MFMAs.
 //  * 128 x 128 (4 waves, two per CU): shapes with about one 256 x 256 tile per CU or fewer.
@@ -114,7 +116,7 @@ VariantEntry regpanel_entry(const char *name, double rate, double overhead)
 // The last entry stages through registers; it is never planned and stays as the measured
 // comparison for the direct loads (forced through sgemm_f32_variant).
 const VariantEntry kVariants[] = {
-    entry<256, 256, 32, 4, 2, 1, 1, true, true>("mfma_256x256x32_w4x2_dl", 1, 1.060, 40, 1.0),
+    entry<256, 256, 32, 4, 2, 1, 1, true, false>("mfma_256x256x32_w4x2_dl", 1, 1.060, 40, 1.0),
     entry<128, 256, 16, 2, 2, 1, 1, true, true>("mfma_128x256x16_w2x2_dl", 2, 1.020, 24, 0.94),
     entry<128, 128, 32, 2, 2, 1, 1, true, true>("mfma_128x128x32_w2x2_dl", 2, 1.020, 32, 0.90),
     entry<64, 64, 32, 2, 1, 2, 4, true, false>("mfma_64x64x32_w2x1_acc2_kg4_dl", 1, 0.880, 212, 1.0),

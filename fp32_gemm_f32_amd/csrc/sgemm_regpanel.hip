@@ -7,7 +7,8 @@
 
 namespace sgemm {
 
-// The kernel's launch handle, for the variant table in sgemm_f32.hip.
-void (*regpanel_kernel())(GemmArgs) { return &k_sgemm_regpanel; }
+// Launch handles of the plain and the stream-K form, for the variant table in sgemm_f32.hip.
+void (*regpanel_kernel())(GemmArgs) { return &k_sgemm_regpanel<false>; }
+void (*regpanel_streamk_kernel())(GemmArgs) { return &k_sgemm_regpanel<true>; }
 
 }  // namespace sgemm

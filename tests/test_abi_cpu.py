@@ -175,7 +175,8 @@ def test_streamk_validation():
     assert lib.sgemm_f32_streamk(*args, -1, None, 1 << 20, None) == -3
     assert lib.sgemm_f32_streamk(*args, -1, ws + 4, 1 << 20, None) == -3    # not 16-byte aligned
     assert lib.sgemm_f32_streamk(*args, -1, P + 64, 1 << 20, None) == -4    # overlaps A
-    assert lib.sgemm_f32_streamk(*args, 0, P + (1 << 27) - 64, 1 << 20, None) == -4  # overlaps C
+    sk0 = g.streamk_variants()[0]
+    assert lib.sgemm_f32_streamk(*args, sk0, P + (1 << 27) - 64, 1 << 20, None) == -4  # overlaps C
     assert lib.sgemm_f32_streamk(-1, 48, 64, P, 64, P + 4096, 48, P + 8192, 48, -1, ws, 64,
                                  None) == -1
     assert lib.sgemm_f32_streamk(64, 48, 64, P, 63, P + 4096, 48, P + 8192, 48, -1, ws, 64,
@@ -238,14 +239,15 @@ def test_streamk_plan_choices():
         assert not d["streamk"], d
         assert d["name"] == g.sgemm_f32_plan_describe(*shape, num_cus=256)["name"]
     # forced stream-K with a variant whose tiles divide evenly is the plain grid
-    d = g.sgemm_f32_streamk_describe(8192, 8192, 8192, 0, 256)
+    rp = g.variant_names().index("mfma_256x256x32_w2x2_rp")
+    d = g.sgemm_f32_streamk_describe(8192, 8192, 8192, rp, 256)
     assert not d["streamk"] and d["tiles"] == 1024
 
 
 def test_variant_info():
     names = g.variant_names()
     planned = g.planned_variants()
-    assert 0 in planned and len(planned) >= 5
+    assert names.index("mfma_256x256x32_w2x2_rp") in planned and len(planned) >= 5
     for i, name in enumerate(names):
         info = g.sgemm_f32_variant_info(i)
         assert info["name"] == name and info["variant"] == i
@@ -254,9 +256,7 @@ def test_variant_info():
         w0, w1 = info["waves"]
         assert info["threads"] == 64 * w0 * w1 * info["k_groups"]
         assert info["kernel"] in ("mfma", "regpanel")
-        # planned variants of the template kernel have a stream-K form; the regpanel kernel
-        # has none
-        assert info["streamk"] == (info["planned"] and info["kernel"] == "mfma")
+        assert info["streamk"] == info["planned"]          # planned variants have a stream-K form
         assert info["direct_loads"] == name.endswith("_dl")
         assert f"{info['BM']}x{info['BN']}x{info['BK']}" in name
     with pytest.raises(g.SgemmError):

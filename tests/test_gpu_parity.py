@@ -112,6 +112,29 @@ def test_planned_variants_at_scale(gpu, M, N, K):
     assert rep["n_nonfinite"] == 0 and rep["n_inexact"] == 0, (plan["name"], rep)
 
 
+# The one-wave-per-SIMD variant forced onto ragged large shapes with NaN-padded leading
+# dimensions: a partial last K-panel (K % 32 != 0, and K % 4 != 0), tiles that hold A's last
+# rows and B's last columns, and a shape with fewer than one panel. The automatic plan only
+# sends it shapes of many whole tiles, so these cases are forced.
+RP_FORCED = [(4095, 4097, 4103), (2300, 1800, 3001), (3000, 2600, 20)]
+
+
+@pytest.mark.parametrize("M,N,K", RP_FORCED)
+def test_regpanel_variant_forced_ragged(gpu, M, N, K):
+    v = g.variant_names().index("mfma_256x256x32_w2x2_rp")
+    rng = np.random.default_rng(M + 5 * N + 11 * K)
+    A = wl.draw(rng, (M, K), "int")
+    B = wl.draw(rng, (K, N), "int")
+    _, dA, lda = device_matrix(A, K + 3)
+    _, dB, ldb = device_matrix(B, N + 5)
+    c = GuardedC(M, N, N + 2)
+    print(f"[parity] {M}x{N}x{K} int forced v{v} lda={lda} ldb={ldb}", flush=True)
+    run_kernel(f"v{v}", M, N, K, dA, lda, dB, ldb, c)
+    gpu.cuda.synchronize()
+    rep = oracle.check(A, B, c.result(), rows=sample_rows(M, 16, seed=N))
+    assert rep["n_nonfinite"] == 0 and rep["n_inexact"] == 0, rep
+
+
 # large shapes whose tile counts fall just past a whole round of 256 x 256 tiles
 STREAMK_PLAN_SHAPES = [(4500, 4500, 8192), (5000, 5000, 2048)]
 
