@@ -78,10 +78,25 @@ def build(asm: bool = False, verbose: bool = False) -> str:
     if r.returncode != 0:
         sys.stderr.write(r.stderr[-8000:])
         raise RuntimeError(f"hipcc link failed ({r.returncode})")
+    check_symbols(OUT + ".tmp")
     os.replace(OUT + ".tmp", OUT)
     if asm:
         assemble()
     return OUT
+
+
+def check_symbols(lib: str) -> None:
+    """Fail on any undefined symbol of the library's own namespace. The compiler can drop a
+    kernel template's host stub without a diagnostic (and exit 0); the library then fails
+    to load only where it is used, so the build refuses it here."""
+    nm = shutil.which("nm") or "/opt/rocm/llvm/bin/llvm-nm"
+    r = subprocess.run([nm, "-D", "--undefined-only", lib], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"nm failed on {lib}: {r.stderr[-2000:]}")
+    missing = [l.split()[-1] for l in r.stdout.splitlines() if "_ZN5sgemm" in l]
+    if missing:
+        raise RuntimeError("library has undefined kernel symbols (host stubs not emitted): " +
+                           ", ".join(missing[:8]))
 
 
 def assemble(out: str | None = None) -> str:

@@ -126,6 +126,18 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const float *base, int64_t by
                                              kBufferWord3);
 }
 
+// Size of a buffer resource that reaches every offset a kernel's loads can use: the host
+// keeps all of them below 2^31 - 64 (offsets_fit in plan.hpp).
+constexpr uint32_t kFullRange = kOob - 64u;
+
+// A buffer resource of `bytes` bytes from base, the size already clamped by the caller in
+// 32-bit scalar arithmetic (no 64-bit compares on the vector ALU inside a panel loop).
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc32(const float *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0,
+                                             int32_t(bytes), kBufferWord3);
+}
+
 __device__ inline f32x4 load_b128(__amdgpu_buffer_rsrc_t r, uint32_t voff)
 {
     return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
@@ -422,8 +434,30 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
             sk_end = sk_start(p.sk, sk_g + 1);
         }
     }
-    // B columns of this thread's chunks inside the tile (per segment under stream-K)
-    bool b_col_ok = ln0 + b_c0 < N;
+    // ---- per-item load offsets and resource bounds (per segment under stream-K). The panel
+    // loop then needs no vector-ALU work for its loads, which measurably costs matrix-pipe
+    // time on gfx950:
+    //  * a chunk whose row lies past M, or whose columns start past N, gets kOob here, once;
+    //  * the K range needs no per-load test: a panel wholly past it gets empty resources,
+    //    B rows past it lie past the end of the panel's B resource (sized to end at the
+    //    item's last K row), and A values past it, which the loads do fetch (from the row's
+    //    padding or the next split), are zeroed before use (write_slot, fix_k_tail);
+    //  * resource sizes come from 32-bit scalar min/select chains (the host bounds every
+    //    product below 2^31): A's only ends before the full range when the tile holds A's
+    //    last row (a_end is all ones otherwise), B's when the item's last K row is in the
+    //    panel (BK + 1 rows cover every offset of a panel otherwise).
+    uint32_t a_voff[A_CH], b_voff[B_CH];
+    uint32_t a_end = 0u;
+    auto set_item = [&]() {
+#pragma unroll
+        for (int l = 0; l < A_CH; ++l)
+            a_voff[l] = lm0 + a_r0 + l * A_RSTEP < M ? a_off0 + uint32_t(l) * a_stride : kOob;
+        // columns past N inside a chunk only reach accumulators that are never stored
+        const bool b_col_ok = ln0 + b_c0 < N;
+#pragma unroll
+        for (int i = 0; i < B_CH; ++i) b_voff[i] = b_col_ok ? b_off0 + uint32_t(i) * b_stride : kOob;
+        a_end = M - lm0 <= BM ? uint32_t((M - 1 - lm0) * lda + (K - lkb)) * 4u : 0xffffffffu;
+    };
 
     // ---- global -> register staging of one panel ----
     f32x4 ra[A_CH], rb[B_CH];
@@ -433,31 +467,37 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     auto set_panel = [&](int k0) {
         k_load = k0;
         const int64_t ea = int64_t(lm0) * lda + lkb + k0, eb = int64_t(lkb + k0) * ldb + ln0;
-        rsa = make_rsrc(p.A + ea, p.a_bytes - ea * 4);
-        rsb = make_rsrc(p.B + eb, p.b_bytes - eb * 4);
+        const int rows = lK - k0;
+        const uint32_t na = min(a_end - 4u * uint32_t(k0), kFullRange);
+        const uint32_t nb =
+            min(uint32_t((min(rows, BK + 1) - 1) * ldb + (N - ln0)) * 4u, kFullRange);
+        rsa = make_rsrc32(p.A + ea, rows > 0 ? na : 0u);
+        rsb = make_rsrc32(p.B + eb, rows > 0 ? nb : 0u);
     };
     // staging slot l < A_CH is A chunk l, otherwise B chunk l - A_CH
+    // (offsets are read through locals: a subscript of the offset arrays written straight
+    // into the load, in the branch that a constant l rules out, makes the compiler drop the
+    // kernel's host stub without a diagnostic; the build checks the library for undefined
+    // symbols)
     auto load_slot = [&](int l) {
         if (l < A_CH) {
-            const int kc = k_load + 4 * a_q;
-            const bool ok = lm0 + a_r0 + l * A_RSTEP < M && kc < lK;
-            ra[l] = load_b128(rsa, ok ? a_off0 + uint32_t(l) * a_stride : kOob);
+            const uint32_t off = a_voff[l];
+            ra[l] = load_b128(rsa, off);
         } else {
             const int i = l - A_CH;
-            const bool ok = k_load + b_k0 + i * B_KSTEP < lK && b_col_ok;
-            // columns past N inside a chunk only reach accumulators that are never stored
-            rb[i] = load_b128(rsb, ok ? b_off0 + uint32_t(i) * b_stride : kOob);
+            const uint32_t off = b_voff[i];
+            rb[i] = load_b128(rsb, off);
         }
     };
     auto write_slot = [&](float *As, int l) {
         if (l < A_CH) {
-            // a chunk that crosses K: its elements past K belong to the row padding or the
-            // next row; zero them (a select, so a NaN there cannot leak). Done here, where
-            // the data is needed anyway, so the select does not wait on the load early.
+            // elements past the K range belong to the row padding, the next row or the next
+            // split; zero them (a select, so a NaN there cannot leak). Done here, where the
+            // data is needed anyway, so the select does not wait on the load early.
             const int kc = k_load + 4 * a_q;
             f32x4 v = ra[l];
 #pragma unroll
-            for (int e = 1; e < 4; ++e) v[e] = kc + e < lK ? v[e] : 0.0f;
+            for (int e = 0; e < 4; ++e) v[e] = kc + e < lK ? v[e] : 0.0f;
             *reinterpret_cast<f32x4 *>(As + a_lds0 + l * A_RSTEP * BK) = v;
         } else
             *reinterpret_cast<f32x4 *>(As + T::A_TILE + b_lds0 + (l - A_CH) * B_KSTEP * BN) =
@@ -471,16 +511,17 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     // after the direct loads of a panel have landed: zero the elements past the K range in
     // this lane's A chunks (their LDS slots are 16 (tid + l NT) bytes into the A tile). The
-    // branch is uniform and taken only in the panel that holds the end of the range.
+    // branch is uniform and taken only in the panel that holds the end of the range (or,
+    // with K-groups, lies past it).
     auto fix_k_tail = [&](float *As) {
-        if (k_load + BK > lK && (lK & 3) != 0) {
+        if (k_load + BK > lK) {
             const int kc = k_load + 4 * a_q;
-            if (kc < lK && kc + 4 > lK) {
+            if (kc + 4 > lK) {
 #pragma unroll
                 for (int l = 0; l < A_CH; ++l) {
                     float *chunk = As + (tid + l * NT) * 4;
 #pragma unroll
-                    for (int e = 1; e < 4; ++e)
+                    for (int e = 0; e < 4; ++e)
                         if (kc + e >= lK) chunk[e] = 0.0f;
                 }
             }
@@ -488,17 +529,14 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     };
     auto load_direct = [&](float *As, int l) {
         if (l < A_CH) {
-            const int kc = k_load + 4 * a_q;
-            const bool ok = lm0 + a_r0 + l * A_RSTEP < M && kc < lK;
+            const uint32_t off = a_voff[l];
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsa, (lds_ptr)(As + (wave_u * 64 + l * NT) * 4), 16,
-                ok ? a_off0 + uint32_t(l) * a_stride : kOob, 0, 0, 0);
+                rsa, (lds_ptr)(As + (wave_u * 64 + l * NT) * 4), 16, off, 0, 0, 0);
         } else {
             const int i = l - A_CH;
-            const bool ok = k_load + b_k0 + i * B_KSTEP < lK && b_col_ok;
+            const uint32_t off = b_voff[i];
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsb, (lds_ptr)(As + T::A_TILE + (wave_u * 64 + i * NT) * 4), 16,
-                ok ? b_off0 + uint32_t(i) * b_stride : kOob, 0, 0, 0);
+                rsb, (lds_ptr)(As + T::A_TILE + (wave_u * 64 + i * NT) * 4), 16, off, 0, 0, 0);
         }
     };
 
@@ -768,7 +806,6 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
                 lkb = __builtin_amdgcn_readfirstlane(kb * BK);
                 lK = __builtin_amdgcn_readfirstlane(min(K, ke * BK) - kb * BK);
                 sk_i += ke - kb;
-                b_col_ok = ln0 + b_c0 < N;
 #pragma unroll
                 for (int h = 0; h < KACC; ++h)
 #pragma unroll
@@ -783,6 +820,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
 
         // ---- the item: the K loop of group kg (panels kg, kg + KG, ...), the K-group sums
         // and the epilogue, into C or (a partial stream-K tile) into workspace slot `slot`
+        set_item();
         set_panel(kg * BK);
         if constexpr (DL) {
 #pragma unroll

@@ -58,15 +58,6 @@ constexpr int STEPS = 16;                       // k-steps of 2 per panel
 constexpr int LOAD_STEPS = 8;                   // steps 4 .. 11 carry the global loads
 static_assert(LDS_FLOATS * 4 <= 160 * 1024, "LDS");
 
-// Size of a buffer resource that reaches every offset a load can use (all offsets stay
-// below 2^31 - 64: the host checks BM * lda and BK * ldb against it).
-constexpr uint32_t kFullRange = kOob - 64u;
-
-__device__ inline __amdgpu_buffer_rsrc_t rsrc(const float *base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0,
-                                             int32_t(bytes), kBufferWord3);
-}
 
 // Release/acquire of LDS only around the barrier: the wave waits for its own LDS accesses,
 // not for the global loads it has in flight.
@@ -134,8 +125,8 @@ __device__ __forceinline__ void regpanel_item(const GemmArgs &p, float *lds, int
                 min(uint32_t((min(rows, BK + 1) - 1) * ldb + (N - n0)) * 4u, kFullRange);
             // a panel past the K range reads zeros (selects, not a branch: the panel loop
             // stays one block)
-            ra = rsrc(p.A + ea, rows > 0 ? na : 0u);
-            rb = rsrc(p.B + eb, rows > 0 ? nb : 0u);
+            ra = make_rsrc32(p.A + ea, rows > 0 ? na : 0u);
+            rb = make_rsrc32(p.B + eb, rows > 0 ? nb : 0u);
         }
 #pragma unroll
         for (int j = lo_j; j < hi_j; ++j) {
