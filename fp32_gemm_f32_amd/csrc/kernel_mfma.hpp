@@ -601,17 +601,24 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     // barrier instead.
     constexpr int STEPS = BK / S::KSTEP;
     constexpr int NL = A_CH + B_CH;                     // staging slots per panel
+    // PAIR unrolls the panel loop by two (constant LDS stages). It costs 30-80 registers; it
+    // measured 1-4 % faster for direct-load tiles of BK >= 32 up to 128 x 128 with one or
+    // two K-groups, and slower for the short-K 128 x 256 x 16 tile (whose epilogue
+    // dominates), the 256 x 256 ones (which then spill) and four K-groups (few panels each).
+    constexpr bool PAIR = DL && BK >= 32 && BM * BN <= 128 * 128 && KG <= 2;
+    int panel_parity = 0;   // the stage of the current panel is panel_parity & 1 (no PAIR)
     constexpr int LS = SGEMM_LOAD_STEPS;
     constexpr int WS = SGEMM_WRITE_STEPS;
     constexpr int PER_LOAD = (NL + LS - 1) / LS;
     constexpr int PER_WRITE = (NL + WS - 1) / WS;
     static_assert(LS + WS < STEPS, "loads and LDS writes of a panel need separate steps");
 
-    auto panel = [&](int cur, auto next_tag) {
+    auto panel = [&](auto cur_tag, auto next_tag) {
         constexpr bool NEXT = decltype(next_tag)::value;
-        const float *As = smem + cur * SSTRIDE;
+        constexpr int cur = decltype(cur_tag)::value;   // -1: the stage parity known at run time
+        const float *As = smem + (cur < 0 ? (panel_parity & 1) : cur) * SSTRIDE;
         const float *Bs = As + T::A_TILE;
-        float *Anext = smem + (cur ^ 1) * SSTRIDE;
+        float *Anext = smem + ((cur < 0 ? (panel_parity & 1) : cur) ^ 1) * SSTRIDE;
         static_for<0, STEPS>([&](auto tc) {
             constexpr int t = decltype(tc)::value;
             constexpr int kb = t >> 2, s = t & 3;
@@ -840,11 +847,36 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
         // the last round stages nothing; a group whose last panel lies past the K range loads
         // only zeros for it
         const int rounds = ((lK + BK - 1) / BK + KG - 1) / KG;
-        for (int r = 0; r + 1 < rounds; ++r) {
-            set_panel(((r + 1) * KG + kg) * BK);
-            panel(r & 1, std::true_type{});
+        if constexpr (PAIR) {
+            // two panels per iteration, so each one's LDS stage is a constant and its operand
+            // reads carry the stage in their immediate offsets (no address arithmetic on the
+            // vector ALU between the MFMAs)
+            using S0 = std::integral_constant<int, 0>;
+            using S1 = std::integral_constant<int, 1>;
+            int r = 0;
+            for (; r + 2 < rounds; r += 2) {
+                set_panel(((r + 1) * KG + kg) * BK);
+                panel(S0{}, std::true_type{});
+                set_panel(((r + 2) * KG + kg) * BK);
+                panel(S1{}, std::true_type{});
+            }
+            if (r + 1 < rounds) {
+                set_panel(((r + 1) * KG + kg) * BK);
+                panel(S0{}, std::true_type{});
+                panel(S1{}, std::false_type{});
+            } else {
+                panel(S0{}, std::false_type{});
+            }
+        } else {
+            using SR = std::integral_constant<int, -1>;
+            for (int r = 0; r + 1 < rounds; ++r) {
+                set_panel(((r + 1) * KG + kg) * BK);
+                panel_parity = r;
+                panel(SR{}, std::true_type{});
+            }
+            panel_parity = rounds - 1;
+            panel(SR{}, std::false_type{});
         }
-        panel((rounds - 1) & 1, std::false_type{});
         finish();
         if (kg == 0) {
             if (!to_workspace) {

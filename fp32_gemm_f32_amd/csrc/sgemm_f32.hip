@@ -117,15 +117,15 @@ VariantEntry regpanel_entry(const char *name, double rate, double overhead)
 // comparison for the direct loads (forced through sgemm_f32_variant).
 const VariantEntry kVariants[] = {
     entry<256, 256, 32, 4, 2, 1, 1, true, false>("mfma_256x256x32_w4x2_dl", 1, 1.085, 40, 1.0),
-    entry<128, 256, 16, 2, 2, 1, 1, true, true>("mfma_128x256x16_w2x2_dl", 2, 1.065, 4, 0.92),
-    entry<128, 128, 32, 2, 2, 1, 1, true, true>("mfma_128x128x32_w2x2_dl", 2, 1.075, 32, 0.92),
+    entry<128, 256, 16, 2, 2, 1, 1, true, true>("mfma_128x256x16_w2x2_dl", 2, 1.045, 0, 0.88),
+    entry<128, 128, 32, 2, 2, 1, 1, true, true>("mfma_128x128x32_w2x2_dl", 2, 1.070, 12, 0.90),
     entry<64, 64, 32, 2, 1, 2, 4, true, false>("mfma_64x64x32_w2x1_acc2_kg4_dl", 1, 0.880, 212, 1.0),
-    entry<64, 64, 32, 2, 1, 1, 2, true, true>("mfma_64x64x32_w2x1_kg2_dl", 2, 0.965, 64, 0.82),
+    entry<64, 64, 32, 2, 1, 1, 2, true, true>("mfma_64x64x32_w2x1_kg2_dl", 2, 1.015, 92, 0.78),
     entry<256, 256, 32, 4, 2, 1, 1, false, false>("mfma_256x256x32_w4x2", 1, 1.045, 52, 1.0),
     entry<80, 64, 32, 1, 2, 1, 4, true, true, 16>("mfma16_80x64x32_w1x2_kg4_dl", 1, 0.985, 236, 1.0),
-    entry<80, 64, 32, 1, 2, 1, 2, true, true, 16>("mfma16_80x64x32_w1x2_kg2_dl", 2, 1.010, 64, 0.84),
+    entry<80, 64, 32, 1, 2, 1, 2, true, true, 16>("mfma16_80x64x32_w1x2_kg2_dl", 2, 1.025, 64, 0.84),
     entry<48, 64, 32, 1, 2, 1, 4, true, true, 16>("mfma16_48x64x32_w1x2_kg4_dl", 1, 0.975, 256, 1.0),
-    entry<64, 64, 64, 2, 2, 1, 2, true, true, 16>("mfma16_64x64x64_w2x2_kg2_dl", 1, 0.985, 192, 1.0),
+    entry<64, 64, 64, 2, 2, 1, 2, true, true, 16>("mfma16_64x64x64_w2x2_kg2_dl", 1, 1.020, 196, 1.0),
     regpanel_entry("mfma_256x256x32_w2x2_rp", 1.105, 44),
 };
 constexpr int kNumVariants = int(sizeof(kVariants) / sizeof(kVariants[0]));
