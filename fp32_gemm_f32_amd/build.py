@@ -24,7 +24,8 @@ BUILD_DIR = os.path.join(PKG, "_build")
 # The one-wave-per-SIMD kernel keeps 256 accumulators per lane in AGPRs, so it is compiled
 # on its own, without that option.
 SOURCES = [(os.path.join(CSRC, "sgemm_f32.hip"), True),
-           (os.path.join(CSRC, "sgemm_regpanel.hip"), False)]
+           (os.path.join(CSRC, "sgemm_regpanel.hip"), False),
+           (os.path.join(CSRC, "sgemm_persist.hip"), False)]
 ARCH = "gfx950"
 
 

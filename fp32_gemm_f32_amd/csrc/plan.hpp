@@ -31,6 +31,10 @@ struct Variant {
     bool direct;            // direct global -> LDS loads
     bool planned;           // candidate for the automatic choice (else forced use only)
     bool splitk = true;     // candidate for split-K items too
+    // planned only for products of whole BM x BN tiles and more than one K-panel (the
+    // persistent kernel; forced on other shapes it computes their whole-tile part and
+    // leaves the rest to the plan)
+    bool whole_tiles = false;
 };
 
 struct Operands {
@@ -48,7 +52,13 @@ inline bool offsets_fit(const Variant &v, const Operands &o)
            int64_t(v.BM) * o.ldc * 4 + int64_t(v.BN) * 4 + 64 < lim;
 }
 
-inline bool variant_allowed(const Variant &v, const Operands &o) { return offsets_fit(v, o); }
+inline bool variant_allowed(const Variant &v, const Operands &o)
+{
+    if (v.whole_tiles &&
+        (o.M % v.BM != 0 || o.N % v.BN != 0 || o.K <= v.BK || o.splits != 1))
+        return false;
+    return offsets_fit(v, o);
+}
 
 inline double variant_cost(const Variant &v, const Operands &o, int cus)
 {

@@ -54,6 +54,9 @@ typedef void (*MfmaKernel)(GemmArgs);
 // k_sgemm_regpanel lives in sgemm_regpanel.hip (a translation unit built with other options)
 MfmaKernel regpanel_kernel();
 MfmaKernel regpanel_streamk_kernel();
+// k_sgemm_persist lives in sgemm_persist.hip (same reason)
+MfmaKernel persist_kernel();
+MfmaKernel persist_ktail_kernel();
 namespace {
 
 struct VariantEntry {
@@ -64,7 +67,9 @@ struct VariantEntry {
     int threads;
     int mb;                 // MFMA block size (32: 32x32x2, 16: 16x16x4)
     int kg;                 // K-groups
-    const char *kernel;     // kernel family: "mfma" (kernel_mfma.hpp) or "regpanel"
+    const char *kernel;     // kernel family: "mfma" (kernel_mfma.hpp), "regpanel", "persist"
+    bool persistent = false;       // one workgroup per CU walks the tiles (kernel_persist.hpp)
+    MfmaKernel kern_ktail = nullptr;   // its form for a K that is not a multiple of BK
 };
 
 // PLANNED variants also get a stream-K form and its fixup kernel; the others are never
@@ -94,6 +99,19 @@ VariantEntry regpanel_entry(const char *name, double rate, double overhead)
         Variant{name, 256, 256, 32, 2, 2, 1, rate, overhead, 1.0, false, true, false},
         regpanel_kernel(), regpanel_streamk_kernel(), &k_streamk_fixup<256, 256>, 256, 32, 1,
         "regpanel"};
+}
+
+// The persistent kernel (kernel_persist.hpp): 128 x 256 tiles of four 64 x 128 waves, one
+// workgroup per CU, each tile's C stored among the next tile's MFMAs. Whole tiles only, at
+// least two K-panels; no split-K or stream-K form.
+VariantEntry persist_entry(const char *name, double rate, double overhead)
+{
+    VariantEntry e{Variant{name, 128, 256, 32, 2, 2, 1, rate, overhead, 1.0, false, false, false},
+                   persist_kernel(), nullptr, nullptr, 256, 32, 1, "persist"};
+    e.v.whole_tiles = true;
+    e.persistent = true;
+    e.kern_ktail = persist_ktail_kernel();
+    return e;
 }
 
 // Rates (throughput at 8192^3 relative to 140 TFLOP/s), per-tile overheads (in units of K)
@@ -127,6 +145,7 @@ const VariantEntry kVariants[] = {
     entry<48, 64, 32, 1, 2, 1, 4, true, true, 16>("mfma16_48x64x32_w1x2_kg4_dl", 1, 0.975, 256, 1.0),
     entry<64, 64, 64, 2, 2, 1, 2, true, true, 16>("mfma16_64x64x64_w2x2_kg2_dl", 1, 1.020, 196, 1.0),
     regpanel_entry("mfma_256x256x32_w2x2_rp", 1.105, 44),
+    persist_entry("mfma_128x256x32_w2x2_ps", 1.05, 0),
 };
 constexpr int kNumVariants = int(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -224,11 +243,61 @@ int choose_streamk(const Operands &o, int cus, bool *sk)
     return best;
 }
 
-// One workgroup per tile.
+int run_variant(int vi, const Operands &o, const float *A, const float *B, float *C,
+                void *stream);
+
+// The plan's choice for o (which never picks a whole-tile variant for a shape it does not
+// fit).
+int run_auto(const Operands &o, const float *A, const float *B, float *C, void *stream)
+{
+    int cus = 0;
+    const int qs = device_cus(&cus);
+    if (qs != SGEMM_OK) return qs;
+    const int vi = choose_variant(g_table, o, cus);
+    return vi < 0 ? SGEMM_ETOO_LARGE : run_variant(vi, o, A, B, C, stream);
+}
+
+// The persistent variant: its kernel on the whole-tile part of C (G = min(tiles, CUs)
+// workgroups), the right and bottom strips, if any, through the plan. A product without a
+// whole tile or with a single K-panel goes to the plan entirely.
+int run_persistent(const VariantEntry &e, const Operands &o, const float *A, const float *B,
+                   float *C, void *stream)
+{
+    const int Mi = o.M / e.v.BM * e.v.BM, Ni = o.N / e.v.BN * e.v.BN;
+    if (Mi == 0 || Ni == 0 || o.K <= e.v.BK) return run_auto(o, A, B, C, stream);
+    Operands oi = o;
+    oi.M = Mi;
+    oi.N = Ni;
+    const GemmArgs p = plain_args(e, oi, A, B, C);
+    int cus = 0;
+    int st = device_cus(&cus);
+    if (st != SGEMM_OK) return st;
+    const int64_t tiles = int64_t(p.tiles_m) * p.tiles_n;
+    const int64_t grid = std::min<int64_t>(tiles, cus);
+    st = launch(o.K % e.v.BK ? e.kern_ktail : e.kern, dim3(unsigned(grid)), dim3(e.threads),
+                stream, p);
+    if (st != SGEMM_OK) return st;
+    if (Ni < o.N) {
+        Operands r = o;
+        r.N = o.N - Ni;
+        st = run_auto(r, A, B + Ni, C + Ni, stream);
+        if (st != SGEMM_OK) return st;
+    }
+    if (Mi < o.M) {
+        Operands b = o;
+        b.M = o.M - Mi;
+        b.N = Ni;
+        st = run_auto(b, A + int64_t(Mi) * o.lda, B, C + int64_t(Mi) * o.ldc, stream);
+    }
+    return st;
+}
+
+// One workgroup per tile (or the persistent variant's walk).
 int run_variant(int vi, const Operands &o, const float *A, const float *B, float *C,
                 void *stream)
 {
     const VariantEntry &e = kVariants[vi];
+    if (e.persistent) return run_persistent(e, o, A, B, C, stream);
     const GemmArgs p = plain_args(e, o, A, B, C);
     const int64_t tiles = int64_t(p.tiles_m) * p.tiles_n;
     if (tiles > INT32_MAX) return SGEMM_ETOO_LARGE;
@@ -626,11 +695,13 @@ extern "C" int sgemm_f32_variant_info(int variant, char *buf, int buflen)
                            "\"threads\": %d, \"mfma\": \"%dx%dx%d\", \"wg_per_cu\": %d, "
                            "\"direct_loads\": %s, \"planned\": %s, \"streamk\": %s, "
                            "\"rate\": %.3f, \"overhead\": %.1f, \"solo\": %.2f, "
-                           "\"kernel\": \"%s\", \"splitk\": %s}",
+                           "\"kernel\": \"%s\", \"splitk\": %s, \"persistent\": %s, "
+                           "\"whole_tiles\": %s}",
                            variant, v.name, v.BM, v.BN, v.BK, v.wgm, v.wgn, e.kg, e.threads, e.mb,
                            e.mb, e.mb == 32 ? 2 : 4, v.wg_per_cu, v.direct ? "true" : "false",
                            v.planned ? "true" : "false", e.kern_sk ? "true" : "false", v.rate,
-                           v.overhead, v.solo, e.kernel, v.splitk ? "true" : "false");
+                           v.overhead, v.solo, e.kernel, v.splitk ? "true" : "false",
+                           e.persistent ? "true" : "false", v.whole_tiles ? "true" : "false");
     if (n < 0 || n >= buflen) return SGEMM_EINVAL_ARG;
     return SGEMM_OK;
 }
@@ -667,7 +738,8 @@ extern "C" int sgemm_f32_plan_describe(int M, int N, int K, const float *A, int 
     if (vi < 0) return SGEMM_ETOO_LARGE;
     const Variant &v = kVariants[vi].v;
     const int64_t tm = (int64_t(M) + v.BM - 1) / v.BM, tn = (int64_t(N) + v.BN - 1) / v.BN;
-    const int64_t grid = tm * tn;
+    // one workgroup per tile, or for the persistent variant one per CU over its tiles
+    const int64_t grid = kVariants[vi].persistent ? std::min<int64_t>(tm * tn, cus) : tm * tn;
     // operand bytes the tiles request: every A row panel once per tile column and every
     // B column panel once per tile row (before any cache reuse)
     const int64_t tile_bytes = 4 * (int64_t(M) * K * tn + int64_t(K) * N * tm);

@@ -201,9 +201,13 @@ int sgemm_f32_lds_transpose(int rows, int cols,
  * the same product for every shape; they differ in tile shape, waves and how panels reach
  * LDS (names ending in "_dl" load straight from global memory into LDS, the others stage
  * through registers; "_rp" is the one-wave-per-SIMD kernel that holds a whole K-panel's
- * operands in registers), and some are never chosen automatically (kept for comparison). A
- * variant whose 31-bit buffer offsets cannot span one workgroup's rows of A or C or one
- * K-panel of B returns SGEMM_ETOO_LARGE.
+ * operands in registers; "_ps" is the persistent kernel, one workgroup per CU walking
+ * 128 x 256 tiles and writing each tile among the next one's MFMAs), and some are never
+ * chosen automatically (kept for comparison). "_ps" computes only whole tiles of a product
+ * with more than 32 values of K: the rest of C (the strips past the last whole tile row and
+ * column), or the whole product when it has no whole tile or K <= 32, is computed by the
+ * automatic choice, on the same stream. A variant whose 31-bit buffer offsets cannot span
+ * one workgroup's rows of A or C or one K-panel of B returns SGEMM_ETOO_LARGE.
  */
 int sgemm_f32_variant(int variant, int M, int N, int K,
                       const float *A, int lda,
@@ -221,8 +225,10 @@ const char *sgemm_f32_variant_name(int variant);
  * threads, the MFMA instruction shape ("32x32x2" or "16x16x4"), resident workgroups per
  * CU, direct loads, whether the automatic plan may pick it, whether it has a stream-K
  * form, the plan's cost-model parameters (rate, overhead, solo) for it, the kernel family
- * ("mfma": the LDS-double-buffered template; "regpanel": the one-wave-per-SIMD kernel) and
- * whether split-K may use it. Host-only, no GPU needed. Returns SGEMM_OK, or
+ * ("mfma": the LDS-double-buffered template; "regpanel": the one-wave-per-SIMD kernel;
+ * "persist": the persistent kernel), whether split-K may use it, whether it runs one
+ * workgroup per CU over the tiles ("persistent") and whether it only takes whole tiles
+ * ("whole_tiles"). Host-only, no GPU needed. Returns SGEMM_OK, or
  * SGEMM_EINVAL_ARG for a bad index or a buffer too small.
  */
 int sgemm_f32_variant_info(int variant, char *buf, int buflen);

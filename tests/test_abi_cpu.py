@@ -255,8 +255,15 @@ def test_variant_info():
         assert name.startswith("mfma16_") == (info["mfma"] == "16x16x4")
         w0, w1 = info["waves"]
         assert info["threads"] == 64 * w0 * w1 * info["k_groups"]
-        assert info["kernel"] in ("mfma", "regpanel")
-        assert info["streamk"] == info["planned"]          # planned variants have a stream-K form
+        assert info["kernel"] in ("mfma", "regpanel", "persist")
+        # planned variants have a stream-K form, except the persistent one (one workgroup
+        # per CU already balances its tiles)
+        assert info["persistent"] == (info["kernel"] == "persist")
+        assert info["whole_tiles"] == info["persistent"]
+        if info["persistent"]:
+            assert not info["streamk"] and not info["splitk"]
+        else:
+            assert info["streamk"] == info["planned"]
         assert info["direct_loads"] == name.endswith("_dl")
         assert f"{info['BM']}x{info['BN']}x{info['BK']}" in name
     with pytest.raises(g.SgemmError):

@@ -136,6 +136,33 @@ def test_regpanel_variant_forced_ragged(gpu, M, N, K):
     assert rep["n_nonfinite"] == 0 and rep["n_inexact"] == 0, rep
 
 
+# The persistent variant (one workgroup per CU walking 128 x 256 tiles, each tile's C stored
+# among the next tile's MFMAs) forced onto: the low-K workload; a ragged shape (whole-tile
+# part on the kernel, right and bottom strips on the plan, K % 32 != 0); K with a partial
+# second panel (33), three panels (96, the per-tile panel loop), four with a partial last
+# (100); fewer tiles than CUs; tile counts that give workgroups an odd and an even number of
+# tiles (the odd ones end on an empty tile); and a K of one panel, which goes to the plan.
+# Leading dimensions are padded with NaN, so a read past a row's end shows in C.
+PS_FORCED = [(16384, 16384, 64), (4095, 4097, 4103), (1024, 2048, 33), (2048, 1024, 96),
+             (896, 1280, 100), (256, 512, 128), (128 * 25, 256 * 31, 64), (640, 768, 20)]
+
+
+@pytest.mark.parametrize("M,N,K", PS_FORCED)
+def test_persistent_variant_forced(gpu, M, N, K):
+    v = g.variant_names().index("mfma_128x256x32_w2x2_ps")
+    rng = np.random.default_rng(M + 7 * N + 13 * K)
+    A = wl.draw(rng, (M, K), "int")
+    B = wl.draw(rng, (K, N), "int")
+    _, dA, lda = device_matrix(A, K + 3)
+    _, dB, ldb = device_matrix(B, N + 5)
+    c = GuardedC(M, N, N + 2)
+    print(f"[parity] {M}x{N}x{K} int forced v{v} lda={lda} ldb={ldb}", flush=True)
+    run_kernel(f"v{v}", M, N, K, dA, lda, dB, ldb, c)
+    gpu.cuda.synchronize()
+    rep = oracle.check(A, B, c.result(), rows=sample_rows(M, 16, seed=K))
+    assert rep["n_nonfinite"] == 0 and rep["n_inexact"] == 0, rep
+
+
 # large shapes whose tile counts fall just past a whole round of 256 x 256 tiles
 STREAMK_PLAN_SHAPES = [(4500, 4500, 8192), (5000, 5000, 2048)]
 
