@@ -47,26 +47,41 @@
 namespace sgemm {
 
 namespace persist {
-constexpr int BM = 128, BN = 256, BK = 32, WM = 64, WN = 128, THREADS = 256;
+constexpr int BM = 128, BN = 256, BK = 32;
 constexpr int A_TILE = BM * BK;                 // A: BM rows of BK floats
 constexpr int LDS_FLOATS = A_TILE + BN * BK;    // + B^T: BN rows of BK floats (48 KiB)
 constexpr int STEPS = 16;                       // k-steps of 2 per panel
-constexpr int NL = 4 + 32;                      // a panel's loads per thread: A chunks, B values
-constexpr int NW = 4 + 8;                       // its LDS writes: A chunks, B^T chunks
 constexpr int kSchedVmemWrite = 0x040;
 static_assert(LDS_FLOATS * 4 <= 64 * 1024, "LDS");
 
-// Panel schedule, per k-step t (8 MFMAs each):
-//   t 0        read group 3 of this panel (6 reads)
+// The tile's split over WAVES waves (4: one per SIMD, 2 x 2 of 64 x 128; 8: two per SIMD,
+// 2 x 4 of 64 x 64) and what each thread stages of a panel.
+template <int WAVES>
+struct Shape {
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int WGN = WAVES / 2;               // waves along N (2 along M)
+    static constexpr int WM = BM / 2, WN = BN / WGN;
+    static constexpr int RB = WM / 32, CB = WN / 32;    // 32 x 32 blocks per wave
+    static constexpr int ACH = BM * BK / 4 / THREADS;   // A chunks per thread
+    static constexpr int ASTEP = THREADS / 8;           // rows between a thread's A chunks
+    static constexpr int BCH = BN * BK / 4 / THREADS;   // B^T chunks per thread
+    static constexpr int NL = ACH + 4 * BCH;            // a panel's loads per thread
+    static constexpr int NW = ACH + BCH;                // its LDS writes
+    static constexpr int NRG = RB + CB;                 // operand reads per group of 8 k
+    static constexpr int NS = RB * CB * 16;             // C values per lane per tile
+    static_assert(ASTEP % 16 == 0 && NW % 2 == 0, "staging layout");
+};
+
+// Panel schedule, per k-step t:
+//   t 0        read group 3 of this panel
 //   after t 1  barrier: every wave has read this panel
-//   t 2, 3     write the staged next panel into LDS (6 chunks each)
-//   t 4 .. 11  load the panel after next (36 loads)
+//   t 2, 3     write the staged next panel into LDS
+//   t 4 .. 11  load the panel after next
 //   after t 7  barrier: the next panel is in LDS
-//   t 8 .. 15  read groups 0, 1, 2 of the next panel (18 reads)
-//   any t      stores of the previous tile (kHalf per step for half of them)
-constexpr int kLoads[8] = {4, 5, 4, 5, 4, 5, 4, 5};
-constexpr int kReads[8] = {3, 3, 3, 3, 2, 2, 1, 1};
-constexpr int kHalf[16] = {2, 6, 2, 2, 4, 4, 4, 4, 2, 2, 2, 2, 7, 7, 7, 7};
+//   t 8 .. 15  read groups 0, 1, 2 of the next panel (a group's registers are free once its
+//              four k-steps are done: groups 0 and 1 from t 8, group 2 from t 12)
+//   any t      stores of the previous tile, weighted by kStoreW
+constexpr int kStoreW[16] = {2, 6, 2, 2, 4, 4, 4, 4, 2, 2, 2, 2, 7, 7, 7, 7};
 
 constexpr int prefix(const int *a, int n)
 {
@@ -74,22 +89,26 @@ constexpr int prefix(const int *a, int n)
     for (int i = 0; i < n; ++i) s += a[i];
     return s;
 }
-static_assert(prefix(kLoads, 8) == NL && prefix(kReads, 8) == 18 && prefix(kHalf, 16) == 64,
-              "schedule counts");
+// n items over `slots` steps, evenly: the first index of step t
+constexpr int spread(int n, int slots, int t) { return t * n / slots; }
 
-// Stores of the previous tile at step t of a panel that carries part PART of them (0: none,
-// 1: stores 0 .. 63, 2: stores 64 .. 127, 3: all 128): first index and count.
-constexpr int store_n(int part, int t) { return part == 0 ? 0 : kHalf[t] * (part == 3 ? 2 : 1); }
-constexpr int store_first(int part, int t)
+// Stores of the previous tile at step t of a panel that carries part PART of its ns stores
+// (0: none, 1: the first half, 2: the second half, 3: all): first index and count.
+constexpr int store_first(int part, int ns, int t)
 {
-    return (part == 2 ? 64 : 0) + prefix(kHalf, t) * (part == 3 ? 2 : 1);
+    const int h = part == 3 ? ns : ns / 2;
+    return (part == 2 ? ns / 2 : 0) + prefix(kStoreW, t) * h / 64;
+}
+constexpr int store_n(int part, int ns, int t)
+{
+    return part == 0 ? 0 : store_first(part, ns, t + 1) - store_first(part, ns, t);
 }
 
-// Of n operations spread over the step's 8 MFMAs (slot i holds [i n / 8, (i + 1) n / 8)),
-// how many of those with index in [lo, hi) fall in slot i.
-constexpr int slot_count(int i, int lo, int hi, int n)
+// Of n operations spread over a step's m MFMAs (slot i holds [i n / m, (i + 1) n / m)), how
+// many of those with index in [lo, hi) fall in slot i.
+constexpr int slot_count(int i, int m, int lo, int hi, int n)
 {
-    const int a = i * n / 8, b = (i + 1) * n / 8;
+    const int a = i * n / m, b = (i + 1) * n / m;
     const int x = a > lo ? a : lo, y = b < hi ? b : hi;
     return y > x ? y - x : 0;
 }
@@ -134,18 +153,21 @@ __device__ SGEMM_INLINE inline void sfor(F &&f)
     if constexpr (END > BEGIN) sfor_impl<BEGIN>(f, std::make_integer_sequence<int, END - BEGIN>{});
 }
 
-template <bool KT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int WAVES, bool KT>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4)))
 void k_sgemm_persist(GemmArgs p)
 {
     using namespace persist;
+    using Sh = Shape<WAVES>;
+    constexpr int WM = Sh::WM, WN = Sh::WN, RB = Sh::RB, CB = Sh::CB, NL = Sh::NL, NW = Sh::NW;
+    constexpr int ACH = Sh::ACH, BCH = Sh::BCH, NRG = Sh::NRG, NS = Sh::NS;
     using regpanel::lds_barrier;
     __shared__ __attribute__((aligned(16))) float lds[LDS_FLOATS];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lo = lane & 31, h = lane >> 5;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / Sh::WGN, wn = wave % Sh::WGN;
     const int M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb, ldc = p.ldc;
     const int T = p.tiles_m * p.tiles_n;
     const int G = gridDim.x;                    // at most T (host)
@@ -165,21 +187,21 @@ void k_sgemm_persist(GemmArgs p)
                        0};
     };
 
-    // ---- staging: thread tid loads A rows a_r + 32 j (16-byte chunk a_q of the panel's 32
-    // columns, j < 4) and B values at rows 4 b_k + e (e < 4) of columns b_c + 32 j (j < 8);
-    // the four values of column b_c + 32 j form the 16-byte chunk b_k of its B^T row.
+    // ---- staging: thread tid loads A rows a_r + ASTEP j (16-byte chunk a_q of the panel's
+    // 32 columns, j < ACH) and B values at rows 4 b_k + e (e < 4) of columns b_n + 32 j
+    // (j < BCH); the four values of one column form the 16-byte chunk b_k of its B^T row.
     const int a_r = tid >> 3, a_q = tid & 7;
-    const int b_c = tid & 31, b_k = tid >> 5;
-    uint32_t a_v[4], b_v[4];
+    const int b_c = tid & 31, b_k = (tid >> 5) & 7, b_n = b_c + 32 * BCH * (tid >> 8);
+    uint32_t a_v[ACH], b_v[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        a_v[j] = uint32_t(a_r + 32 * j) * uint32_t(lda) * 4u + 16u * a_q;
-        b_v[j] = uint32_t(4 * b_k + j) * uint32_t(ldb) * 4u + 4u * b_c;
-    }
+    for (int j = 0; j < ACH; ++j)
+        a_v[j] = uint32_t(a_r + Sh::ASTEP * j) * uint32_t(lda) * 4u + 16u * a_q;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) b_v[e] = uint32_t(4 * b_k + e) * uint32_t(ldb) * 4u + 4u * b_n;
     static_assert(32 % a_swizzle_period<8>() == 0, "a thread's rows share one swizzle");
     const int a_lds = a_r * BK + 4 * (a_q ^ a_swizzle<8>(a_r));
-    const int b_lds = A_TILE + b_c * BK + 4 * (b_k ^ a_swizzle<8>(b_c));
-    f32x4 pa[4], pb[8];
+    const int b_lds = A_TILE + b_n * BK + 4 * (b_k ^ a_swizzle<8>(b_c));
+    f32x4 pa[ACH], pb[BCH];
     int kp = 0;   // first k of the staged panel
     __amdgpu_buffer_rsrc_t ra, rb;
     // Resources of the panel at k0 of the tile at (m0, n0): A's ends at the end of row
@@ -198,27 +220,27 @@ void k_sgemm_persist(GemmArgs p)
     };
     auto load_one = [&](auto jc) SGEMM_INLINE {
         constexpr int j = decltype(jc)::value;
-        if constexpr (j < 4) {
+        if constexpr (j < ACH) {
             pa[j] = load_b128(ra, a_v[j]);
         } else {
-            constexpr int c = (j - 4) >> 2, e = (j - 4) & 3;
+            constexpr int c = (j - ACH) >> 2, e = (j - ACH) & 3;
             pb[c][e] = load_b32(rb, b_v[e] + 128u * c);
         }
     };
-    // Staged chunk j to LDS (A chunks 0 .. 3, then B^T chunks); with KT the A values at or
-    // past K are cleared.
+    // Staged chunk j to LDS (A chunks 0 .. ACH - 1, then B^T chunks); with KT the A values at
+    // or past K are cleared.
     auto write_one = [&](auto jc) SGEMM_INLINE {
         constexpr int j = decltype(jc)::value;
-        if constexpr (j < 4) {
+        if constexpr (j < ACH) {
             f32x4 v = pa[j];
             if constexpr (KT) {
                 const int kc = kp + 4 * a_q;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = kc + e < K ? v[e] : 0.0f;
             }
-            *reinterpret_cast<f32x4 *>(lds + a_lds + 32 * j * BK) = v;
+            *reinterpret_cast<f32x4 *>(lds + a_lds + Sh::ASTEP * j * BK) = v;
         } else {
-            *reinterpret_cast<f32x4 *>(lds + b_lds + 32 * (j - 4) * BK) = pb[j - 4];
+            *reinterpret_cast<f32x4 *>(lds + b_lds + 32 * (j - ACH) * BK) = pb[j - ACH];
         }
     };
 
@@ -227,29 +249,30 @@ void k_sgemm_persist(GemmArgs p)
     const int a_row = (wm * WM + lo) * BK;
     const int b_row = A_TILE + (wn * WN + lo) * BK;
     const int sw = a_swizzle<8>(lo);
-    f32x4 oa[4][2], ob[4][4];
-    auto read_one = [&](auto qc) SGEMM_INLINE {   // q = 6 g + j: j < 2 an A block, else B block j - 2
-        constexpr int g = decltype(qc)::value / 6, j = decltype(qc)::value % 6;
+    f32x4 oa[4][RB], ob[4][CB];
+    // q = NRG g + j: j < RB an A block, else B block j - RB
+    auto read_one = [&](auto qc) SGEMM_INLINE {
+        constexpr int g = decltype(qc)::value / NRG, j = decltype(qc)::value % NRG;
         const int chunk = 4 * ((2 * g + h) ^ sw);
-        if constexpr (j < 2)
+        if constexpr (j < RB)
             oa[g][j] = *reinterpret_cast<const f32x4 *>(lds + a_row + 32 * j * BK + chunk);
         else
-            ob[g][j - 2] =
-                *reinterpret_cast<const f32x4 *>(lds + b_row + 32 * (j - 2) * BK + chunk);
+            ob[g][j - RB] =
+                *reinterpret_cast<const f32x4 *>(lds + b_row + 32 * (j - RB) * BK + chunk);
     };
 
-    f32x16 acc[2][2][4];
+    f32x16 acc[2][RB][CB];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int r = 0; r < 2; ++r)
+        for (int r = 0; r < RB; ++r)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) acc[s][r][c] = f32x16{};
+            for (int c = 0; c < CB; ++c) acc[s][r][c] = f32x16{};
 
     // ---- C: lane (lo, h) holds, in register v of block (r, c), row 32 r + 8 (v / 4) + v % 4
-    // + 4 h and column 32 c + lo of the wave's 64 x 128. Store q of a tile is register
-    // v = (q / 4) % 16 of block (q / 64, q % 4): four consecutive stores fill 2 rows x 512
-    // bytes. Rows 32 r + 8 (v / 4) go in the scalar offset (8 values), rows v % 4 + 4 h and
+    // + 4 h and column 32 c + lo of the wave's WM x WN. Store q of a tile is register
+    // v = (q / CB) % 16 of block (q / (16 CB), q % CB): CB consecutive stores fill 2 rows of
+    // the wave's columns. Rows 32 r + 8 (v / 4) go in the scalar offset (8 values), rows v % 4 + 4 h and
     // the column in one of 4 lane offsets, 128 c bytes in the instruction's offset.
     __amdgpu_buffer_rsrc_t rc = make_rsrc32(p.C, 0u);   // the previous tile (or none)
     uint32_t lane_c[4];
@@ -258,7 +281,7 @@ void k_sgemm_persist(GemmArgs p)
         lane_c[e] = (uint32_t(4 * h + e) * uint32_t(ldc) + uint32_t(lo)) * 4u;
     auto store_one = [&](auto oc, auto qc) SGEMM_INLINE {
         constexpr int O = decltype(oc)::value, q = decltype(qc)::value;
-        constexpr int r = q >> 6, v = (q >> 2) & 15, c = q & 3;
+        constexpr int r = q / (16 * CB), v = (q / CB) % 16, c = q % CB;
         const uint32_t so = uint32_t(32 * r + 8 * (v >> 2)) * ldc4;
         // the element goes through a float first: __builtin_bit_cast applied to a vector
         // element lvalue reads the vector's first element instead
@@ -291,29 +314,26 @@ void k_sgemm_persist(GemmArgs p)
         sfor<0, STEPS>([&](auto tc) SGEMM_INLINE {
             constexpr int t = decltype(tc)::value;
             constexpr int g = t >> 2, s = t & 3;
-            constexpr int nr = t == 0 ? 6 : t >= 8 ? kReads[t - 8] : 0;
-            constexpr int nw = t == 2 || t == 3 ? 6 : 0;
-            constexpr int nl = t >= 4 && t < 12 ? kLoads[t - 4] : 0;
-            constexpr int ns = store_n(PART, t);
-            if constexpr (t == 0) sfor<18, 24>(read_one);
-            if constexpr (t >= 8) {
-                constexpr int q0 = prefix(kReads, t - 8);
-                sfor<q0, q0 + nr>(read_one);
-            }
-            if constexpr (nw > 0) sfor<(t - 2) * 6, (t - 1) * 6>(write_one);
+            constexpr int r0 = t >= 8 ? spread(3 * NRG, 8, t - 8) : 0;
+            constexpr int nr = t == 0 ? NRG : t >= 8 ? spread(3 * NRG, 8, t - 7) - r0 : 0;
+            constexpr int nw = t == 2 || t == 3 ? NW / 2 : 0;
+            constexpr int l0 = t >= 4 && t < 12 ? spread(NL, 8, t - 4) : 0;
+            constexpr int nl = t >= 4 && t < 12 ? spread(NL, 8, t - 3) - l0 : 0;
+            constexpr int ns = store_n(PART, NS, t);
+            static_assert(t >= 12 || r0 + nr <= 2 * NRG, "group 2 is still in use");
+            if constexpr (t == 0) sfor<3 * NRG, 4 * NRG>(read_one);
+            if constexpr (t >= 8) sfor<r0, r0 + nr>(read_one);
+            if constexpr (nw > 0) sfor<(t - 2) * (NW / 2), (t - 1) * (NW / 2)>(write_one);
             if constexpr (t == 4) load_set(next2);
-            if constexpr (nl > 0) {
-                constexpr int l0 = prefix(kLoads, t - 4);
-                sfor<l0, l0 + nl>(load_one);
-            }
+            if constexpr (nl > 0) sfor<l0, l0 + nl>(load_one);
             if constexpr (ns > 0) {
-                constexpr int s0 = store_first(PART, t);
+                constexpr int s0 = store_first(PART, NS, t);
                 sfor<s0, s0 + ns>([&](auto qc) SGEMM_INLINE { store_one(std::integral_constant<int, O>{}, qc); });
             }
 #pragma unroll
-            for (int r = 0; r < 2; ++r)
+            for (int r = 0; r < RB; ++r)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
+                for (int c = 0; c < CB; ++c) {
                     if constexpr (FIRST && t == 0)
                         acc[S][r][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(
                             oa[g][r][s], ob[g][c][s], f32x16{}, 0, 0, 0);
@@ -321,14 +341,14 @@ void k_sgemm_persist(GemmArgs p)
                         acc[S][r][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(
                             oa[g][r][s], ob[g][c][s], acc[S][r][c], 0, 0, 0);
                 }
-            // pin the step's order: its memory instructions spread over its 8 MFMAs
-            constexpr int n = nr + nw + nl + ns;
-            sfor<0, 8>([&](auto ic) SGEMM_INLINE {
+            // pin the step's order: its memory instructions spread over its MFMAs
+            constexpr int n = nr + nw + nl + ns, m = RB * CB;
+            sfor<0, m>([&](auto ic) SGEMM_INLINE {
                 constexpr int i = decltype(ic)::value;
-                constexpr int cr = slot_count(i, 0, nr, n);
-                constexpr int cw = slot_count(i, nr, nr + nw, n);
-                constexpr int cl = slot_count(i, nr + nw, nr + nw + nl, n);
-                constexpr int cs = slot_count(i, nr + nw + nl, n, n);
+                constexpr int cr = slot_count(i, m, 0, nr, n);
+                constexpr int cw = slot_count(i, m, nr, nr + nw, n);
+                constexpr int cl = slot_count(i, m, nr + nw, nr + nw + nl, n);
+                constexpr int cs = slot_count(i, m, nr + nw + nl, n, n);
                 __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
                 if constexpr (cr > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, cr, 0);
                 if constexpr (cw > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, cw, 0);
@@ -348,11 +368,11 @@ void k_sgemm_persist(GemmArgs p)
         sfor<0, NL>(load_one);
         sfor<0, NW>(write_one);
         lds_barrier();
-        sfor<0, 6>(read_one);
+        sfor<0, NRG>(read_one);
         __builtin_amdgcn_sched_barrier(0);
-        sfor<6, 12>(read_one);
+        sfor<NRG, 2 * NRG>(read_one);
         __builtin_amdgcn_sched_barrier(0);
-        sfor<12, 18>(read_one);
+        sfor<2 * NRG, 3 * NRG>(read_one);
         __builtin_amdgcn_sched_barrier(0);
         PanelAt t1 = t0;
         t1.k0 = BK;
@@ -390,7 +410,7 @@ void k_sgemm_persist(GemmArgs p)
         prev = tile(S1{}, i + 1, prev);
     }
     rc = c_rsrc(prev.m0, prev.n0, prev.v);
-    sfor<0, 128>([&](auto qc) SGEMM_INLINE { store_one(S1{}, qc); });
+    sfor<0, NS>([&](auto qc) SGEMM_INLINE { store_one(S1{}, qc); });
 }
 
 }  // namespace sgemm

@@ -55,8 +55,8 @@ typedef void (*MfmaKernel)(GemmArgs);
 MfmaKernel regpanel_kernel();
 MfmaKernel regpanel_streamk_kernel();
 // k_sgemm_persist lives in sgemm_persist.hip (same reason)
-MfmaKernel persist_kernel();
-MfmaKernel persist_ktail_kernel();
+MfmaKernel persist_kernel(int waves);
+MfmaKernel persist_ktail_kernel(int waves);
 namespace {
 
 struct VariantEntry {
@@ -101,16 +101,19 @@ VariantEntry regpanel_entry(const char *name, double rate, double overhead)
         "regpanel"};
 }
 
-// The persistent kernel (kernel_persist.hpp): 128 x 256 tiles of four 64 x 128 waves, one
-// workgroup per CU, each tile's C stored among the next tile's MFMAs. Whole tiles only, at
-// least two K-panels; no split-K or stream-K form.
-VariantEntry persist_entry(const char *name, double rate, double overhead)
+// The persistent kernel (kernel_persist.hpp): 128 x 256 tiles of four 64 x 128 waves (one
+// per SIMD) or eight 64 x 64 waves (two per SIMD), one workgroup per CU, each tile's C
+// stored among the next tile's MFMAs. Whole tiles only, at least two K-panels; no split-K
+// or stream-K form.
+VariantEntry persist_entry(const char *name, int waves, bool planned, double rate,
+                           double overhead)
 {
-    VariantEntry e{Variant{name, 128, 256, 32, 2, 2, 1, rate, overhead, 1.0, false, false, false},
-                   persist_kernel(), nullptr, nullptr, 256, 32, 1, "persist"};
+    VariantEntry e{Variant{name, 128, 256, 32, 2, waves / 2, 1, rate, overhead, 1.0, false, planned,
+                           false},
+                   persist_kernel(waves), nullptr, nullptr, 64 * waves, 32, 1, "persist"};
     e.v.whole_tiles = true;
     e.persistent = true;
-    e.kern_ktail = persist_ktail_kernel();
+    e.kern_ktail = persist_ktail_kernel(waves);
     return e;
 }
 
@@ -144,8 +147,9 @@ const VariantEntry kVariants[] = {
     entry<80, 64, 32, 1, 2, 1, 2, true, true, 16>("mfma16_80x64x32_w1x2_kg2_dl", 2, 1.025, 64, 0.84),
     entry<48, 64, 32, 1, 2, 1, 4, true, true, 16>("mfma16_48x64x32_w1x2_kg4_dl", 1, 0.975, 256, 1.0),
     entry<64, 64, 64, 2, 2, 1, 2, true, true, 16>("mfma16_64x64x64_w2x2_kg2_dl", 1, 1.020, 196, 1.0),
-    regpanel_entry("mfma_256x256x32_w2x2_rp", 1.105, 44),
-    persist_entry("mfma_128x256x32_w2x2_ps", 1.05, 0),
+    regpanel_entry("mfma_256x256x32_w2x2_rp", 1.105, 20),
+    persist_entry("mfma_128x256x32_w2x2_ps", 4, false, 1.05, 0),
+    persist_entry("mfma_128x256x32_w2x4_ps", 8, true, 1.10, 0),
 };
 constexpr int kNumVariants = int(sizeof(kVariants) / sizeof(kVariants[0]));
 

@@ -8,8 +8,15 @@
 
 namespace sgemm {
 
-// Launch handles for the variant table in sgemm_f32.hip: K a multiple of 32, and any K.
-void (*persist_kernel())(GemmArgs) { return &k_sgemm_persist<false>; }
-void (*persist_ktail_kernel())(GemmArgs) { return &k_sgemm_persist<true>; }
+// Launch handles for the variant table in sgemm_f32.hip, by waves per workgroup (4: one per
+// SIMD, 8: two): K a multiple of 32, and any K.
+void (*persist_kernel(int waves))(GemmArgs)
+{
+    return waves == 8 ? &k_sgemm_persist<8, false> : &k_sgemm_persist<4, false>;
+}
+void (*persist_ktail_kernel(int waves))(GemmArgs)
+{
+    return waves == 8 ? &k_sgemm_persist<8, true> : &k_sgemm_persist<4, true>;
+}
 
 }  // namespace sgemm

@@ -101,13 +101,17 @@ def test_plan(shape, expect_tile):
     plan = g.sgemm_f32_plan_describe(M, N, K, P, None, P + (1 << 30), None, P + (1 << 31), None,
                                      num_cus=256)
     tiles = plan["tiles"][0] * plan["tiles"][1]
-    assert plan["grid"] == tiles            # one workgroup per tile
+    info = g.sgemm_f32_variant_info(plan["variant"])
+    # one workgroup per tile, or one per CU walking the tiles
+    assert plan["grid"] == (min(tiles, 256) if info["persistent"] else tiles)
     assert plan["direct_loads"] == plan["name"].endswith("_dl")
     assert plan["tiles"][0] * plan["BM"] >= M and plan["tiles"][1] * plan["BN"] >= N
     if expect_tile:
         assert plan["BM"] == plan["BN"] == expect_tile
     elif M * N >= 1 << 20:
         assert plan["grid"] >= 64   # 1024-class shapes still spread over the chip
+    if shape == (16384, 16384, 64):
+        assert plan["name"] == "mfma_128x256x32_w2x4_ps"   # C's stores among the MFMAs
     # the request-bytes model: each A panel once per tile column, each B panel per tile row
     tm, tn = plan["tiles"]
     assert plan["tile_request_bytes"] == 4 * (M * K * tn + K * N * tm)

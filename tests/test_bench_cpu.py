@@ -48,7 +48,8 @@ def test_committed_traffic_entries_are_well_formed():
         assert entry["bytes_per_launch"] >= entry["compulsory_bytes"] * 0.9, name
         assert len(entry["kernel_code_sha"]) == 16 and entry["variant"].startswith("mfma")
         assert entry["kernel_symbol"].startswith(("_ZN5sgemm12k_sgemm_mfma",
-                                                  "_ZN5sgemm16k_sgemm_regpanel"))
+                                                  "_ZN5sgemm16k_sgemm_regpanel",
+                                                  "_ZN5sgemm15k_sgemm_persist"))
 
 
 def test_more_than_one_gpu_is_refused():

@@ -147,9 +147,10 @@ PS_FORCED = [(16384, 16384, 64), (4095, 4097, 4103), (1024, 2048, 33), (2048, 10
              (896, 1280, 100), (256, 512, 128), (128 * 25, 256 * 31, 64), (640, 768, 20)]
 
 
+@pytest.mark.parametrize("name", ["mfma_128x256x32_w2x2_ps", "mfma_128x256x32_w2x4_ps"])
 @pytest.mark.parametrize("M,N,K", PS_FORCED)
-def test_persistent_variant_forced(gpu, M, N, K):
-    v = g.variant_names().index("mfma_128x256x32_w2x2_ps")
+def test_persistent_variant_forced(gpu, M, N, K, name):
+    v = g.variant_names().index(name)
     rng = np.random.default_rng(M + 7 * N + 13 * K)
     A = wl.draw(rng, (M, K), "int")
     B = wl.draw(rng, (K, N), "int")
