@@ -11,15 +11,19 @@
 //
 //  * One workgroup per CU walks tiles pos, pos + G, ... (G workgroups, pos its place in an
 //    order that keeps each XCD's workgroups contiguous, so the tiles in flight on one XCD are
-//    neighbours in the grouped tile order and share A rows and B columns in its L2). Four
-//    waves (2 x 2), one per SIMD; a wave's 64 x 128 of the tile is 2 x 4 blocks of 32 x 32
-//    accumulated by v_mfma_f32_32x32x2_f32.
-//  * Two accumulator sets of 128 registers per lane (all 256 AGPRs): tile i accumulates in
-//    set i % 2 while the previous tile's set is written, one 4-byte buffer store at a time
-//    between the MFMAs, 128 per lane per tile spread over the tile's first two K-panels.
-//    Measured in a one-wave-per-SIMD MFMA stream writing 1 GiB, stores placed so cost the
-//    matrix pipe nothing, while assembling 16-byte chunks of a row first (register moves
-//    among the MFMAs) cost a fifth of its time.
+//    neighbours in the grouped tile order and share A rows and B columns in its L2). WAVES
+//    waves: eight (2 x 4, two per SIMD, 64 x 64 each: the planned form) or four (2 x 2,
+//    one per SIMD, 64 x 128 each); a wave's part is 32 x 32 blocks accumulated by
+//    v_mfma_f32_32x32x2_f32. The eight-wave form is the faster (16384^2 x 64: 291 against
+//    323 us): with one wave per SIMD and 8 MFMAs per k-step the load and barrier latencies
+//    show; a second wave per SIMD hides them.
+//  * Two accumulator sets per lane (64 registers each with eight waves, in 238 registers
+//    in all; 128 each in the 256 AGPRs with four): tile i accumulates in set i % 2 while
+//    the previous tile's set is written, one 4-byte buffer store at a time between the
+//    MFMAs, spread over the tile's first two K-panels. Measured in a one-wave-per-SIMD MFMA
+//    stream writing 1 GiB, stores placed so cost the matrix pipe nothing, while assembling
+//    16-byte chunks of a row first (register moves among the MFMAs) cost a fifth of its
+//    time.
 //  * Why 4-byte stores: in the 32 x 32 MFMA's result a lane holds 16 rows of one column, so
 //    one register over the wave is 2 rows of 32 consecutive columns, two whole 128-byte
 //    lines. That needs plain 32-column blocks (no column interleave), so each B operand read
@@ -29,9 +33,9 @@
 //    written as 16-byte chunks of four k. The A and B^T reads and writes are conflict-free.
 //  * Each tile's first k-step takes a zero accumulator operand: no register clears.
 //  * The panel pipeline is kernel_regpanel.hpp's: one LDS stage (48 KiB), the panel after
-//    next staged in registers (4 A chunks and 32 B values per thread), a whole panel's
-//    operands read ahead, two barriers per panel, every memory instruction between MFMAs
-//    (pinned by scheduling barriers). The stream of panels runs on across tiles: a tile's
+//    next staged in registers (with eight waves 2 A chunks and 16 B values per thread), a
+//    whole panel's operands read ahead, two barriers per panel, every memory instruction
+//    between MFMAs (pinned by scheduling barriers). The stream of panels runs on across tiles: a tile's
 //    last panels load the next tile's first ones.
 //  * Whole tiles only: M and N are multiples of 128 and 256 (the host computes any
 //    remaining strip of C with the other kernels), so no store needs a per-lane condition.
