@@ -66,7 +66,9 @@ inline double variant_cost(const Variant &v, const Operands &o, int cus)
     const int64_t tn = (int64_t(o.N) + v.BN - 1) / v.BN;
     // the busiest CU runs ceil(tiles / CUs) tiles; each is BM*BN*K multiply-adds at the
     // variant's measured relative rate plus the variant's per-tile overhead
-    const int64_t per_cu = (tm * tn * o.splits + cus - 1) / cus;
+    int64_t per_cu = (tm * tn * o.splits + cus - 1) / cus;
+    // the persistent kernel walks its tiles in pairs: an odd count ends on an empty tile
+    if (v.whole_tiles) per_cu += per_cu & 1;
     const double k = o.K > 0 ? double(o.K) / o.splits : 1;
     const double rate = per_cu >= v.wg_per_cu ? v.rate : v.rate * v.solo;
     return double(per_cu) * double(v.BM) * v.BN * (k / rate + v.overhead);
