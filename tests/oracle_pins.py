@@ -212,6 +212,62 @@ def pin_check_exact(lib):
     assert oracle.check(Az, B, ez, lib=lib)["n_zero_den_bad"] == 1
 
 
+def pin_check_integer(lib):
+    """oracle.check on non-constant small-integer A and B at the pages' worked shapes and
+    at square shapes (M = N = K, where a transposed or mis-strided operand index still
+    reads inside the arrays): the exact answer, from Python-integer sums, must be reported
+    exact everywhere, and an error planted at any one position must be reported there,
+    with the exact normalised size 1 / sum_k |a_ik b_kj|.
+    Each C element is the length-K dot product of row i of A with column j of B ("SGEMM:
+    Shared Memory Tiling Visualizer", "Why Tiling Works (The Math)")."""
+    rng = np.random.default_rng(23)
+    shapes = [(7, 7, 7), (9, 9, 9), (6, 6, 9), (4, 4, 8), (8, 8, 8), (5, 11, 3)]
+    for (M, N, K) in shapes:
+        A = _ints(rng, (M, K))
+        B = _ints(rng, (K, N))
+        # no zero rows of A or columns of B, so every magnitude sum is positive
+        A[A == 0] = 1
+        B[B == 0] = -1
+        exact_i = _exact_int_product(A, B)
+        den_i = [[sum(abs(int(A[i, k]) * int(B[k, j])) for k in range(K)) for j in range(N)]
+                 for i in range(M)]
+        exact = np.array(exact_i, dtype=np.float32)
+        rep = oracle.check(A, B, exact, lib=lib)
+        assert rep["n_checked"] == M * N, rep
+        assert rep["n_inexact"] == 0 and rep["max_err"] == 0.0, (M, N, K, rep)
+        assert rep["n_nonfinite"] == 0 and rep["n_zero_den_bad"] == 0, rep
+        for (i, j) in [(0, 0), (M - 1, N - 1), (M // 2, N - 1), (M - 1, 0), (M // 3, N // 2)]:
+            bad = exact.copy()
+            bad[i, j] += 1.0
+            rep = oracle.check(A, B, bad, lib=lib)
+            assert rep["n_inexact"] == 1, (M, N, K, i, j, rep)
+            assert (rep["arg_i"], rep["arg_j"]) == (i, j), (M, N, K, i, j, rep)
+            assert rep["max_err"] == 1.0 / den_i[i][j], (M, N, K, i, j, rep)
+            # the same row checked alone, and a row list that skips it
+            rep = oracle.check(A, B, bad, rows=[i], lib=lib)
+            assert rep["n_checked"] == N and rep["n_inexact"] == 1, rep
+            others = [r for r in range(M) if r != i]
+            rep = oracle.check(A, B, bad, rows=others, lib=lib)
+            assert rep["n_inexact"] == 0 and rep["n_checked"] == (M - 1) * N, rep
+
+
+def pin_sample_integer(lib):
+    """oracle.sample on non-constant small-integer A and B at square and worked shapes:
+    every element against Python-integer sums, and every magnitude sum against
+    sum_k |a_ik b_kj| in integers."""
+    rng = np.random.default_rng(24)
+    for (M, N, K) in [(8, 8, 8), (6, 6, 9), (5, 9, 4)]:
+        A = _ints(rng, (M, K))
+        B = _ints(rng, (K, N))
+        exact = np.array(_exact_int_product(A, B), dtype=np.float64)
+        den = np.array([[sum(abs(int(A[i, k]) * int(B[k, j])) for k in range(K))
+                         for j in range(N)] for i in range(M)], dtype=np.float64)
+        iv, jv = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+        ref, d = oracle.sample(A, B, iv.ravel(), jv.ravel(), lib=lib)
+        assert np.array_equal(ref, exact.ravel()), f"sample values at {M}x{N}x{K}"
+        assert np.array_equal(d, den.ravel()), f"sample magnitude sums at {M}x{N}x{K}"
+
+
 def pin_sample(lib):
     """oracle.sample on closed forms: identity (value and |value| as magnitude sum),
     all-ones (K and K)."""
@@ -255,4 +311,5 @@ def pin_transpose(lib):
 ALL_PINS = [pin_identity, pin_permutation, pin_all_ones, pin_rank_one,
             pin_worked_shapes_exact, pin_transpose_identity, pin_k_split,
             pin_rational_bound, pin_numpy_matmul, pin_leading_dimensions,
-            pin_check_exact, pin_sample, pin_transpose]
+            pin_check_exact, pin_check_integer, pin_sample, pin_sample_integer,
+            pin_transpose]
