@@ -171,11 +171,48 @@ def cpu_baseline(A, B, C_dev, M, N, K, seconds: float):
     rep = oracle.check(A, B, C_host, rows=rows, lib=lib)
     t = time.perf_counter() - t0
     flop = 2.0 * len(rows) * N * K
-    return {"value": round(flop / t / 1e9, 3), "unit": "GFLOP/s", "cores": oracle.threads(lib),
+    cores = oracle.threads(lib)
+    # the same oracle on one thread, over a few of those rows (about 3 s of work)
+    n1 = int(min(len(rows), max(1, 3.0 / (per_row * cores))))
+    rows1 = rows[np.linspace(0, len(rows) - 1, num=n1).astype(np.int64)]
+    prev = oracle.set_threads(1, lib)
+    try:
+        t0 = time.perf_counter()
+        oracle.check(A, B, C_host, rows=rows1, lib=lib)
+        t1 = time.perf_counter() - t0
+    finally:
+        oracle.set_threads(prev, lib)
+    return {"value": round(flop / t / 1e9, 3), "unit": "GFLOP/s", "cores": cores,
             "kind": "oracle",
             "sample": f"{len(rows)} of {M} rows of C (all {N} columns, K={K}), fp64 oracle, "
                       f"OpenMP over rows, {t:.1f} s",
+            "single_thread": {"value": round(2.0 * n1 * N * K / t1 / 1e9, 3),
+                              "unit": "GFLOP/s", "cores": 1,
+                              "sample": f"{n1} of those rows on one thread, {t1:.2f} s"},
             "check_max_err": rep["max_err"], "check_nonfinite": rep["n_nonfinite"]}
+
+
+def launch_stats(step, torch, dev, stream, steps: int, flush=None) -> dict:
+    """Per-launch times from an event pair around each step (a separate pass after the
+    timed region). With `flush`, a 512 MiB buffer is overwritten before each launch, outside
+    its events, so every launch starts with A, B and C evicted from L2 and the memory-side
+    cache (cold), instead of back to back (warm)."""
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize(dev)
+    for i in range(steps):
+        if flush is not None:
+            flush.fill_(float(i))
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize(dev)
+    ms = sorted(a.elapsed_time(b) for a, b in zip(starts, ends))
+    n = len(ms)
+    pick = lambda q: ms[min(n - 1, max(0, int(round(q * (n - 1)))))]
+    return {"launches": n, "median_ms": round(pick(0.5), 5), "min_ms": round(ms[0], 5),
+            "p90_ms": round(pick(0.9), 5), "mean_ms": round(sum(ms) / n, 5),
+            "max_ms": round(ms[-1], 5)}
 
 
 def bench_transpose(args) -> int:
@@ -238,6 +275,9 @@ def main() -> int:
                     help="the entry point a step calls (default: the hot path sgemm_f32); the "
                          "transposes move an M x N matrix of the workload's A shape")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time launches with L2 and the memory-side cache flushed before "
+                         "each (512 MiB written between launches, outside the timed launch)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run a plain device copy of this size instead (counter scaling)")
@@ -288,7 +328,7 @@ def main() -> int:
         plan["BM"] = plan["BN"] = plan["BK"] = plan["grid"] = None   # chosen per split count
     if kern == "streamk":
         sk_plan = g.sgemm_f32_streamk_describe(M, N, K, args.variant)
-        ws_bytes = lib.sgemm_f32_streamk_workspace_size(M, N, K, args.variant)
+        ws_bytes = lib.sgemm_f32_streamk_workspace_size(M, N, K, K, N, N, args.variant)
         ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device=dev)
         plan["streamk_workspace_bytes"] = ws_bytes
         plan["streamk_plan"] = sk_plan
@@ -339,10 +379,21 @@ def main() -> int:
     gflops = flop * args.steps / (elapsed_ms / 1e3) / 1e9
     log(f"bench: {ms:.4f} ms/step (events), wall {wall:.3f} s, {gflops:.1f} GFLOP/s")
 
+    # per-launch statistics, in passes of their own after the timed region
+    timing = {"region_ms_per_step": round(ms, 5),
+              "host_us_per_call": round(wall / args.steps * 1e6, 2),
+              "warm": launch_stats(step, torch, dev, stream, args.steps)}
+    if args.cold:
+        flush = torch.empty((512 << 20) // 4, dtype=torch.float32, device=dev)
+        timing["cold"] = launch_stats(step, torch, dev, stream, args.steps, flush)
+        del flush
+    log(f"bench: per-launch timing {timing}")
+
     # roofline of the one kernel a step launches
     compulsory = 4.0 * (M * K + K * N + M * N)
     t_mfma = flop / (PEAK_FP32_MFMA_TFLOPS * 1e12)
     t_hbm = compulsory / (PEAK_HBM_GBS * 1e9)
+    t_step = ms / 1e3
     if kern not in ("auto", "splitk", "streamk"):
         # the scalar rungs run on the vector ALUs without packed FP32: 256 CUs x 4 SIMDs x
         # 16 lanes x 2 FLOP x 2.4 GHz
@@ -360,6 +411,13 @@ def main() -> int:
     roof["traffic"] = (measured_traffic(args.workload, plan["name"])
                        if kern == "auto" and args.variant < 0 else None)
     roof["kernel"] = plan["name"]
+    # both floors against the measured step, whichever binds: the FP32 matrix floor 2MNK /
+    # 157.3 TFLOP/s and the HBM floor 4 (MK + KN + MN) / 8 TB/s (read A and B, write C once)
+    roof["frac_mfma"] = round(t_mfma / t_step, 4)
+    roof["frac_hbm"] = round(t_hbm / t_step, 4)
+    roof["compulsory_bytes"] = int(compulsory)
+    if roof["traffic"]:
+        roof["traffic_over_compulsory"] = round(roof["traffic"] / compulsory, 3)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -381,6 +439,7 @@ def main() -> int:
                    "grid": plan["grid"], "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "timing": timing,
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -10,7 +10,7 @@ Raw layer (same names and arguments as the C ABI; pointers are integers):
     sgemm_f32_splitk(..., splits, workspace, workspace_bytes, stream=0)
     sgemm_f32_splitk_workspace_size(M, N, K, splits) -> int
     sgemm_f32_streamk(..., variant, workspace, workspace_bytes, stream=0)
-    sgemm_f32_streamk_workspace_size(M, N, K, variant=-1) -> int
+    sgemm_f32_streamk_workspace_size(M, N, K, lda, ldb, ldc, variant=-1) -> int
     sgemm_f32_streamk_describe(M, N, K, variant=-1, num_cus=0) -> dict
     sgemm_f32_regtiled(..., tm=4, tn=4, stream=0)
     sgemm_f32_lds_transpose(rows, cols, src, ldi, dst, ldo, tile=32, pad=0, stream=0)
@@ -66,7 +66,7 @@ def _load():
         lib.sgemm_f32_splitk_workspace_size.restype = ctypes.c_size_t
         lib.sgemm_f32_streamk.argtypes = gemm + [i, p, ctypes.c_size_t, p]
         lib.sgemm_f32_streamk.restype = i
-        lib.sgemm_f32_streamk_workspace_size.argtypes = [i, i, i, i]
+        lib.sgemm_f32_streamk_workspace_size.argtypes = [i, i, i, i, i, i, i]
         lib.sgemm_f32_streamk_workspace_size.restype = ctypes.c_size_t
         lib.sgemm_f32_streamk_describe.argtypes = [i, i, i, i, i, ctypes.c_char_p, i]
         lib.sgemm_f32_streamk_describe.restype = i
@@ -135,8 +135,11 @@ def sgemm_f32_streamk(M, N, K, A, lda, B, ldb, C, ldc, variant, workspace, works
            "sgemm_f32_streamk")
 
 
-def sgemm_f32_streamk_workspace_size(M, N, K, variant=-1) -> int:
-    return _load().sgemm_f32_streamk_workspace_size(M, N, K, variant)
+def sgemm_f32_streamk_workspace_size(M, N, K, lda=None, ldb=None, ldc=None, variant=-1) -> int:
+    lda = K if lda is None else lda
+    ldb = N if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    return _load().sgemm_f32_streamk_workspace_size(M, N, K, lda, ldb, ldc, variant)
 
 
 def sgemm_f32_streamk_describe(M, N, K, variant=-1, num_cus=0) -> dict:
@@ -254,7 +257,8 @@ def matmul(A, B, out=None, kernel: str = "auto", variant: int = -1, tile=32, pad
             ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device=A.device)
             sgemm_f32_splitk(*args, splits, ws.data_ptr(), ws_bytes, stream=stream)
         elif kernel == "streamk":
-            ws_bytes = sgemm_f32_streamk_workspace_size(M, N, K, variant)
+            ws_bytes = sgemm_f32_streamk_workspace_size(M, N, K, args[4], args[6], args[8],
+                                                        variant)
             ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device=A.device)
             sgemm_f32_streamk(*args, variant, ws.data_ptr(), ws_bytes, stream=stream)
         elif kernel == "regtiled":

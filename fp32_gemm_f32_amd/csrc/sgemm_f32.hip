@@ -23,7 +23,7 @@
 namespace sgemm {
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 // Hardware grid dimensions above 65535 workgroups in y are avoided; the simple kernels
 // stride their rows over the grid instead.
 constexpr unsigned kMaxGridY = 65535;
@@ -484,12 +484,14 @@ extern "C" int sgemm_f32_splitk(int M, int N, int K, const float *A, int lda, co
     return run_splitk(splits, o, A, B, C, workspace, workspace_bytes, stream, cus);
 }
 
-extern "C" size_t sgemm_f32_streamk_workspace_size(int M, int N, int K, int variant)
+extern "C" size_t sgemm_f32_streamk_workspace_size(int M, int N, int K, int lda, int ldb,
+                                                   int ldc, int variant)
 {
-    if (M <= 0 || N <= 0 || K <= 0) return 0;
+    if (M <= 0 || N <= 0 || K <= 0 || validate_shape(M, N, K, lda, ldb, ldc) != SGEMM_OK)
+        return 0;
     int cus = 0;
     if (device_cus(&cus) != SGEMM_OK) return 0;
-    const Operands o = make_operands(M, N, K, K, N, N);
+    const Operands o = make_operands(M, N, K, lda, ldb, ldc);
     bool sk = false;
     const int vi = plan_streamk(variant < 0 ? -1 : variant, o, cus, &sk);
     if (vi < 0 || !sk) return 0;
@@ -731,8 +733,9 @@ extern "C" int sgemm_f32_plan_describe(int M, int N, int K, const float *A, int 
 {
     if (!buf || buflen <= 0) return SGEMM_EINVAL_ARG;
     (void)A; (void)B; (void)C;
+    const int vs = validate_shape(M, N, K, lda, ldb, ldc);
+    if (vs != SGEMM_OK) return vs;
     const Operands o = make_operands(M, N, K, lda, ldb, ldc);
-    if (M < 0 || N < 0 || K < 0) return SGEMM_EINVAL_DIM;
     int cus = num_cus;
     if (cus <= 0) {
         const int qs = device_cus(&cus);

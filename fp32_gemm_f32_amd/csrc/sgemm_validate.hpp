@@ -31,12 +31,21 @@ inline bool overlap(const void *a, int64_t a_elems, const void *b, int64_t b_ele
     return a0 < b1 && b0 < a1;
 }
 
-inline int validate(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
-                    const float *C, int ldc)
+// The shape rules alone (dimensions, then leading dimensions), for the entry points that
+// plan without operands.
+inline int validate_shape(int M, int N, int K, int lda, int ldb, int ldc)
 {
     if (M < 0 || N < 0 || K < 0) return SGEMM_EINVAL_DIM;
     if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
         return SGEMM_EINVAL_LD;
+    return SGEMM_OK;
+}
+
+inline int validate(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
+                    const float *C, int ldc)
+{
+    const int st = validate_shape(M, N, K, lda, ldb, ldc);
+    if (st != SGEMM_OK) return st;
     const int64_t sa = span_elems(M, K, lda);
     const int64_t sb = span_elems(K, N, ldb);
     const int64_t sc = span_elems(M, N, ldc);

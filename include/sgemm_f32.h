@@ -67,7 +67,10 @@ int sgemm_f32(int M, int N, int K,
 
 /*
  * Split-K for shapes whose M x N gives too few tiles to fill the GPU (small M * N, large
- * K): K is cut into `splits` ranges of whole K-panels; the hot kernel computes each
+ * K). The pages fill the GPU by the choice of tile size alone ("Shared Memory Tiling",
+ * "Choosing a tile size"; "Visual walkthrough - Memory hierarchy", Step 7); when even the
+ * smallest tile leaves compute units idle, this entry point also cuts each tile's K-sum.
+ * K is cut into `splits` ranges of whole K-panels; the hot kernel computes each
  * (tile, range) item into its own M x N slice of `workspace` (packed rows of N floats),
  * and a second kernel sums the slices in ascending range order into C, so repeated calls
  * give identical bits. splits = 0 lets the library choose (about two items per compute
@@ -120,9 +123,12 @@ int sgemm_f32_streamk(int M, int N, int K,
                       int variant, float *workspace, size_t workspace_bytes,
                       void *stream);
 
-/* Bytes of workspace sgemm_f32_streamk needs for this shape and variant on the current
- * device (0 when the plan shares no tile, for empty shapes, or on a bad variant). */
-size_t sgemm_f32_streamk_workspace_size(int M, int N, int K, int variant);
+/* Bytes of workspace sgemm_f32_streamk needs for these arguments on the current device:
+ * the same shape, leading dimensions and variant the call will get (the plan depends on
+ * them). 0 when the plan shares no tile, for empty shapes, for dimensions or leading
+ * dimensions that sgemm_f32_streamk would reject, or on a bad variant. */
+size_t sgemm_f32_streamk_workspace_size(int M, int N, int K, int lda, int ldb, int ldc,
+                                        int variant);
 
 /*
  * Writes a one-line JSON description of sgemm_f32_streamk's plan for packed operands of
@@ -240,10 +246,13 @@ const char *sgemm_f32_status_string(int status);
  * Writes a one-line JSON description of the plan sgemm_f32 would run for these
  * arguments into buf (at most buflen bytes including the NUL): variant, tile shape,
  * waves, grid, workgroups resident per CU, whether panels load straight into LDS, and
- * the operand bytes the tiles request. Pointers are used for their
- * alignment only and are never dereferenced. num_cus > 0 plans for that many compute
- * units; num_cus <= 0 queries the current device (SGEMM_ELAUNCH if none). Returns the
- * variant index (>= 0), or a negative sgemm_status (buffer too small: SGEMM_EINVAL_ARG).
+ * the operand bytes the tiles request. The plan is the pages' tile-size trade-off: reuse
+ * per staged element against the parallelism left ("Shared Memory Tiling", "Choosing a
+ * tile size"). Dimensions and leading dimensions are validated as in sgemm_f32
+ * (SGEMM_EINVAL_DIM, SGEMM_EINVAL_LD); pointers are used for their alignment only and
+ * are never dereferenced. num_cus > 0 plans for that many compute units; num_cus <= 0
+ * queries the current device (SGEMM_ELAUNCH if none). Returns the variant index (>= 0),
+ * or a negative sgemm_status (buffer too small: SGEMM_EINVAL_ARG).
  */
 int sgemm_f32_plan_describe(int M, int N, int K,
                             const float *A, int lda,

@@ -56,6 +56,8 @@ def _bind(lib):
     lib.oracle_transpose.restype = ctypes.c_int
     lib.oracle_threads.argtypes = []
     lib.oracle_threads.restype = ctypes.c_int
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_threads.restype = ctypes.c_int
     return lib
 
 
@@ -150,3 +152,8 @@ def transpose(X: np.ndarray, lib=None) -> np.ndarray:
 def threads(lib=None) -> int:
     """OpenMP threads the oracle's parallel loops use."""
     return (lib or load()).oracle_threads()
+
+
+def set_threads(n: int, lib=None) -> int:
+    """Threads for the oracle's later parallel regions; returns the previous count."""
+    return (lib or load()).oracle_set_threads(n)

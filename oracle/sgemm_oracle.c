@@ -214,3 +214,16 @@ int oracle_threads(void)
     return 1;
 #endif
 }
+
+/* Sets the threads of the oracle's later parallel regions (for timing it on one core);
+ * returns the previous count. Results do not depend on it: rows are independent. */
+int oracle_set_threads(int n)
+{
+    const int prev = oracle_threads();
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+    return prev;
+}

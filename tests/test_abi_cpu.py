@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert g.abi_version() == 1
+    assert g.abi_version() == 2
     lib = g.library()
     for code in range(-7, 1):
         s = lib.sgemm_f32_status_string(code).decode()
@@ -188,6 +188,25 @@ def test_streamk_validation():
     # empty output: nothing to do, before any device query
     assert lib.sgemm_f32_streamk(0, 48, 64, P, 64, P + 4096, 48, P + 8192, 48, -1, ws, 64,
                                  None) == 0
+
+
+def test_workspace_queries_validate_leading_dimensions():
+    lib = g.library()
+    # invalid dimensions or leading dimensions need no workspace (and make no device query)
+    assert lib.sgemm_f32_streamk_workspace_size(64, 48, 64, 63, 48, 48, -1) == 0
+    assert lib.sgemm_f32_streamk_workspace_size(64, 48, 64, 64, 47, 48, -1) == 0
+    assert lib.sgemm_f32_streamk_workspace_size(64, 48, 64, 64, 48, 47, -1) == 0
+    assert lib.sgemm_f32_streamk_workspace_size(-1, 48, 64, 64, 48, 48, -1) == 0
+
+
+def test_plan_describe_validates_leading_dimensions():
+    lib = g.library()
+    buf = ctypes.create_string_buffer(1024)
+    assert lib.sgemm_f32_plan_describe(64, 48, 64, P, 63, P, 48, P, 48, 256, buf, 1024) == -2
+    assert lib.sgemm_f32_plan_describe(64, 48, 64, P, 64, P, 47, P, 48, 256, buf, 1024) == -2
+    assert lib.sgemm_f32_plan_describe(64, 48, 64, P, 64, P, 48, P, 40, 256, buf, 1024) == -2
+    assert lib.sgemm_f32_plan_describe(-1, 48, 64, P, 64, P, 48, P, 48, 256, buf, 1024) == -1
+    assert lib.sgemm_f32_plan_describe(64, 48, 64, P, 64, P, 48, P, 48, 256, buf, 1024) >= 0
 
 
 def _shapes(n, seed):

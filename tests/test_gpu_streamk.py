@@ -43,7 +43,7 @@ def run_streamk(torch, A, B, variant=-1, ldc=None, lda=None, ldb=None, ws_fill=f
     _, dA, lda = device_matrix(A, lda)
     _, dB, ldb = device_matrix(B, ldb)
     c = GuardedC(M, N, ldc)
-    ws_bytes = g.sgemm_f32_streamk_workspace_size(M, N, K, variant)
+    ws_bytes = g.sgemm_f32_streamk_workspace_size(M, N, K, lda, ldb, c.ldc, variant=variant)
     ws = torch.full((max(ws_bytes // 4, 1) + 64,), ws_fill, device="cuda")
     d = g.sgemm_f32_streamk_describe(M, N, K, variant)
     print(f"[streamk] {M}x{N}x{K} variant {variant} plan {d}", flush=True)
@@ -147,7 +147,7 @@ def test_streamk_edges(gpu):
     # a workspace smaller than the plan needs is refused before anything runs
     M, N, K = 1023, 1025, 1027
     v = shared_c3_variant()
-    need = g.sgemm_f32_streamk_workspace_size(M, N, K, v)
+    need = g.sgemm_f32_streamk_workspace_size(M, N, K, variant=v)
     assert need > 0
     big = torch.zeros(need // 4 + 64, device="cuda")
     _, dA, _ = device_matrix(np.ones((M, K), np.float32))

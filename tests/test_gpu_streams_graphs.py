@@ -50,7 +50,7 @@ def test_graph_capture_and_replay(gpu, M, N, K, kernel):
     if kernel == "streamk":
         # the 64 x 64 tile with two workgroups per CU shares tiles on both shapes
         sk_variant = g.variant_names().index("mfma_64x64x32_w2x1_kg2_dl")
-        ws_bytes = g.sgemm_f32_streamk_workspace_size(M, N, K, sk_variant)
+        ws_bytes = g.sgemm_f32_streamk_workspace_size(M, N, K, variant=sk_variant)
         assert ws_bytes > 0 and g.sgemm_f32_streamk_describe(M, N, K, sk_variant)["streamk"]
         ws = torch.empty(ws_bytes // 4, device="cuda")
     args = (M, N, K, dA.data_ptr(), max(K, 1), dB.data_ptr(), N, dC.data_ptr(), N)
