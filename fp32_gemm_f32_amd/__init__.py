@@ -11,6 +11,8 @@ Raw layer (same names and arguments as the C ABI; pointers are integers):
     sgemm_f32_splitk_workspace_size(M, N, K, splits) -> int
     sgemm_f32_streamk(..., variant, workspace, workspace_bytes, stream=0)
     sgemm_f32_streamk_workspace_size(M, N, K, lda, ldb, ldc, variant=-1) -> int
+    sgemm_f32_streamk_noalloc(..., variant, stream=0)
+    sgemm_f32_streamk_noalloc_scratch_bytes() -> int
     sgemm_f32_streamk_describe(M, N, K, variant=-1, num_cus=0) -> dict
     sgemm_f32_regtiled(..., tm=4, tn=4, stream=0)
     sgemm_f32_lds_transpose(rows, cols, src, ldi, dst, ldo, tile=32, pad=0, stream=0)
@@ -33,7 +35,7 @@ LIB_PATH = os.path.join(_PKG, "libsgemm_f32.so")
 SGEMM_OK = 0
 STATUS_NAMES = {0: "SGEMM_OK", -1: "SGEMM_EINVAL_DIM", -2: "SGEMM_EINVAL_LD",
                 -3: "SGEMM_EINVAL_PTR", -4: "SGEMM_EALIAS", -5: "SGEMM_ELAUNCH",
-                -6: "SGEMM_EINVAL_ARG", -7: "SGEMM_ETOO_LARGE"}
+                -6: "SGEMM_EINVAL_ARG", -7: "SGEMM_ETOO_LARGE", -8: "SGEMM_ESCRATCH"}
 
 _lib = None
 
@@ -68,6 +70,10 @@ def _load():
         lib.sgemm_f32_streamk.restype = i
         lib.sgemm_f32_streamk_workspace_size.argtypes = [i, i, i, i, i, i, i]
         lib.sgemm_f32_streamk_workspace_size.restype = ctypes.c_size_t
+        lib.sgemm_f32_streamk_noalloc.argtypes = gemm + [i, p]
+        lib.sgemm_f32_streamk_noalloc.restype = i
+        lib.sgemm_f32_streamk_noalloc_scratch_bytes.argtypes = []
+        lib.sgemm_f32_streamk_noalloc_scratch_bytes.restype = ctypes.c_size_t
         lib.sgemm_f32_streamk_describe.argtypes = [i, i, i, i, i, ctypes.c_char_p, i]
         lib.sgemm_f32_streamk_describe.restype = i
         lib.sgemm_f32_regtiled.argtypes = gemm + [i, i, p]
@@ -140,6 +146,15 @@ def sgemm_f32_streamk_workspace_size(M, N, K, lda=None, ldb=None, ldc=None, vari
     ldb = N if ldb is None else ldb
     ldc = N if ldc is None else ldc
     return _load().sgemm_f32_streamk_workspace_size(M, N, K, lda, ldb, ldc, variant)
+
+
+def sgemm_f32_streamk_noalloc(M, N, K, A, lda, B, ldb, C, ldc, variant=-1, stream=0) -> None:
+    _check(_load().sgemm_f32_streamk_noalloc(M, N, K, A, lda, B, ldb, C, ldc, variant,
+                                             stream or None), "sgemm_f32_streamk_noalloc")
+
+
+def sgemm_f32_streamk_noalloc_scratch_bytes() -> int:
+    return _load().sgemm_f32_streamk_noalloc_scratch_bytes()
 
 
 def sgemm_f32_streamk_describe(M, N, K, variant=-1, num_cus=0) -> dict:

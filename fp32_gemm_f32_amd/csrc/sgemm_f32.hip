@@ -8,6 +8,7 @@
 
 #include <atomic>
 #include <cstdint>
+#include <mutex>
 #include <cstdio>
 #include <cstring>
 #include <algorithm>
@@ -424,6 +425,48 @@ int run_hot(int variant, int M, int N, int K, const float *A, int lda, const flo
 }  // namespace
 }  // namespace sgemm
 
+// ------------------------------------------------------------------ static scratch --------
+// The partial tiles of sgemm_f32_streamk_noalloc live in this file-scope device array
+// instead of a caller's workspace. Each GPU the library runs on holds its own copy, for as
+// long as the process lives. In host code `scratch` names a host-side stand-in, not the
+// device memory: host code takes the array's device address from hipGetSymbolAddress
+// (device_scratch below) and passes that to the kernels.
+namespace sgemm {
+constexpr size_t kScratchBytes = size_t(64) << 20;
+}
+static __device__ __align__(256) float scratch[sgemm::kScratchBytes / 4];
+
+namespace sgemm {
+namespace {
+
+std::mutex g_scratch_mutex;
+std::atomic<float *> g_scratch[64];
+
+// Device address of the current device's scratch array, looked up once per device (with
+// that device current) and kept; devices past the table's end look it up on every call.
+int device_scratch(float **out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return SGEMM_ELAUNCH;
+    float *p = dev < 64 ? g_scratch[dev].load(std::memory_order_acquire) : nullptr;
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        if (dev < 64) p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            void *addr = nullptr;
+            if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || addr == nullptr)
+                return SGEMM_ELAUNCH;
+            p = static_cast<float *>(addr);
+            if (dev < 64) g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return SGEMM_OK;
+}
+
+}  // namespace
+}  // namespace sgemm
+
 using namespace sgemm;
 
 extern "C" int sgemm_f32(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
@@ -528,6 +571,35 @@ extern "C" int sgemm_f32_streamk(int M, int N, int K, const float *A, int lda, c
     if (!sk) return run_variant(vi, o, A, B, C, stream);
     return run_streamk(vi, o, A, B, C, workspace, workspace_bytes, stream, cus);
 }
+
+extern "C" int sgemm_f32_streamk_noalloc(int M, int N, int K, const float *A, int lda,
+                                         const float *B, int ldb, float *C, int ldc, int variant,
+                                         void *stream)
+{
+    const int st = validate(M, N, K, A, lda, B, ldb, C, ldc);
+    if (st != SGEMM_OK) return st;
+    if (variant >= kNumVariants || (variant >= 0 && !kVariants[variant].kern_sk))
+        return SGEMM_EINVAL_ARG;
+    if (M == 0 || N == 0) return SGEMM_OK;
+    if (K == 0) return fill_zero(M, N, C, ldc, stream);
+    const Operands o = make_operands(M, N, K, lda, ldb, ldc);
+    int cus = 0;
+    const int qs = device_cus(&cus);
+    if (qs != SGEMM_OK) return qs;
+    bool sk = false;
+    const int vi = plan_streamk(variant < 0 ? -1 : variant, o, cus, &sk);
+    if (vi < 0) return vi;
+    if (!sk) return run_variant(vi, o, A, B, C, stream);
+    const Variant &v = kVariants[vi].v;
+    if (streamk_workspace_bytes(v, streamk_geometry(v, o, cus)) > kScratchBytes)
+        return SGEMM_ESCRATCH;
+    float *W = nullptr;
+    const int ss = device_scratch(&W);
+    if (ss != SGEMM_OK) return ss;
+    return run_streamk(vi, o, A, B, C, W, kScratchBytes, stream, cus);
+}
+
+extern "C" size_t sgemm_f32_streamk_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 extern "C" int sgemm_f32_streamk_describe(int M, int N, int K, int variant, int num_cus,
                                           char *buf, int buflen)
@@ -723,6 +795,8 @@ extern "C" const char *sgemm_f32_status_string(int status)
     case SGEMM_ELAUNCH: return "HIP runtime error (launch or device query)";
     case SGEMM_EINVAL_ARG: return "invalid option argument";
     case SGEMM_ETOO_LARGE: return "shape too large for the selected kernel";
+    case SGEMM_ESCRATCH:
+        return "the plan's partial tiles exceed the library's static scratch (64 MiB per GPU)";
     default: return "unknown status";
     }
 }

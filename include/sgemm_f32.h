@@ -48,7 +48,9 @@ typedef enum {
     SGEMM_EALIAS = -4,       /* C overlaps A or B                                        */
     SGEMM_ELAUNCH = -5,      /* the HIP runtime refused a launch or device query         */
     SGEMM_EINVAL_ARG = -6,   /* an option argument (tile, pad, variant, buffer) is invalid */
-    SGEMM_ETOO_LARGE = -7    /* the shape exceeds what the chosen kernel can address     */
+    SGEMM_ETOO_LARGE = -7,   /* the shape exceeds what the chosen kernel can address     */
+    SGEMM_ESCRATCH = -8      /* sgemm_f32_streamk_noalloc: the plan's partial tiles exceed
+                                the library's static scratch                             */
 } sgemm_status;
 
 /*
@@ -129,6 +131,35 @@ int sgemm_f32_streamk(int M, int N, int K,
  * dimensions that sgemm_f32_streamk would reject, or on a bad variant. */
 size_t sgemm_f32_streamk_workspace_size(int M, int N, int K, int lda, int ldb, int ldc,
                                         int variant);
+
+/*
+ * sgemm_f32_streamk for callers that cannot allocate device memory: code being captured
+ * into a HIP graph, tight serving loops, and harnesses that forbid allocation. It takes no
+ * workspace. The partial tiles go to a static scratch array that the library holds on
+ * each GPU it runs on until the process ends. Its size is
+ * sgemm_f32_streamk_noalloc_scratch_bytes(), 64 MiB. The function calls no allocator: no
+ * hipMalloc, no hipFree, no allocating library routine.
+ *
+ * Arguments, plan, kernels and results are those of sgemm_f32_streamk with the same
+ * variant, so the two give identical bits. A plan whose partial tiles need more scratch
+ * than that returns SGEMM_ESCRATCH before any launch. That needs 2 x the workgroup count
+ * x one tile of floats above 64 MiB: 256 x 256 tiles, or 128 x 256 tiles at two per CU.
+ *
+ * Every call on one GPU shares that GPU's scratch, which keeps the last call's partial
+ * tiles. Nothing in it needs to start at zero: each slot is written before it is read.
+ * Calls that overlap in time on one GPU race on it: different streams, or host threads
+ * that are not synchronised. Such calls give wrong results. Calls on one stream are
+ * ordered and safe.
+ */
+int sgemm_f32_streamk_noalloc(int M, int N, int K,
+                              const float *A, int lda,
+                              const float *B, int ldb,
+                              float *C, int ldc,
+                              int variant,
+                              void *stream);
+
+/* Bytes of the static scratch behind sgemm_f32_streamk_noalloc (per GPU). */
+size_t sgemm_f32_streamk_noalloc_scratch_bytes(void);
 
 /*
  * Writes a one-line JSON description of sgemm_f32_streamk's plan for packed operands of

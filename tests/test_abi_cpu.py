@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
 def test_abi_version_and_status_strings():
     assert g.abi_version() == 2
     lib = g.library()
-    for code in range(-7, 1):
+    for code in range(-8, 1):
         s = lib.sgemm_f32_status_string(code).decode()
         assert s and s != "unknown status"
     assert lib.sgemm_f32_status_string(-99).decode() == "unknown status"
@@ -188,6 +188,29 @@ def test_streamk_validation():
     # empty output: nothing to do, before any device query
     assert lib.sgemm_f32_streamk(0, 48, 64, P, 64, P + 4096, 48, P + 8192, 48, -1, ws, 64,
                                  None) == 0
+
+
+def test_streamk_noalloc_validation():
+    """The no-allocation stream-K entry point validates like sgemm_f32_streamk, before any
+    HIP call, and reports its fixed scratch size."""
+    lib = g.library()
+    assert lib.sgemm_f32_streamk_noalloc_scratch_bytes() == 64 << 20
+    n = lib.sgemm_f32_variant_count()
+    args = (64, 48, 4096, P, 4096, P + (1 << 26), 48, P + (1 << 27), 48)
+    assert lib.sgemm_f32_streamk_noalloc(*args, n, None) == -6              # no such variant
+    for i in [i for i in range(n) if i not in g.streamk_variants()]:      # no stream-K form
+        assert lib.sgemm_f32_streamk_noalloc(*args, i, None) == -6
+    assert lib.sgemm_f32_streamk_noalloc(-1, 48, 64, P, 64, P + 4096, 48, P + 8192, 48, -1,
+                                         None) == -1
+    assert lib.sgemm_f32_streamk_noalloc(64, 48, 64, P, 63, P + 4096, 48, P + 8192, 48, -1,
+                                         None) == -2
+    assert lib.sgemm_f32_streamk_noalloc(64, 48, 64, 0, 64, P + 4096, 48, P + 8192, 48, -1,
+                                         None) == -3
+    assert lib.sgemm_f32_streamk_noalloc(64, 48, 64, P, 64, P + 4096, 48, P + 64, 48, -1,
+                                         None) == -4                        # C overlaps A
+    assert lib.sgemm_f32_streamk_noalloc(0, 48, 64, P, 64, P + 4096, 48, P + 8192, 48, -1,
+                                         None) == 0
+    assert lib.sgemm_f32_status_string(-8).decode().startswith("the plan's partial tiles")
 
 
 def test_workspace_queries_validate_leading_dimensions():
