@@ -53,6 +53,13 @@ def _load():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built: run `python -m fp32_gemm_f32_amd.build` "
                                "(or __graft_entry__.build()) first")
+        # torch carries its own HIP runtime under the same soname as the system's. Loaded
+        # first, it is the one the library binds to; loaded after the library, it would be a
+        # second runtime in the process, and the library's own would see no device.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         lib = ctypes.CDLL(LIB_PATH)
         i, p = ctypes.c_int, ctypes.c_void_p
         gemm = [i, i, i, p, i, p, i, p, i]

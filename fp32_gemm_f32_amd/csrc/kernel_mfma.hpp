@@ -116,7 +116,16 @@ struct GemmArgs {
     // 2 * sk.G partial tiles of BM x BN floats.
     SkGeom sk;
     float *W;
+    // Column strip (plain kernels only): when strip_wgs > 0, the tiles cover columns
+    // [0, strip_n0) and workgroups 0 .. strip_wgs - 1 compute the last N - strip_n0 (1 to
+    // kStripCols) columns, kStripRows rows each, on the vector ALUs; tile t is workgroup
+    // strip_wgs + t. strip_wgs is a multiple of the XCD count, so each tile keeps its XCD.
+    int strip_n0;
+    int strip_wgs;
 };
+
+// Most columns a strip may hold: a thin remainder of N past the last whole tile column.
+constexpr int kStripCols = 4;
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const float *base, int64_t bytes)
 {
@@ -186,9 +195,10 @@ __device__ inline void store_vec(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32
 // A vector store wider than 64 bits reads its data registers after it issues; a VALU
 // write to those registers right behind it corrupts lanes of the stored data on gfx950
 // (measured: the last four lanes of each 16-lane quarter). The compiler's hazard model
-// skips stores whose soffset is an SGPR, as every epilogue store here is, so kernels whose
-// register pressure lets it reuse a store's data registers immediately (the stream-K
-// forms) pin two wait states behind each store.
+// skips stores whose soffset is an SGPR, as every epilogue store here is, so every kernel
+// whose epilogue stores 16 bytes at a time pins two wait states behind each such store
+// (the register allocator reuses a store's data registers immediately in the stream-K
+// forms, and in the plain forms of the 4-wide column-interleaved tiles).
 template <bool GUARD>
 __device__ inline void store_data_guard()
 {
@@ -291,6 +301,126 @@ template <> struct MfmaShape<16> {
     static constexpr int row(int v) { return v; }
 };
 
+// The column strip: C[r][n] = sum_k A[r][k] B[k][n] for the last R = N - strip_n0 columns
+// (1 <= R <= kStripCols). A tile column holding so few columns would waste most of its MFMA
+// blocks and put a whole tile's time on each compute unit it runs on, so the strip's dot
+// products run on the vector ALUs, in workgroups of their own that share compute units
+// with the tiles. Strip workgroup s computes rows [8 s, 8 s + 8), two per wave.
+//  * K is walked in groups of 2048 values: the group's B values of the strip's columns are
+//    staged in LDS once for the four waves, then each lane takes k = 4 l .. 4 l + 3 of each
+//    of the group's eight chunks of 256 and reads them from each of its wave's rows with one
+//    16-byte load (consecutive lanes, consecutive addresses). All 16 of a group's A loads
+//    are issued before the first is used (chunks past K load nothing), so a group costs
+//    about one memory latency.
+//  * With a long K the strip workgroups first sleep about 2 us: the tiles beside them load
+//    their first panels meanwhile, which the strip's loads would otherwise delay, and the
+//    strip still ends long before the tiles do.
+//  * A lane's partial sums are added over the 64 lanes by a fixed butterfly, so the result
+//    does not vary between runs.
+constexpr int kStripWaveRows = 2;
+constexpr int kStripRows = 4 * kStripWaveRows;     // rows per strip workgroup (four waves)
+constexpr int kStripChunks = 8;                    // chunks of 256 values of k per group
+
+template <int CW>
+__device__ inline void column_strip_cw(const GemmArgs &p, int s, float *bs)
+{
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int M = p.M, K = p.K, lda = p.lda, ldb = p.ldb;
+    const int n0 = p.strip_n0, R = p.N - n0;
+    const int r0 = s * kStripRows + wave * kStripWaveRows;   // this wave's first row
+    const int64_t ea = int64_t(r0 < M ? r0 : 0) * lda;
+    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(p.A + ea, p.a_bytes - ea * 4);
+    float acc[kStripWaveRows][CW];
+#pragma unroll
+    for (int i = 0; i < kStripWaveRows; ++i)
+#pragma unroll
+        for (int c = 0; c < CW; ++c) acc[i][c] = 0.0f;
+    constexpr int GROUP = 256 * kStripChunks;
+    if (K >= 1024) __builtin_amdgcn_s_sleep(64);
+#pragma unroll 1
+    for (int kg0 = 0; kg0 < K; kg0 += GROUP) {
+        // B rows kg0 .. kg0 + 2047 of the strip's columns into LDS, one row per thread per
+        // pass, from a resource rebased at row kg0 (offsets stay in 31 bits); rows past K
+        // and columns past N are zeros
+        __syncthreads();   // every wave is done with the previous group's values
+        const int64_t eb = int64_t(kg0) * ldb + n0;
+        const __amdgpu_buffer_rsrc_t rsb = make_rsrc(p.B + eb, p.b_bytes - eb * 4);
+#pragma unroll
+        for (int q = 0; q < GROUP / 256; ++q) {
+            const int row = tid + 256 * q;
+            const uint32_t off = kg0 + row < K ? uint32_t(row) * uint32_t(ldb) * 4u : kOob;
+            float v[CW];
+            if constexpr (CW == 1) {
+                v[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsb, off, 0, 0));
+            } else if constexpr (CW == 2) {
+                const f32x2 w = __builtin_bit_cast(
+                    f32x2, __builtin_amdgcn_raw_buffer_load_b64(rsb, off, 0, 0));
+                v[0] = w[0]; v[1] = w[1];
+            } else {
+                const f32x4 w = load_b128(rsb, off);
+#pragma unroll
+                for (int c = 0; c < CW; ++c) v[c] = w[c];
+            }
+#pragma unroll
+            for (int c = 0; c < CW; ++c) bs[row * CW + c] = c < R ? v[c] : 0.0f;
+        }
+        // A: every row of this wave, every chunk of the group, all in flight together; rows
+        // past M read zeros (kOob), values past K are replaced by zeros below
+        f32x4 a[kStripChunks][kStripWaveRows];
+#pragma unroll
+        for (int j = 0; j < kStripChunks; ++j)
+#pragma unroll
+            for (int i = 0; i < kStripWaveRows; ++i) {
+                const int k = kg0 + 256 * j + 4 * lane;
+                const uint32_t off = r0 + i < M && k < K
+                                         ? (uint32_t(i) * uint32_t(lda) + uint32_t(k)) * 4u
+                                         : kOob;
+                a[j][i] = load_b128(rsa, off);
+            }
+        __syncthreads();   // the group's B values are in LDS
+#pragma unroll
+        for (int j = 0; j < kStripChunks; ++j) {
+            const int k = kg0 + 256 * j + 4 * lane;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float *brow = bs + (256 * j + 4 * lane + e) * CW;
+                float b[CW];
+#pragma unroll
+                for (int c = 0; c < CW; ++c) b[c] = brow[c];
+#pragma unroll
+                for (int i = 0; i < kStripWaveRows; ++i) {
+                    const float x = k + e < K ? a[j][i][e] : 0.0f;
+#pragma unroll
+                    for (int c = 0; c < CW; ++c) acc[i][c] += x * b[c];
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kStripWaveRows; ++i)
+#pragma unroll
+        for (int c = 0; c < CW; ++c) {
+            float v = acc[i][c];
+#pragma unroll
+            for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+            if (lane == c && r0 + i < M && c < R)
+                p.C[int64_t(r0 + i) * p.ldc + n0 + c] = v;
+        }
+}
+
+// Strip workgroup s (of the kernel's 256 threads) in the narrowest register form that holds
+// the strip's columns; bs is LDS for 2048 rows of them.
+__device__ inline void column_strip(const GemmArgs &p, int s, float *bs)
+{
+    if (s * kStripRows >= p.M) return;   // a workgroup of the rounding to whole XCDs
+    const int R = p.N - p.strip_n0;
+    if (R == 1) column_strip_cw<1>(p, s, bs);
+    else if (R == 2) column_strip_cw<2>(p, s, bs);
+    else column_strip_cw<kStripCols>(p, s, bs);
+}
+
 template <int BM, int BN, int BK, int WGM, int WGN, int KACC = 1, int KG = 1, int MB = 32>
 struct MfmaTile {
     static constexpr int kGroupThreads = 64 * WGM * WGN;   // one K-group of waves
@@ -354,6 +484,21 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
 
     __shared__ __attribute__((aligned(16))) float lds_all[T::LDS_FLOATS];
 
+    // the first strip_wgs workgroups compute the column strip (they go first, so that they
+    // run beside the first tiles); the tiles follow
+    int bid = blockIdx.x;
+    if constexpr (!SK) {
+        static_assert(64 * WGM * WGN * KG != 256 || T::LDS_FLOATS >= 256 * kStripChunks * kStripCols,
+                      "the strip's B values fit in LDS");
+        if (p.strip_wgs > 0) {
+            if (bid < p.strip_wgs) {
+                if constexpr (64 * WGM * WGN * KG == 256) column_strip(p, bid, lds_all);
+                return;
+            }
+            bid -= p.strip_wgs;
+        }
+    }
+
     // K-group of this wave: uniform across the wave (NT is a multiple of 64), which the
     // compiler must be told, or every buffer load's resource looks divergent
     const int kg = KG == 1 ? 0 : __builtin_amdgcn_readfirstlane(int(threadIdx.x) / NT);
@@ -410,7 +555,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     bool sk_mode = false;
     if constexpr (!SK) {
         int tm, tn;
-        const int item = blockIdx.x;
+        const int item = bid;
         ls = item / ntiles;
         tile_coords(item - ls * ntiles, p.tiles_m, p.tiles_n, tm, tn);
         lm0 = __builtin_amdgcn_readfirstlane(tm * BM);
@@ -613,17 +758,21 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     constexpr int PER_WRITE = (NL + WS - 1) / WS;
     static_assert(LS + WS < STEPS, "loads and LDS writes of a panel need separate steps");
 
-    auto panel = [&](auto cur_tag, auto next_tag) {
+    // NS: the k-steps of the panel that run. A group's last panel runs only the k-groups
+    // (4 steps each) that hold values of k inside its range; every other panel runs all.
+    auto panel = [&](auto cur_tag, auto next_tag, auto ns_tag) {
         constexpr bool NEXT = decltype(next_tag)::value;
         constexpr int cur = decltype(cur_tag)::value;   // -1: the stage parity known at run time
+        constexpr int NS = decltype(ns_tag)::value;
+        static_assert(NS % 4 == 0 && NS <= STEPS && (NS == STEPS || !NEXT), "steps of a panel");
         const float *As = smem + (cur < 0 ? (panel_parity & 1) : cur) * SSTRIDE;
         const float *Bs = As + T::A_TILE;
         float *Anext = smem + ((cur < 0 ? (panel_parity & 1) : cur) ^ 1) * SSTRIDE;
-        static_for<0, STEPS>([&](auto tc) {
+        static_for<0, NS>([&](auto tc) {
             constexpr int t = decltype(tc)::value;
             constexpr int kb = t >> 2, s = t & 3;
-            constexpr bool next_b = t + 1 < STEPS;
-            constexpr bool next_a = s == 0 && kb + 1 < BK / (4 * S::KSTEP);
+            constexpr bool next_b = t + 1 < NS;
+            constexpr bool next_a = s == 0 && 4 * (kb + 1) < NS;
             constexpr int w0 = t - (STEPS - 1 - WS);            // write group of this step
             constexpr int l_first = t * PER_LOAD;
             constexpr int n_load = (NEXT && t < LS)
@@ -685,7 +834,33 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
         });
     };
 
-    static_assert(STEPS % KACC == 0, "accumulator sets divide the k-steps of a panel");
+    static_assert(STEPS % KACC == 0 && 4 % KACC == 0,
+                  "accumulator sets divide the k-steps of a k-group");
+
+    // The last panel of this group: panel index kg + (rounds - 1) KG of the item. Only its
+    // k-groups that reach into the K range run (none if the panel lies wholly past it, as
+    // the last panel of a group can when the panel count is not a multiple of KG); the
+    // values of k past the range in the k-groups that do run are zeros in LDS.
+    // Tiles above 128 x 128 skip only a panel wholly past the range: shorter copies of the
+    // panel next to their large accumulator sets made the compiler spill.
+    constexpr int KGROUPS = STEPS / 4;
+    constexpr bool TRIM = BM * BN <= 128 * 128;
+    using AllSteps = std::integral_constant<int, STEPS>;
+    auto last_panel = [&](auto cur_tag, int rounds) {
+        const int valid = lK - (kg + (rounds - 1) * KG) * BK;
+        const int nkg = valid <= 0 ? 0 : (valid + 4 * S::KSTEP - 1) / (4 * S::KSTEP);
+        if (!TRIM) {
+            if (nkg > 0) panel(cur_tag, std::false_type{}, AllSteps{});
+        } else if (nkg >= KGROUPS) {
+            panel(cur_tag, std::false_type{}, AllSteps{});
+        } else {
+            static_for<1, KGROUPS>([&](auto nc) {
+                constexpr int n = decltype(nc)::value;
+                if (nkg == n)
+                    panel(cur_tag, std::false_type{}, std::integral_constant<int, 4 * n>{});
+            });
+        }
+    };
 
     // ---- epilogue of one tile: accumulators to C through a buffer resource ----
     const int ldc = p.ldc;
@@ -765,7 +940,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
                     }
                     const bool ok = col_full && lrow + dr < rows_left;
                     store_vec<CI, POLICY>(rsc, ok ? vbase : kOob, uint32_t(dr) * ldc4, out);
-                    store_data_guard<SK && CI >= 4>();
+                    store_data_guard<CI >= 4>();
                 }
             }
         }
@@ -856,26 +1031,26 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
             int r = 0;
             for (; r + 2 < rounds; r += 2) {
                 set_panel(((r + 1) * KG + kg) * BK);
-                panel(S0{}, std::true_type{});
+                panel(S0{}, std::true_type{}, AllSteps{});
                 set_panel(((r + 2) * KG + kg) * BK);
-                panel(S1{}, std::true_type{});
+                panel(S1{}, std::true_type{}, AllSteps{});
             }
             if (r + 1 < rounds) {
                 set_panel(((r + 1) * KG + kg) * BK);
-                panel(S0{}, std::true_type{});
-                panel(S1{}, std::false_type{});
+                panel(S0{}, std::true_type{}, AllSteps{});
+                last_panel(S1{}, rounds);
             } else {
-                panel(S0{}, std::false_type{});
+                last_panel(S0{}, rounds);
             }
         } else {
             using SR = std::integral_constant<int, -1>;
             for (int r = 0; r + 1 < rounds; ++r) {
                 set_panel(((r + 1) * KG + kg) * BK);
                 panel_parity = r;
-                panel(SR{}, std::true_type{});
+                panel(SR{}, std::true_type{}, AllSteps{});
             }
             panel_parity = rounds - 1;
-            panel(SR{}, std::false_type{});
+            last_panel(SR{}, rounds);
         }
         finish();
         if (kg == 0) {

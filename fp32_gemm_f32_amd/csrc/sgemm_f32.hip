@@ -85,10 +85,12 @@ constexpr VariantEntry entry(const char *name, int wg_per_cu, double rate, doubl
         sk = &k_sgemm_mfma<BM, BN, BK, WGM, WGN, KACC, KG, DL, true, MB>;
         fix = &k_streamk_fixup<BM, BN>;
     }
-    return VariantEntry{
+    VariantEntry e{
         Variant{name, BM, BN, BK, WGM, WGN, wg_per_cu, rate, overhead, solo, DL, PLANNED},
         &k_sgemm_mfma<BM, BN, BK, WGM, WGN, KACC, KG, DL, false, MB>, sk, fix,
         64 * WGM * WGN * KG, MB, KG, "mfma"};
+    e.v.strip = wg_per_cu >= 2 && 64 * WGM * WGN * KG == 256;
+    return e;
 }
 
 // The one-wave-per-SIMD kernel (kernel_regpanel.hpp): 256 x 256 tiles of four 128 x 128
@@ -185,9 +187,13 @@ int device_cus(int *out)
     return SGEMM_OK;
 }
 
-// Kernel arguments of the plain product with variant e.
+static_assert(kStripCols == kStripColsMax && kStripRows == kStripRowsPlan,
+              "strip geometry of the kernels and of the plan");
+
+// Kernel arguments of the plain product with variant e; with `cus` > 0, a thin remainder of
+// N goes to strip workgroups when the plan prices that lower (strip_cols).
 GemmArgs plain_args(const VariantEntry &e, const Operands &o, const float *A, const float *B,
-                    float *C)
+                    float *C, int cus = 0)
 {
     GemmArgs p{};
     p.A = A; p.B = B; p.C = C;
@@ -195,11 +201,14 @@ GemmArgs plain_args(const VariantEntry &e, const Operands &o, const float *A, co
     p.b_bytes = span_elems(o.K, o.N, o.ldb) * 4;
     p.c_bytes = span_elems(o.M, o.N, o.ldc) * 4;
     p.M = o.M; p.N = o.N; p.K = o.K; p.lda = o.lda; p.ldb = o.ldb; p.ldc = o.ldc;
+    const int r = cus > 0 ? strip_cols(e.v, o, cus) : 0;
     p.tiles_m = (o.M + e.v.BM - 1) / e.v.BM;
-    p.tiles_n = (o.N + e.v.BN - 1) / e.v.BN;
+    p.tiles_n = (o.N - r + e.v.BN - 1) / e.v.BN;
     p.splits = 1;
     p.k_chunk = o.K;
     p.c_split_stride = 0;
+    p.strip_n0 = o.N - r;
+    p.strip_wgs = r > 0 ? strip_wgs(o.M) : 0;
     return p;
 }
 
@@ -303,10 +312,13 @@ int run_variant(int vi, const Operands &o, const float *A, const float *B, float
 {
     const VariantEntry &e = kVariants[vi];
     if (e.persistent) return run_persistent(e, o, A, B, C, stream);
-    const GemmArgs p = plain_args(e, o, A, B, C);
-    const int64_t tiles = int64_t(p.tiles_m) * p.tiles_n;
-    if (tiles > INT32_MAX) return SGEMM_ETOO_LARGE;
-    return launch(e.kern, dim3(unsigned(tiles)), dim3(e.threads), stream, p);
+    int cus = 0;
+    const int qs = device_cus(&cus);
+    if (qs != SGEMM_OK) return qs;
+    const GemmArgs p = plain_args(e, o, A, B, C, cus);
+    const int64_t grid = int64_t(p.tiles_m) * p.tiles_n + p.strip_wgs;
+    if (grid > INT32_MAX) return SGEMM_ETOO_LARGE;
+    return launch(e.kern, dim3(unsigned(grid)), dim3(e.threads), stream, p);
 }
 
 // Split-K geometry: K is cut into `splits` ranges of whole BK panels (the last may be
@@ -774,12 +786,13 @@ extern "C" int sgemm_f32_variant_info(int variant, char *buf, int buflen)
                            "\"direct_loads\": %s, \"planned\": %s, \"streamk\": %s, "
                            "\"rate\": %.3f, \"overhead\": %.1f, \"solo\": %.2f, "
                            "\"kernel\": \"%s\", \"splitk\": %s, \"persistent\": %s, "
-                           "\"whole_tiles\": %s}",
+                           "\"whole_tiles\": %s, \"strip\": %s}",
                            variant, v.name, v.BM, v.BN, v.BK, v.wgm, v.wgn, e.kg, e.threads, e.mb,
                            e.mb, e.mb == 32 ? 2 : 4, v.wg_per_cu, v.direct ? "true" : "false",
                            v.planned ? "true" : "false", e.kern_sk ? "true" : "false", v.rate,
                            v.overhead, v.solo, e.kernel, v.splitk ? "true" : "false",
-                           e.persistent ? "true" : "false", v.whole_tiles ? "true" : "false");
+                           e.persistent ? "true" : "false", v.whole_tiles ? "true" : "false",
+                           v.strip ? "true" : "false");
     if (n < 0 || n >= buflen) return SGEMM_EINVAL_ARG;
     return SGEMM_OK;
 }
@@ -818,9 +831,13 @@ extern "C" int sgemm_f32_plan_describe(int M, int N, int K, const float *A, int 
     const int vi = choose_variant(g_table, o, cus);
     if (vi < 0) return SGEMM_ETOO_LARGE;
     const Variant &v = kVariants[vi].v;
-    const int64_t tm = (int64_t(M) + v.BM - 1) / v.BM, tn = (int64_t(N) + v.BN - 1) / v.BN;
-    // one workgroup per tile, or for the persistent variant one per CU over its tiles
-    const int64_t grid = kVariants[vi].persistent ? std::min<int64_t>(tm * tn, cus) : tm * tn;
+    const int strip = kVariants[vi].persistent ? 0 : strip_cols(v, o, cus);
+    const int64_t tm = (int64_t(M) + v.BM - 1) / v.BM,
+                  tn = (int64_t(N) - strip + v.BN - 1) / v.BN;
+    // one workgroup per tile (and per strip row block), or for the persistent variant one
+    // per CU over its tiles
+    const int64_t grid = kVariants[vi].persistent ? std::min<int64_t>(tm * tn, cus)
+                                                  : tm * tn + (strip ? strip_wgs(M) : 0);
     // operand bytes the tiles request: every A row panel once per tile column and every
     // B column panel once per tile row (before any cache reuse)
     const int64_t tile_bytes = 4 * (int64_t(M) * K * tn + int64_t(K) * N * tm);
@@ -828,10 +845,12 @@ extern "C" int sgemm_f32_plan_describe(int M, int N, int K, const float *A, int 
                            "{\"variant\": %d, \"name\": \"%s\", \"BM\": %d, \"BN\": %d, "
                            "\"BK\": %d, \"waves\": [%d, %d], \"threads\": %d, \"grid\": %lld, "
                            "\"tiles\": [%lld, %lld], \"cus\": %d, \"wg_per_cu\": %d, "
-                           "\"direct_loads\": %s, \"tile_request_bytes\": %lld}",
+                           "\"direct_loads\": %s, \"tile_request_bytes\": %lld, "
+                           "\"strip_cols\": %d, \"strip_wgs\": %lld}",
                            vi, v.name, v.BM, v.BN, v.BK, v.wgm, v.wgn, kVariants[vi].threads,
                            (long long)grid, (long long)tm, (long long)tn, cus, v.wg_per_cu,
-                           v.direct ? "true" : "false", (long long)tile_bytes);
+                           v.direct ? "true" : "false", (long long)tile_bytes, strip,
+                           (long long)(strip ? strip_wgs(M) : 0));
     if (n < 0 || n >= buflen) return SGEMM_EINVAL_ARG;
     return vi;
 }

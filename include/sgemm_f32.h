@@ -57,8 +57,10 @@ typedef enum {
  * The hot path: the LDS-tiled, register-tiled matrix-core kernel ("SGEMM: 2D Register
  * Tiling Visualizer", "Why 2D Register Tiling Dominates", carried onto the FP32 MFMA
  * instructions), with tiles zero-filled past the edges of ragged shapes. The tile shape
- * is chosen per (M, N, K) and compute-unit count; any 4-byte aligned pointers and any
- * leading dimensions work. Leading dimensions so large that 256 rows of A or C (or 32
+ * is chosen per (M, N, K) and compute-unit count; when N leaves 1 to 4 columns past the
+ * last whole tile column, those columns may be computed in the same launch by workgroups
+ * on the vector ALUs instead of a nearly empty column of tiles. Any 4-byte aligned
+ * pointers and any leading dimensions work. Leading dimensions so large that 256 rows of A or C (or 32
  * rows of B) exceed 2^31 bytes return SGEMM_ETOO_LARGE.
  */
 int sgemm_f32(int M, int N, int K,
@@ -264,8 +266,10 @@ const char *sgemm_f32_variant_name(int variant);
  * form, the plan's cost-model parameters (rate, overhead, solo) for it, the kernel family
  * ("mfma": the LDS-double-buffered template; "regpanel": the one-wave-per-SIMD kernel;
  * "persist": the persistent kernel), whether split-K may use it, whether it runs one
- * workgroup per CU over the tiles ("persistent") and whether it only takes whole tiles
- * ("whole_tiles"). Host-only, no GPU needed. Returns SGEMM_OK, or
+ * workgroup per CU over the tiles ("persistent"), whether it only takes whole tiles
+ * ("whole_tiles") and whether a thin remainder of N (1 to 4 columns past the last whole
+ * tile column) goes to strip workgroups on the vector ALUs ("strip"). Host-only, no GPU
+ * needed. Returns SGEMM_OK, or
  * SGEMM_EINVAL_ARG for a bad index or a buffer too small.
  */
 int sgemm_f32_variant_info(int variant, char *buf, int buflen);

@@ -102,10 +102,22 @@ def test_plan(shape, expect_tile):
                                      num_cus=256)
     tiles = plan["tiles"][0] * plan["tiles"][1]
     info = g.sgemm_f32_variant_info(plan["variant"])
-    # one workgroup per tile, or one per CU walking the tiles
-    assert plan["grid"] == (min(tiles, 256) if info["persistent"] else tiles)
+    # one workgroup per tile (plus one per tile row for a column strip), or one per CU
+    # walking the tiles
+    assert plan["grid"] == (min(tiles, 256) if info["persistent"]
+                            else tiles + plan["strip_wgs"])
     assert plan["direct_loads"] == plan["name"].endswith("_dl")
-    assert plan["tiles"][0] * plan["BM"] >= M and plan["tiles"][1] * plan["BN"] >= N
+    # the tiles cover C but for the strip's columns, which lie past whole tile columns
+    assert plan["tiles"][0] * plan["BM"] >= M
+    assert plan["tiles"][1] * plan["BN"] == N - plan["strip_cols"] or (
+        plan["strip_cols"] == 0 and plan["tiles"][1] * plan["BN"] >= N)
+    if plan["strip_cols"]:
+        assert info["strip"] and 1 <= plan["strip_cols"] <= 4
+        assert plan["strip_wgs"] == ((M + 7) // 8 + 7) // 8 * 8
+    if shape == (1023, 1025, 1027):
+        # the ragged workload: 256 whole 64 x 64 tiles and a one-column strip, instead of
+        # a 17th column of nearly empty tiles
+        assert plan["strip_cols"] == 1 and tiles == 256
     if expect_tile:
         assert plan["BM"] == plan["BN"] == expect_tile
     elif M * N >= 1 << 20:
@@ -316,3 +328,21 @@ def test_variant_info():
         g.sgemm_f32_variant_info(len(names))
     buf = ctypes.create_string_buffer(8)
     assert g.library().sgemm_f32_variant_info(0, buf, 8) == -6
+
+
+def test_one_hip_runtime_in_the_process():
+    """Loading the library first must not leave two HIP runtimes in the process: torch
+    carries its own under the system one's soname, and a second runtime sees no device.
+    In a fresh interpreter: load the library, then import torch, and count the distinct
+    libamdhip64 files mapped."""
+    import subprocess, sys
+    code = (
+        "import fp32_gemm_f32_amd as g; g.library(); import torch;"
+        "paths = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l};"
+        "print(len(paths), sorted(paths))")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                       cwd=ROOT, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    n = int(r.stdout.split()[0])
+    assert n == 1, r.stdout
+
