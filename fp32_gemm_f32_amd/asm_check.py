@@ -28,6 +28,12 @@ def _vgprs(tok: str) -> set[int]:
     return {int(m.group(1))} if m else set()
 
 
+def _data_operand(op: str) -> int:
+    """Position of the data registers among a store's operands: first for buffer stores
+    (vdata, vaddr, srsrc, soffset), second for global and flat stores (vaddr, vdata, ...)."""
+    return 1 if op.startswith("buffer_") else 2
+
+
 def store_data_hazards(asm: str, need: int = 2) -> dict[str, list[tuple[int, str, str]]]:
     """Kernel symbol -> [(wait states, store, writing instruction)] for every finding."""
     kernel, insts, hits = None, [], {}
@@ -47,7 +53,7 @@ def store_data_hazards(asm: str, need: int = 2) -> dict[str, list[tuple[int, str
                 if waits >= need:
                     break
                 p = prev.split()
-                if p[0].startswith(WIDE_STORES) and written & _vgprs(p[1].rstrip(",")):
+                if p[0].startswith(WIDE_STORES) and written & _vgprs(p[_data_operand(p[0])].rstrip(",")):
                     hits.setdefault(kernel, []).append((waits, prev, s))
                     break
                 waits += int(p[1]) + 1 if p[0] == "s_nop" else 1

@@ -89,6 +89,7 @@ constexpr int kXcds = 8;
 #define SGEMM_WRITE_STEPS 3
 #endif
 // Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedValu = 0x002;
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedVmemRead = 0x020;
 constexpr int kSchedDsRead = 0x100;
@@ -116,16 +117,15 @@ struct GemmArgs {
     // 2 * sk.G partial tiles of BM x BN floats.
     SkGeom sk;
     float *W;
-    // Column strip (plain kernels only): when strip_wgs > 0, the tiles cover columns
-    // [0, strip_n0) and workgroups 0 .. strip_wgs - 1 compute the last N - strip_n0 (1 to
-    // kStripCols) columns, kStripRows rows each, on the vector ALUs; tile t is workgroup
-    // strip_wgs + t. strip_wgs is a multiple of the XCD count, so each tile keeps its XCD.
+    // Column strip (plain kernels only): when strip_cols > 0, the tiles cover columns
+    // [0, strip_n0), and the workgroups of the last tile column also compute the
+    // strip_cols = N - strip_n0 (at most kStripCols) columns past it, on the vector ALUs.
     int strip_n0;
-    int strip_wgs;
+    int strip_cols;
 };
 
-// Most columns a strip may hold: a thin remainder of N past the last whole tile column.
-constexpr int kStripCols = 4;
+// Most columns a strip may hold: a one-column remainder of N past the last whole tile column.
+constexpr int kStripCols = 1;
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const float *base, int64_t bytes)
 {
@@ -301,126 +301,6 @@ template <> struct MfmaShape<16> {
     static constexpr int row(int v) { return v; }
 };
 
-// The column strip: C[r][n] = sum_k A[r][k] B[k][n] for the last R = N - strip_n0 columns
-// (1 <= R <= kStripCols). A tile column holding so few columns would waste most of its MFMA
-// blocks and put a whole tile's time on each compute unit it runs on, so the strip's dot
-// products run on the vector ALUs, in workgroups of their own that share compute units
-// with the tiles. Strip workgroup s computes rows [8 s, 8 s + 8), two per wave.
-//  * K is walked in groups of 2048 values: the group's B values of the strip's columns are
-//    staged in LDS once for the four waves, then each lane takes k = 4 l .. 4 l + 3 of each
-//    of the group's eight chunks of 256 and reads them from each of its wave's rows with one
-//    16-byte load (consecutive lanes, consecutive addresses). All 16 of a group's A loads
-//    are issued before the first is used (chunks past K load nothing), so a group costs
-//    about one memory latency.
-//  * With a long K the strip workgroups first sleep about 2 us: the tiles beside them load
-//    their first panels meanwhile, which the strip's loads would otherwise delay, and the
-//    strip still ends long before the tiles do.
-//  * A lane's partial sums are added over the 64 lanes by a fixed butterfly, so the result
-//    does not vary between runs.
-constexpr int kStripWaveRows = 2;
-constexpr int kStripRows = 4 * kStripWaveRows;     // rows per strip workgroup (four waves)
-constexpr int kStripChunks = 8;                    // chunks of 256 values of k per group
-
-template <int CW>
-__device__ inline void column_strip_cw(const GemmArgs &p, int s, float *bs)
-{
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int M = p.M, K = p.K, lda = p.lda, ldb = p.ldb;
-    const int n0 = p.strip_n0, R = p.N - n0;
-    const int r0 = s * kStripRows + wave * kStripWaveRows;   // this wave's first row
-    const int64_t ea = int64_t(r0 < M ? r0 : 0) * lda;
-    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(p.A + ea, p.a_bytes - ea * 4);
-    float acc[kStripWaveRows][CW];
-#pragma unroll
-    for (int i = 0; i < kStripWaveRows; ++i)
-#pragma unroll
-        for (int c = 0; c < CW; ++c) acc[i][c] = 0.0f;
-    constexpr int GROUP = 256 * kStripChunks;
-    if (K >= 1024) __builtin_amdgcn_s_sleep(64);
-#pragma unroll 1
-    for (int kg0 = 0; kg0 < K; kg0 += GROUP) {
-        // B rows kg0 .. kg0 + 2047 of the strip's columns into LDS, one row per thread per
-        // pass, from a resource rebased at row kg0 (offsets stay in 31 bits); rows past K
-        // and columns past N are zeros
-        __syncthreads();   // every wave is done with the previous group's values
-        const int64_t eb = int64_t(kg0) * ldb + n0;
-        const __amdgpu_buffer_rsrc_t rsb = make_rsrc(p.B + eb, p.b_bytes - eb * 4);
-#pragma unroll
-        for (int q = 0; q < GROUP / 256; ++q) {
-            const int row = tid + 256 * q;
-            const uint32_t off = kg0 + row < K ? uint32_t(row) * uint32_t(ldb) * 4u : kOob;
-            float v[CW];
-            if constexpr (CW == 1) {
-                v[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsb, off, 0, 0));
-            } else if constexpr (CW == 2) {
-                const f32x2 w = __builtin_bit_cast(
-                    f32x2, __builtin_amdgcn_raw_buffer_load_b64(rsb, off, 0, 0));
-                v[0] = w[0]; v[1] = w[1];
-            } else {
-                const f32x4 w = load_b128(rsb, off);
-#pragma unroll
-                for (int c = 0; c < CW; ++c) v[c] = w[c];
-            }
-#pragma unroll
-            for (int c = 0; c < CW; ++c) bs[row * CW + c] = c < R ? v[c] : 0.0f;
-        }
-        // A: every row of this wave, every chunk of the group, all in flight together; rows
-        // past M read zeros (kOob), values past K are replaced by zeros below
-        f32x4 a[kStripChunks][kStripWaveRows];
-#pragma unroll
-        for (int j = 0; j < kStripChunks; ++j)
-#pragma unroll
-            for (int i = 0; i < kStripWaveRows; ++i) {
-                const int k = kg0 + 256 * j + 4 * lane;
-                const uint32_t off = r0 + i < M && k < K
-                                         ? (uint32_t(i) * uint32_t(lda) + uint32_t(k)) * 4u
-                                         : kOob;
-                a[j][i] = load_b128(rsa, off);
-            }
-        __syncthreads();   // the group's B values are in LDS
-#pragma unroll
-        for (int j = 0; j < kStripChunks; ++j) {
-            const int k = kg0 + 256 * j + 4 * lane;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float *brow = bs + (256 * j + 4 * lane + e) * CW;
-                float b[CW];
-#pragma unroll
-                for (int c = 0; c < CW; ++c) b[c] = brow[c];
-#pragma unroll
-                for (int i = 0; i < kStripWaveRows; ++i) {
-                    const float x = k + e < K ? a[j][i][e] : 0.0f;
-#pragma unroll
-                    for (int c = 0; c < CW; ++c) acc[i][c] += x * b[c];
-                }
-            }
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < kStripWaveRows; ++i)
-#pragma unroll
-        for (int c = 0; c < CW; ++c) {
-            float v = acc[i][c];
-#pragma unroll
-            for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-            if (lane == c && r0 + i < M && c < R)
-                p.C[int64_t(r0 + i) * p.ldc + n0 + c] = v;
-        }
-}
-
-// Strip workgroup s (of the kernel's 256 threads) in the narrowest register form that holds
-// the strip's columns; bs is LDS for 2048 rows of them.
-__device__ inline void column_strip(const GemmArgs &p, int s, float *bs)
-{
-    if (s * kStripRows >= p.M) return;   // a workgroup of the rounding to whole XCDs
-    const int R = p.N - p.strip_n0;
-    if (R == 1) column_strip_cw<1>(p, s, bs);
-    else if (R == 2) column_strip_cw<2>(p, s, bs);
-    else column_strip_cw<kStripCols>(p, s, bs);
-}
-
 template <int BM, int BN, int BK, int WGM, int WGN, int KACC = 1, int KG = 1, int MB = 32>
 struct MfmaTile {
     static constexpr int kGroupThreads = 64 * WGM * WGN;   // one K-group of waves
@@ -441,7 +321,18 @@ struct MfmaTile {
     // partial sums of K-groups 1 .. KG-1, handed to group 0 after the last panel; they reuse
     // the stages' memory
     static constexpr int RED = (KG - 1) * kGroupThreads * NACC * ACC;
-    static constexpr int LDS_FLOATS = 2 * KG * STAGE > RED ? 2 * KG * STAGE : RED;
+    // Column strip (see the kernel): per stage, 64 floats of the strip's B column (one per
+    // value of k of the panel), loaded with the panel; then a reduction area for the lanes'
+    // partial sums: one row of BM floats per K-group and MFMA lane group.
+    static constexpr int STRIP_STAGE = 64;
+    static constexpr int STRIP_FLOATS = 2 * KG * STRIP_STAGE + KG * MfmaShape<MB>::H * BM;
+    static constexpr bool STRIP_OK = BM <= kGroupThreads * KG && BK <= 64 &&
+                                     RED <= 2 * KG * STAGE &&
+                                     (2 * KG * STAGE + STRIP_FLOATS) * 4 <= 160 * 1024;
+    static constexpr int BASE_FLOATS = 2 * KG * STAGE > RED ? 2 * KG * STAGE : RED;
+    static constexpr int LDS_FLOATS =
+        STRIP_OK && 2 * KG * STAGE + STRIP_FLOATS > BASE_FLOATS ? 2 * KG * STAGE + STRIP_FLOATS
+                                                                 : BASE_FLOATS;
     static constexpr int LDS_BYTES = LDS_FLOATS * 4;
     static_assert(WM % MB == 0 && WN % MB == 0, "wave tile is made of MB x MB blocks");
     static_assert(WN % (MB * CI) == 0, "column groups");
@@ -483,21 +374,6 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     typedef typename fvec<CI>::type bvec;
 
     __shared__ __attribute__((aligned(16))) float lds_all[T::LDS_FLOATS];
-
-    // the first strip_wgs workgroups compute the column strip (they go first, so that they
-    // run beside the first tiles); the tiles follow
-    int bid = blockIdx.x;
-    if constexpr (!SK) {
-        static_assert(64 * WGM * WGN * KG != 256 || T::LDS_FLOATS >= 256 * kStripChunks * kStripCols,
-                      "the strip's B values fit in LDS");
-        if (p.strip_wgs > 0) {
-            if (bid < p.strip_wgs) {
-                if constexpr (64 * WGM * WGN * KG == 256) column_strip(p, bid, lds_all);
-                return;
-            }
-            bid -= p.strip_wgs;
-        }
-    }
 
     // K-group of this wave: uniform across the wave (NT is a multiple of 64), which the
     // compiler must be told, or every buffer load's resource looks divergent
@@ -555,7 +431,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     bool sk_mode = false;
     if constexpr (!SK) {
         int tm, tn;
-        const int item = bid;
+        const int item = blockIdx.x;
         ls = item / ntiles;
         tile_coords(item - ls * ntiles, p.tiles_m, p.tiles_n, tm, tn);
         lm0 = __builtin_amdgcn_readfirstlane(tm * BM);
@@ -593,7 +469,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     //    panel (BK + 1 rows cover every offset of a panel otherwise).
     uint32_t a_voff[A_CH], b_voff[B_CH];
     uint32_t a_end = 0u;
-    auto set_item = [&]() {
+    auto set_item = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int l = 0; l < A_CH; ++l)
             a_voff[l] = lm0 + a_r0 + l * A_RSTEP < M ? a_off0 + uint32_t(l) * a_stride : kOob;
@@ -609,7 +485,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     __amdgpu_buffer_rsrc_t rsa, rsb;   // resources rebased at the panel being staged
     int k_load = 0;
 
-    auto set_panel = [&](int k0) {
+    auto set_panel = [&](int k0) __attribute__((always_inline)) {
         k_load = k0;
         const int64_t ea = int64_t(lm0) * lda + lkb + k0, eb = int64_t(lkb + k0) * ldb + ln0;
         const int rows = lK - k0;
@@ -624,7 +500,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     // into the load, in the branch that a constant l rules out, makes the compiler drop the
     // kernel's host stub without a diagnostic; the build checks the library for undefined
     // symbols)
-    auto load_slot = [&](int l) {
+    auto load_slot = [&](int l) __attribute__((always_inline)) {
         if (l < A_CH) {
             const uint32_t off = a_voff[l];
             ra[l] = load_b128(rsa, off);
@@ -634,7 +510,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
             rb[i] = load_b128(rsb, off);
         }
     };
-    auto write_slot = [&](float *As, int l) {
+    auto write_slot = [&](float *As, int l) __attribute__((always_inline)) {
         if (l < A_CH) {
             // elements past the K range belong to the row padding, the next row or the next
             // split; zero them (a select, so a NaN there cannot leak). Done here, where the
@@ -658,7 +534,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     // this lane's A chunks (their LDS slots are 16 (tid + l NT) bytes into the A tile). The
     // branch is uniform and taken only in the panel that holds the end of the range (or,
     // with K-groups, lies past it).
-    auto fix_k_tail = [&](float *As) {
+    auto fix_k_tail = [&](float *As) __attribute__((always_inline)) {
         if (k_load + BK > lK) {
             const int kc = k_load + 4 * a_q;
             if (kc + 4 > lK) {
@@ -672,7 +548,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
             }
         }
     };
-    auto load_direct = [&](float *As, int l) {
+    auto load_direct = [&](float *As, int l) __attribute__((always_inline)) {
         if (l < A_CH) {
             const uint32_t off = a_voff[l];
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -758,16 +634,72 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     constexpr int PER_WRITE = (NL + WS - 1) / WS;
     static_assert(LS + WS < STEPS, "loads and LDS writes of a panel need separate steps");
 
+    // ---- column strip: the workgroups of the last tile column also compute the column of C
+    // past it (strip_cols = 1), instead of a column of tiles that would hold one valid
+    // column. The strip's B values of a panel (zeros past the K range) are loaded straight
+    // into LDS with the panel, stage s of group kg at strip_lds + (s KG + kg) STRIP_STAGE,
+    // value k of the panel at + k, by the group's first wave. The MFMA's A operands already
+    // hold, in each lane, four consecutive values of k of each of the lane's rows (k-group
+    // kb: 4 (H kb + hi) .. + 3); a lane multiplies them by the strip's four B values for
+    // those k (one 16-byte LDS read per k-group, the same address for all lanes of a lane
+    // group) into sacc, on the vector ALU between the MFMAs. Waves that differ only in wn
+    // hold the same rows, so only the wn = 0 waves' sums are used; after the last panel the
+    // lane groups and K-groups are added in a fixed order. (Vector work among the MFMAs
+    // costs the matrix pipe time on gfx950: the strip tiles run a few per cent longer than
+    // the others. Spreading the strip's rows over every tile of a row costs every tile
+    // about that much, which is worse once the tiles take more than one round.)
+    constexpr bool CAN_STRIP = !SK && DL && T::STRIP_OK;
+    float *const strip_lds = lds_all + 2 * KG * T::STAGE;
+    float *const strip_red = strip_lds + 2 * KG * T::STRIP_STAGE;
+    __amdgpu_buffer_rsrc_t rss;
+    uint32_t s_off = kOob;
+    float sacc[RB];
+    f32x4 sbv;   // the strip's B values of the current k-group
+    auto set_strip_item = [&]() __attribute__((always_inline)) {
+        s_off = lane < BK ? uint32_t(lane) * uint32_t(ldb) * 4u : kOob;
+#pragma unroll
+        for (int r = 0; r < RB; ++r) sacc[r] = 0.0f;
+    };
+    // the strip's B resource for the panel at k0 of the item: it ends at the last row of the
+    // K range (rows past it read zeros)
+    auto set_strip_panel = [&](int k0) __attribute__((always_inline)) {
+        const int rows = lK - k0;
+        const int64_t es = int64_t(lkb + k0) * ldb + p.strip_n0;
+        const uint32_t ns = rows > 0 ? uint32_t((min(rows, BK) - 1) * ldb + 1) * 4u : 0u;
+        rss = make_rsrc32(p.B + es, ns);
+    };
+    auto strip_load = [&](int stage) __attribute__((always_inline)) {
+        if (wave_u == 0) {
+            const uint32_t off = s_off;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rss, (lds_ptr)(strip_lds + (stage * KG + kg) * T::STRIP_STAGE), 4, off, 0, 0, 0);
+        }
+    };
+    // The empty asm after the products keeps them at this step: left alone, the compiler
+    // gathers the products of a whole panel at its end, with all their operands live.
+    auto strip_fma = [&](const f32x4 (&av)[RB]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sacc[r] += av[r][e] * sbv[e];
+            asm volatile("" : "+v"(sacc[r]));
+        }
+    };
+
     // NS: the k-steps of the panel that run. A group's last panel runs only the k-groups
     // (4 steps each) that hold values of k inside its range; every other panel runs all.
-    auto panel = [&](auto cur_tag, auto next_tag, auto ns_tag) {
+    // STRIP: the panel also loads the next panel's strip values and computes this one's.
+    auto panel = [&](auto cur_tag, auto next_tag, auto ns_tag, auto strip_tag) __attribute__((always_inline)) {
+        constexpr bool STRIP = decltype(strip_tag)::value;
         constexpr bool NEXT = decltype(next_tag)::value;
         constexpr int cur = decltype(cur_tag)::value;   // -1: the stage parity known at run time
         constexpr int NS = decltype(ns_tag)::value;
         static_assert(NS % 4 == 0 && NS <= STEPS && (NS == STEPS || !NEXT), "steps of a panel");
-        const float *As = smem + (cur < 0 ? (panel_parity & 1) : cur) * SSTRIDE;
+        const int cur_stage = cur < 0 ? (panel_parity & 1) : cur;
+        const float *As = smem + cur_stage * SSTRIDE;
         const float *Bs = As + T::A_TILE;
-        float *Anext = smem + ((cur < 0 ? (panel_parity & 1) : cur) ^ 1) * SSTRIDE;
+        float *Anext = smem + (cur_stage ^ 1) * SSTRIDE;
+        const float *Ss = strip_lds + (cur_stage * KG + kg) * T::STRIP_STAGE;
         static_for<0, NS>([&](auto tc) {
             constexpr int t = decltype(tc)::value;
             constexpr int kb = t >> 2, s = t & 3;
@@ -789,6 +721,15 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
                     if constexpr (DL) load_direct(Anext, l); else load_slot(l);
                 }
             }
+            // strip: the next panel's B values with the first loads; k-group kb's B values
+            // read at its first step and its products added at its third
+            constexpr int n_sload = (STRIP && NEXT && t == 0) ? 1 : 0;
+            constexpr bool s_rd = STRIP && s == 0;
+            constexpr bool s_fma = STRIP && s == 2;
+            if constexpr (n_sload > 0) strip_load(cur_stage ^ 1);
+            if constexpr (s_fma) strip_fma(a[kb & 1]);
+            if constexpr (s_rd)
+                sbv = *reinterpret_cast<const f32x4 *>(Ss + 4 * (S::H * kb + hi));
             if constexpr (n_write > 0) {
 #pragma unroll
                 for (int l = w_first; l < w_first + n_write; ++l) write_slot(Anext, l);
@@ -809,8 +750,9 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
                 read_b(Anext + T::A_TILE, 0, b[0]);
             }
             // pin the order: memory instructions of this step first, then its MFMAs
-            if constexpr (n_load > 0)
-                __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, n_load, 0);
+            if constexpr (n_load + n_sload > 0)
+                __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, n_load + n_sload, 0);
+
             if constexpr (n_write > 0)
                 __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, n_write, 0);
             if constexpr (next_b || next_a)
@@ -846,18 +788,19 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     constexpr int KGROUPS = STEPS / 4;
     constexpr bool TRIM = BM * BN <= 128 * 128;
     using AllSteps = std::integral_constant<int, STEPS>;
-    auto last_panel = [&](auto cur_tag, int rounds) {
+    auto last_panel = [&](auto cur_tag, int rounds, auto strip_tag) __attribute__((always_inline)) {
         const int valid = lK - (kg + (rounds - 1) * KG) * BK;
         const int nkg = valid <= 0 ? 0 : (valid + 4 * S::KSTEP - 1) / (4 * S::KSTEP);
         if (!TRIM) {
-            if (nkg > 0) panel(cur_tag, std::false_type{}, AllSteps{});
+            if (nkg > 0) panel(cur_tag, std::false_type{}, AllSteps{}, strip_tag);
         } else if (nkg >= KGROUPS) {
-            panel(cur_tag, std::false_type{}, AllSteps{});
+            panel(cur_tag, std::false_type{}, AllSteps{}, strip_tag);
         } else {
             static_for<1, KGROUPS>([&](auto nc) {
                 constexpr int n = decltype(nc)::value;
                 if (nkg == n)
-                    panel(cur_tag, std::false_type{}, std::integral_constant<int, 4 * n>{});
+                    panel(cur_tag, std::false_type{}, std::integral_constant<int, 4 * n>{},
+                          strip_tag);
             });
         }
     };
@@ -865,7 +808,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     // ---- epilogue of one tile: accumulators to C through a buffer resource ----
     const int ldc = p.ldc;
     // Sum the accumulator sets, then (KG > 1) the K-groups, into group 0's acc[0].
-    auto finish = [&]() {
+    auto finish = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int h = 1; h < KACC; ++h)
 #pragma unroll
@@ -914,7 +857,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     // Stores the tile through resource rsc (its first element at offset 0, rows ldc4 bytes
     // apart), rows_left x cols_left of it inside the destination, with cache policy POLICY.
     auto epilogue = [&](__amdgpu_buffer_rsrc_t rsc, uint32_t ldc4, int rows_left,
-                        int cols_left, auto policy_tag) {
+                        int cols_left, auto policy_tag) __attribute__((always_inline)) {
         constexpr int POLICY = decltype(policy_tag)::value;
         // Lane (lo, hi) owns rows lrow + dr (dr = 8 (v / 4) + v % 4 for accumulator v) and
         // columns col .. col + CI - 1 of each of its blocks. The row step dr * ldc goes in
@@ -1001,58 +944,93 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
         }
 
         // ---- the item: the K loop of group kg (panels kg, kg + KG, ...), the K-group sums
-        // and the epilogue, into C or (a partial stream-K tile) into workspace slot `slot`
-        set_item();
-        set_panel(kg * BK);
-        if constexpr (DL) {
+        // and the epilogue, into C or (a partial stream-K tile) into workspace slot `slot`;
+        // with STRIP also the column strip's rows of this tile
+        auto run_item = [&](auto strip_tag) __attribute__((always_inline)) {
+            constexpr bool STRIP = decltype(strip_tag)::value;
+            auto setp = [&](int k0) __attribute__((always_inline)) {
+                set_panel(k0);
+                if constexpr (STRIP) set_strip_panel(k0);
+            };
+            set_item();
+            if constexpr (STRIP) set_strip_item();
+            setp(kg * BK);
+            if constexpr (DL) {
 #pragma unroll
-            for (int l = 0; l < NL; ++l) load_direct(smem, l);
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            fix_k_tail(smem);
-        } else {
-#pragma unroll
-            for (int l = 0; l < NL; ++l) load_slot(l);
-#pragma unroll
-            for (int l = 0; l < NL; ++l) write_slot(smem, l);
-        }
-        __syncthreads();
-        read_a(smem, 0, a[0]);
-        read_b(smem + T::A_TILE, 0, b[0]);
-
-        // the last round stages nothing; a group whose last panel lies past the K range loads
-        // only zeros for it
-        const int rounds = ((lK + BK - 1) / BK + KG - 1) / KG;
-        if constexpr (PAIR) {
-            // two panels per iteration, so each one's LDS stage is a constant and its operand
-            // reads carry the stage in their immediate offsets (no address arithmetic on the
-            // vector ALU between the MFMAs)
-            using S0 = std::integral_constant<int, 0>;
-            using S1 = std::integral_constant<int, 1>;
-            int r = 0;
-            for (; r + 2 < rounds; r += 2) {
-                set_panel(((r + 1) * KG + kg) * BK);
-                panel(S0{}, std::true_type{}, AllSteps{});
-                set_panel(((r + 2) * KG + kg) * BK);
-                panel(S1{}, std::true_type{}, AllSteps{});
-            }
-            if (r + 1 < rounds) {
-                set_panel(((r + 1) * KG + kg) * BK);
-                panel(S0{}, std::true_type{}, AllSteps{});
-                last_panel(S1{}, rounds);
+                for (int l = 0; l < NL; ++l) load_direct(smem, l);
+                if constexpr (STRIP) strip_load(0);
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                fix_k_tail(smem);
             } else {
-                last_panel(S0{}, rounds);
+#pragma unroll
+                for (int l = 0; l < NL; ++l) load_slot(l);
+#pragma unroll
+                for (int l = 0; l < NL; ++l) write_slot(smem, l);
             }
+            __syncthreads();
+            read_a(smem, 0, a[0]);
+            read_b(smem + T::A_TILE, 0, b[0]);
+
+            // the last round stages nothing; a group whose last panel lies past the K range
+            // loads only zeros for it
+            const int rounds = ((lK + BK - 1) / BK + KG - 1) / KG;
+            if constexpr (PAIR) {
+                // two panels per iteration, so each one's LDS stage is a constant and its
+                // operand reads carry the stage in their immediate offsets (no address
+                // arithmetic on the vector ALU between the MFMAs)
+                using S0 = std::integral_constant<int, 0>;
+                using S1 = std::integral_constant<int, 1>;
+                int r = 0;
+                for (; r + 2 < rounds; r += 2) {
+                    setp(((r + 1) * KG + kg) * BK);
+                    panel(S0{}, std::true_type{}, AllSteps{}, strip_tag);
+                    setp(((r + 2) * KG + kg) * BK);
+                    panel(S1{}, std::true_type{}, AllSteps{}, strip_tag);
+                }
+                if (r + 1 < rounds) {
+                    setp(((r + 1) * KG + kg) * BK);
+                    panel(S0{}, std::true_type{}, AllSteps{}, strip_tag);
+                    last_panel(S1{}, rounds, strip_tag);
+                } else {
+                    last_panel(S0{}, rounds, strip_tag);
+                }
+            } else {
+                using SR = std::integral_constant<int, -1>;
+                for (int r = 0; r + 1 < rounds; ++r) {
+                    setp(((r + 1) * KG + kg) * BK);
+                    panel_parity = r;
+                    panel(SR{}, std::true_type{}, AllSteps{}, strip_tag);
+                }
+                panel_parity = rounds - 1;
+                last_panel(SR{}, rounds, strip_tag);
+            }
+            finish();
+            if constexpr (STRIP) {
+                // the wn = 0 waves' partial sums of each (K-group, lane group) for each row,
+                // then their sum in ascending order of both, stored to C (rows past M are not)
+                if (wn == 0) {
+#pragma unroll
+                    for (int r = 0; r < RB; ++r)
+                        strip_red[(kg * S::H + hi) * BM + wm * WM + r * MB + lo] = sacc[r];
+                }
+                __syncthreads();
+                const int row = threadIdx.x;
+                if (row < BM && lm0 + row < M) {
+                    float v = 0.0f;
+                    for (int g = 0; g < KG * S::H; ++g) v += strip_red[g * BM + row];
+                    p.C[int64_t(lm0 + row) * ldc + p.strip_n0] = v;
+                }
+            }
+        };
+        bool strip_here = false;
+        if constexpr (CAN_STRIP)
+            strip_here = p.strip_cols > 0 && ln0 + BN == p.strip_n0;
+        if constexpr (CAN_STRIP) {
+            if (strip_here) run_item(std::true_type{});
+            else run_item(std::false_type{});
         } else {
-            using SR = std::integral_constant<int, -1>;
-            for (int r = 0; r + 1 < rounds; ++r) {
-                set_panel(((r + 1) * KG + kg) * BK);
-                panel_parity = r;
-                panel(SR{}, std::true_type{}, AllSteps{});
-            }
-            panel_parity = rounds - 1;
-            last_panel(SR{}, rounds);
+            run_item(std::false_type{});
         }
-        finish();
         if (kg == 0) {
             if (!to_workspace) {
                 const int64_t ec = ls * p.c_split_stride + int64_t(lm0) * ldc + ln0;

@@ -35,9 +35,8 @@ struct Variant {
     // persistent kernel; forced on other shapes it computes their whole-tile part and
     // leaves the rest to the plan)
     bool whole_tiles = false;
-    // a thin remainder of N past the last whole tile column may be computed by strip
-    // workgroups on the vector ALUs, next to the tiles on the same compute units (needs room
-    // for a second workgroup per CU)
+    // a one-column remainder of N past the last whole tile column may be computed by the
+    // tiles of the last tile column, on the vector ALUs (the kernel's column strip)
     bool strip = false;
 };
 
@@ -56,30 +55,18 @@ inline bool offsets_fit(const Variant &v, const Operands &o)
            int64_t(v.BM) * o.ldc * 4 + int64_t(v.BN) * 4 + 64 < lim;
 }
 
-// Most columns a strip may hold, and rows per strip workgroup (the kernels' kStripCols and
-// kStripRows).
-constexpr int kStripColsMax = 4;
-constexpr int kStripRowsPlan = 8;
+// Most columns a strip may hold (the kernels' kStripCols).
+constexpr int kStripColsMax = 1;
 
-// Strip workgroups for M rows: one per 8 rows, rounded up to a multiple of the 8 XCDs so
-// the tiles that follow them in the grid keep their XCD (the extra ones have no rows).
-inline int strip_wgs(int M)
-{
-    const int n = (M + kStripRowsPlan - 1) / kStripRowsPlan;
-    return (n + 7) / 8 * 8;
-}
-
-// Columns variant v could leave to strip workgroups for o: N mod BN when that is 1 to
-// kStripColsMax and N holds at least one whole tile column, else 0. The strip reads B 2048
-// rows at a time from one buffer resource, so those rows must span less than 2^31 bytes.
-// Whether the plan uses the strip is a choice priced by variant_cost (strip_cols).
+// Columns variant v could leave to the strip for o: N mod BN when that is 1 to
+// kStripColsMax and N holds at least one whole tile column, else 0 (the strip's B values
+// of a panel lie inside the panel's rows of B, so the offsets bound of offsets_fit covers
+// them). Whether the plan uses the strip is a choice priced by variant_cost (strip_cols).
 inline int strip_eligible(const Variant &v, const Operands &o)
 {
     if (!v.strip || o.splits != 1 || o.N <= v.BN) return 0;
     const int r = o.N % v.BN;
-    if (r < 1 || r > kStripColsMax) return 0;
-    if (int64_t(2052) * o.ldb * 4 + 64 >= (int64_t(1) << 31)) return 0;
-    return r;
+    return r >= 1 && r <= kStripColsMax ? r : 0;
 }
 
 inline bool variant_allowed(const Variant &v, const Operands &o)
@@ -92,14 +79,10 @@ inline bool variant_allowed(const Variant &v, const Operands &o)
 
 // Cost units: one multiply-add on one CU at rate 1 (140 TFLOP/s over 256 CUs).
 constexpr double kUnitsPerUs = 140e12 / 2 / 256 * 1e-6;
-// A strip workgroup sleeps about 2 us and then waits a few global-memory latencies per 2048
-// values of K (measured beside tiles: about 17 us at K = 1027). While it runs it slows the
-// tile on its compute unit by about 15 % of its own time (measured: 1023 x 1025 x 1027 took
-// 2.6 us longer than its tiles alone), and when the tiles take more than one round it holds
-// a slot that a tile could use; the other tile of that compute unit then runs alone, which
-// recovers about half of it.
-constexpr double kStripUsPerGroup = 15.0;
-constexpr double kStripShare = 0.15;
+// The tiles of the last tile column also compute the strip, on the vector ALUs between
+// their MFMAs; they run a few per cent longer than the others (measured: 7 % at
+// 1023 x 1025 x 1027 with 64 x 64 tiles).
+constexpr double kStripShare = 0.03;
 
 // Busiest-CU estimate for variant v with tn tile columns, in multiply-adds at rate 1.
 inline double tiles_cost(const Variant &v, const Operands &o, int cus, int64_t tn)
@@ -118,18 +101,11 @@ inline double tiles_cost(const Variant &v, const Operands &o, int cus, int64_t t
 // The same with a column strip of the last N mod BN columns (strip_eligible).
 inline double strip_cost(const Variant &v, const Operands &o, int cus)
 {
-    const int64_t tm = (int64_t(o.M) + v.BM - 1) / v.BM, tn = o.N / v.BN;
-    const double tiles = tiles_cost(v, o, cus, tn);
-    const double t_strip = double(1 + (o.K - 1) / 2048) * kStripUsPerGroup * kUnitsPerUs;
-    const int64_t slots = int64_t(cus) * v.wg_per_cu;
-    double cost = (tiles > t_strip ? tiles : t_strip) + kStripShare * t_strip;
-    if (tm * tn + strip_wgs(o.M) > slots)
-        cost += 0.5 * double(strip_wgs(o.M)) * t_strip / double(slots);
-    return cost;
+    return tiles_cost(v, o, cus, o.N / v.BN) * (1.0 + kStripShare);
 }
 
-// Columns variant v leaves to strip workgroups for o: those of strip_eligible when the
-// strip is priced below a last column of masked tiles, else 0.
+// Columns variant v leaves to the strip for o: those of strip_eligible when the strip is
+// priced below a last column of masked tiles, else 0.
 inline int strip_cols(const Variant &v, const Operands &o, int cus)
 {
     const int r = strip_eligible(v, o);

@@ -89,7 +89,8 @@ constexpr VariantEntry entry(const char *name, int wg_per_cu, double rate, doubl
         Variant{name, BM, BN, BK, WGM, WGN, wg_per_cu, rate, overhead, solo, DL, PLANNED},
         &k_sgemm_mfma<BM, BN, BK, WGM, WGN, KACC, KG, DL, false, MB>, sk, fix,
         64 * WGM * WGN * KG, MB, KG, "mfma"};
-    e.v.strip = wg_per_cu >= 2 && 64 * WGM * WGN * KG == 256;
+    // the kernel's column strip (kernel_mfma.hpp): direct loads and room in LDS
+    e.v.strip = DL && MfmaTile<BM, BN, BK, WGM, WGN, KACC, KG, MB>::STRIP_OK;
     return e;
 }
 
@@ -187,8 +188,7 @@ int device_cus(int *out)
     return SGEMM_OK;
 }
 
-static_assert(kStripCols == kStripColsMax && kStripRows == kStripRowsPlan,
-              "strip geometry of the kernels and of the plan");
+static_assert(kStripCols == kStripColsMax, "strip width of the kernels and of the plan");
 
 // Kernel arguments of the plain product with variant e; with `cus` > 0, a thin remainder of
 // N goes to strip workgroups when the plan prices that lower (strip_cols).
@@ -208,7 +208,7 @@ GemmArgs plain_args(const VariantEntry &e, const Operands &o, const float *A, co
     p.k_chunk = o.K;
     p.c_split_stride = 0;
     p.strip_n0 = o.N - r;
-    p.strip_wgs = r > 0 ? strip_wgs(o.M) : 0;
+    p.strip_cols = r;
     return p;
 }
 
@@ -316,7 +316,7 @@ int run_variant(int vi, const Operands &o, const float *A, const float *B, float
     const int qs = device_cus(&cus);
     if (qs != SGEMM_OK) return qs;
     const GemmArgs p = plain_args(e, o, A, B, C, cus);
-    const int64_t grid = int64_t(p.tiles_m) * p.tiles_n + p.strip_wgs;
+    const int64_t grid = int64_t(p.tiles_m) * p.tiles_n;
     if (grid > INT32_MAX) return SGEMM_ETOO_LARGE;
     return launch(e.kern, dim3(unsigned(grid)), dim3(e.threads), stream, p);
 }
@@ -630,6 +630,8 @@ extern "C" int sgemm_f32_streamk_describe(int M, int N, int K, int variant, int 
     if (vi < 0) return vi;
     const Variant &v = kVariants[vi].v;
     const SkGeom g = streamk_geometry(v, o, cus);
+    // a plain plan may leave a thin remainder of N to the last tile column (strip_cols)
+    const int strip = sk || kVariants[vi].persistent ? 0 : strip_cols(v, o, cus);
     // walk every stream-K range with the kernels' own functions: each unit must belong to
     // exactly one range, each shared tile's partial slots must be distinct and written by
     // the segment that the fixup reads them for
@@ -677,13 +679,15 @@ extern "C" int sgemm_f32_streamk_describe(int M, int N, int K, int variant, int 
                            "\"tiles_sk\": %d, \"panels\": %d, \"units\": %lld, "
                            "\"shared_tiles\": %lld, \"max_contributors\": %lld, "
                            "\"max_segments\": %lld, \"workspace_bytes\": %zu, "
-                           "\"partition_ok\": %s}",
+                           "\"partition_ok\": %s, \"strip_cols\": %d}",
                            vi, v.name, sk ? "true" : "false", v.BM, v.BN, v.BK, cus, g.G,
-                           (long long)(int64_t((M + v.BM - 1) / v.BM) * ((N + v.BN - 1) / v.BN)),
+                           (long long)(int64_t((M + v.BM - 1) / v.BM) *
+                                       ((N - strip + v.BN - 1) / v.BN)),
                            sk ? g.tiles_dp : 0, sk ? g.tiles_sk : 0, g.panels,
                            (long long)(sk ? g.iters : 0), (long long)shared,
                            (long long)max_contrib, (long long)max_segments,
-                           sk ? streamk_workspace_bytes(v, g) : size_t(0), ok ? "true" : "false");
+                           sk ? streamk_workspace_bytes(v, g) : size_t(0), ok ? "true" : "false",
+                           strip);
     if (n < 0 || n >= buflen) return SGEMM_EINVAL_ARG;
     return vi;
 }
@@ -837,7 +841,7 @@ extern "C" int sgemm_f32_plan_describe(int M, int N, int K, const float *A, int 
     // one workgroup per tile (and per strip row block), or for the persistent variant one
     // per CU over its tiles
     const int64_t grid = kVariants[vi].persistent ? std::min<int64_t>(tm * tn, cus)
-                                                  : tm * tn + (strip ? strip_wgs(M) : 0);
+                                                  : tm * tn;
     // operand bytes the tiles request: every A row panel once per tile column and every
     // B column panel once per tile row (before any cache reuse)
     const int64_t tile_bytes = 4 * (int64_t(M) * K * tn + int64_t(K) * N * tm);
@@ -846,11 +850,11 @@ extern "C" int sgemm_f32_plan_describe(int M, int N, int K, const float *A, int 
                            "\"BK\": %d, \"waves\": [%d, %d], \"threads\": %d, \"grid\": %lld, "
                            "\"tiles\": [%lld, %lld], \"cus\": %d, \"wg_per_cu\": %d, "
                            "\"direct_loads\": %s, \"tile_request_bytes\": %lld, "
-                           "\"strip_cols\": %d, \"strip_wgs\": %lld}",
+                           "\"strip_cols\": %d, \"strip_tiles\": %lld}",
                            vi, v.name, v.BM, v.BN, v.BK, v.wgm, v.wgn, kVariants[vi].threads,
                            (long long)grid, (long long)tm, (long long)tn, cus, v.wg_per_cu,
                            v.direct ? "true" : "false", (long long)tile_bytes, strip,
-                           (long long)(strip ? strip_wgs(M) : 0));
+                           (long long)(strip ? tm : 0));
     if (n < 0 || n >= buflen) return SGEMM_EINVAL_ARG;
     return vi;
 }

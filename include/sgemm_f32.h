@@ -57,9 +57,9 @@ typedef enum {
  * The hot path: the LDS-tiled, register-tiled matrix-core kernel ("SGEMM: 2D Register
  * Tiling Visualizer", "Why 2D Register Tiling Dominates", carried onto the FP32 MFMA
  * instructions), with tiles zero-filled past the edges of ragged shapes. The tile shape
- * is chosen per (M, N, K) and compute-unit count; when N leaves 1 to 4 columns past the
- * last whole tile column, those columns may be computed in the same launch by workgroups
- * on the vector ALUs instead of a nearly empty column of tiles. Any 4-byte aligned
+ * is chosen per (M, N, K) and compute-unit count; when N leaves one column past the last
+ * whole tile column, the tiles of that last column may also compute it, on the vector ALUs
+ * beside their MFMAs, instead of a nearly empty column of tiles. Any 4-byte aligned
  * pointers and any leading dimensions work. Leading dimensions so large that 256 rows of A or C (or 32
  * rows of B) exceed 2^31 bytes return SGEMM_ETOO_LARGE.
  */
@@ -168,9 +168,10 @@ size_t sgemm_f32_streamk_noalloc_scratch_bytes(void);
  * this shape into buf: variant and tile, whether it shares tiles, the workgroup count G,
  * the plain and shared tile counts, K-panels per tile, the shared units, how many tiles
  * are shared and by at most how many workgroups, segments per workgroup, workspace bytes,
- * and "partition_ok": the result of walking every range with the kernels' own partition
+ * "partition_ok": the result of walking every range with the kernels' own partition
  * functions (every unit in exactly one range, every partial slot the fixup reads written
- * once for that tile). num_cus > 0 plans for that many compute units (no GPU needed);
+ * once for that tile), and for a plain plan the columns its last tile column computes as a
+ * strip ("strip_cols"; the tile count then leaves them out). num_cus > 0 plans for that many compute units (no GPU needed);
  * num_cus <= 0 queries the current device. M, N and K must be positive (else
  * SGEMM_EINVAL_DIM). Returns the variant index, or a negative sgemm_status.
  */
@@ -267,9 +268,8 @@ const char *sgemm_f32_variant_name(int variant);
  * ("mfma": the LDS-double-buffered template; "regpanel": the one-wave-per-SIMD kernel;
  * "persist": the persistent kernel), whether split-K may use it, whether it runs one
  * workgroup per CU over the tiles ("persistent"), whether it only takes whole tiles
- * ("whole_tiles") and whether a thin remainder of N (1 to 4 columns past the last whole
- * tile column) goes to strip workgroups on the vector ALUs ("strip"). Host-only, no GPU
- * needed. Returns SGEMM_OK, or
+ * ("whole_tiles") and whether the tiles of its last tile column can also compute one
+ * column of N past it, on the vector ALUs ("strip"). Host-only, no GPU needed. Returns SGEMM_OK, or
  * SGEMM_EINVAL_ARG for a bad index or a buffer too small.
  */
 int sgemm_f32_variant_info(int variant, char *buf, int buflen);
@@ -280,8 +280,10 @@ const char *sgemm_f32_status_string(int status);
 /*
  * Writes a one-line JSON description of the plan sgemm_f32 would run for these
  * arguments into buf (at most buflen bytes including the NUL): variant, tile shape,
- * waves, grid, workgroups resident per CU, whether panels load straight into LDS, and
- * the operand bytes the tiles request. The plan is the pages' tile-size trade-off: reuse
+ * waves, grid, workgroups resident per CU, whether panels load straight into LDS, the
+ * operand bytes the tiles request, and the column strip: "strip_cols" (the column past
+ * the last whole tile column that the tiles of that column also compute, 0 or 1) and
+ * "strip_tiles" (how many tiles do). The plan is the pages' tile-size trade-off: reuse
  * per staged element against the parallelism left ("Shared Memory Tiling", "Choosing a
  * tile size"). Dimensions and leading dimensions are validated as in sgemm_f32
  * (SGEMM_EINVAL_DIM, SGEMM_EINVAL_LD); pointers are used for their alignment only and

@@ -102,10 +102,8 @@ def test_plan(shape, expect_tile):
                                      num_cus=256)
     tiles = plan["tiles"][0] * plan["tiles"][1]
     info = g.sgemm_f32_variant_info(plan["variant"])
-    # one workgroup per tile (plus one per tile row for a column strip), or one per CU
-    # walking the tiles
-    assert plan["grid"] == (min(tiles, 256) if info["persistent"]
-                            else tiles + plan["strip_wgs"])
+    # one workgroup per tile, or one per CU walking the tiles
+    assert plan["grid"] == (min(tiles, 256) if info["persistent"] else tiles)
     assert plan["direct_loads"] == plan["name"].endswith("_dl")
     # the tiles cover C but for the strip's columns, which lie past whole tile columns
     assert plan["tiles"][0] * plan["BM"] >= M
@@ -113,7 +111,7 @@ def test_plan(shape, expect_tile):
         plan["strip_cols"] == 0 and plan["tiles"][1] * plan["BN"] >= N)
     if plan["strip_cols"]:
         assert info["strip"] and 1 <= plan["strip_cols"] <= 4
-        assert plan["strip_wgs"] == ((M + 7) // 8 + 7) // 8 * 8
+        assert plan["strip_tiles"] == plan["tiles"][0]
     if shape == (1023, 1025, 1027):
         # the ragged workload: 256 whole 64 x 64 tiles and a one-column strip, instead of
         # a 17th column of nearly empty tiles

@@ -1,6 +1,6 @@
-"""The column strip through the C ABI: when N leaves 1 to 4 columns past the last whole
-tile column, variants with room for a second workgroup per compute unit compute those
-columns in strip workgroups on the vector ALUs, in the same launch as the tiles. Checked
+"""The column strip through the C ABI: when N leaves one column past the last whole tile
+column, the workgroups of the last tile column also compute that column, on the vector
+ALUs between their MFMAs, from the A operands they read for the MFMAs. Checked
 against the oracle (exact on small integers, within the normalised tolerance on floats)
 with NaN-poisoned row padding and guard bands around C, for every strip-capable variant
 forced, for the automatic plan, and for run-to-run determinism."""
@@ -29,13 +29,17 @@ def strip_variants():
 
 
 def shapes_for(v):
-    """(M, N, K) with N = (whole tile columns) + R, R = 1..4, K on both sides of the strip's
-    256-wide chunks, its 2048-wide groups and the panel depth, M ragged."""
+    """(M, N, K) with N = (whole tile columns) + 1: enough tile columns that every tile takes
+    a share of the strip's rows (five or more; 17 gives shares that end inside the tiles),
+    K on both sides of the panel depth and of K-group rounds (with partial last panels),
+    M ragged; and two products without a strip (a wider remainder, too few tile columns)."""
     bn = g.sgemm_f32_variant_info(v)["BN"]
-    return [(63, bn + 1, 33), (130, bn + 2, 256), (200, 2 * bn + 3, 257),
-            (65, bn + 4, 300), (257, 3 * bn + 1, 5), (129, bn + 2, 1),
-            # K across several of the strip's 2048-wide groups, and its sleep before a long K
-            (70, bn + 1, 2050), (17, bn + 3, 4353)]
+    return [(63, 5 * bn + 1, 33), (130, 8 * bn + 1, 256), (200, 5 * bn + 1, 257),
+            (65, 17 * bn + 1, 300), (257, 5 * bn + 1, 5), (129, 6 * bn + 1, 1),
+            (70, 5 * bn + 1, 2050), (17, 9 * bn + 1, 4353), (100, 5 * bn + 1, 37),
+            (33, 7 * bn + 1, 64),
+            # no strip: a remainder wider than it, or too few tile columns to share its rows
+            (130, 5 * bn + 2, 256), (65, bn + 1, 300)]
 
 
 def _check(A, B, C, kind, what):
@@ -52,7 +56,7 @@ def test_strip_variants_exist():
     assert vs, "no variant computes a column strip"
     for v in vs:
         info = g.sgemm_f32_variant_info(v)
-        assert info["wg_per_cu"] >= 2 and info["kernel"] == "mfma", info
+        assert info["direct_loads"] and info["kernel"] == "mfma", info
 
 
 def test_strip_shapes_forced(gpu):
@@ -83,8 +87,8 @@ def test_ragged_workload_plan_uses_strip(gpu, kind):
     M, N, K = 1023, 1025, 1027
     plan = g.sgemm_f32_plan_describe(M, N, K)
     print(f"[strip] plan {plan}", flush=True)
-    # one strip workgroup per 8 rows, rounded up to a multiple of the 8 XCDs
-    assert plan["strip_cols"] == 1 and plan["strip_wgs"] == ((M + 7) // 8 + 7) // 8 * 8
+    # the tiles of the last tile column (one per tile row) compute the strip
+    assert plan["strip_cols"] == 1 and plan["strip_tiles"] == plan["tiles"][0]
     A, B = wl.operands("c3", kind)
     _, dA, lda = device_matrix(A, K + 1)
     _, dB, ldb = device_matrix(B)

@@ -24,6 +24,15 @@ def test_scanner_finds_the_pattern():
     one_gap = bad.replace("\tv_mov_b32_e32 v2, v17", "\ts_movk_i32 s4, 0x400\n\tv_mov_b32_e32 v2, v17")
     assert asm_check.store_data_hazards(one_gap)          # 1 wait state is not enough
     assert asm_check.store_data_hazards(one_gap, need=1) == {}
+    # global stores name the address first and the data second
+    glob = """_ZN5sgemm4kernE:
+\tglobal_store_dwordx4 v[2:3], v[6:9], off offset:-8
+\tv_lshl_add_u64 v[2:3], v[2:3], 0, 16
+"""
+    assert asm_check.store_data_hazards(glob) == {}
+    assert list(asm_check.store_data_hazards(glob.replace("v[2:3], v[2:3], 0, 16",
+                                                          "v[6:7], v[2:3], 0, 16"))) == \
+        ["_ZN5sgemm4kernE"]
 
 
 @pytest.mark.skipif(shutil.which("hipcc") is None and not build.os.path.exists("/opt/rocm/bin/hipcc"),
