@@ -266,7 +266,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5", "sk"])
+    ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5", "sk", "rk"])
     ap.add_argument("--variant", type=int, default=-1, help="force a hot-kernel tile variant")
     ap.add_argument("--kernel", default="auto",
                     choices=["auto", "splitk", "streamk", "naive", "tiled16", "tiled32", "tiled32p", "regtiled41",

@@ -270,6 +270,15 @@ __device__ __forceinline__ void regpanel_item(const GemmArgs &p, float *lds, int
         rows_left = WT;
         cols_left = WT;
     }
+    // The chunk that crosses N is stored element by element. The stream-K form stores it
+    // right after each vector store, from the same registers: a second pass over the
+    // accumulators (the plain form's, kept as its timings were taken) makes it spill.
+    const bool crosses = col < cols_left && col + 4 > cols_left;
+    auto store_partial = [&](int lr, int c, float x) {
+        const bool keep = crosses && col + c < cols_left && lr < rows_left;
+        store_vec<1, kStoreNonTemporal>(rc, keep ? uint32_t(lr) * ldc4 + 4u * (col + c) : kOob,
+                                        0u, x);
+    };
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
 #pragma unroll
@@ -280,10 +289,18 @@ __device__ __forceinline__ void regpanel_item(const GemmArgs &p, float *lds, int
             store_vec<4, kStoreNonTemporal>(rc, ok ? uint32_t(lr) * ldc4 + 16u * lo : kOob, 0u,
                                             out);
             store_data_guard<SK>();
+            if constexpr (SK) {
+                if (cols_left < WT) {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        store_partial(lr, c, out[c]);
+                        store_data_guard<true>();
+                    }
+                }
+            }
         }
     }
-    if (cols_left < WT) {
-        // the chunk that crosses N, element by element
+    if (!SK && cols_left < WT) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll

@@ -15,6 +15,7 @@ shape, the large square headline shape and a low-K shape:
   c4    8192   8192   8192  uniform[-1, 1]
   c5    16384  16384  64    uniform[-1, 1]
   sk    256    256    32768 uniform[-1, 1]    (an under-filled shape for split-K)
+  rk    4500   4500   8192  uniform[-1, 1]    (a large ragged shape for stream-K)
 
 Seeds: A = 1000*i + 1, B = 1000*i + 2 for config ci; the integer variant uses
 1000*i + 3 and 1000*i + 4. All operands are packed row-major (lda = K, ldb = N).
@@ -52,6 +53,9 @@ WORKLOADS = {
     "c5": Workload("c5", 5, 16384, 16384, 64, "uniform", "low-K 16384x16384x64"),
     # not one of the five: an under-filled shape (16 tiles of 64 x 64) for split-K
     "sk": Workload("sk", 6, 256, 256, 32768, "uniform", "under-filled 256x256x32768"),
+    # not one of the five: 18 x 18 tiles of 256 x 256, just past one round of 256 compute
+    # units, so whole-tile rounds leave most units idle in the last one (stream-K's case)
+    "rk": Workload("rk", 7, 4500, 4500, 8192, "uniform", "ragged large 4500x4500x8192"),
 }
 
 
