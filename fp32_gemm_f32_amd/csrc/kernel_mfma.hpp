@@ -323,9 +323,12 @@ struct MfmaTile {
     static constexpr int RED = (KG - 1) * kGroupThreads * NACC * ACC;
     // Column strip (see the kernel): per stage, 64 floats of the strip's B column (one per
     // value of k of the panel), loaded with the panel; then a reduction area for the lanes'
-    // partial sums: one row of BM floats per K-group and MFMA lane group.
+    // partial sums: one row per K-group and MFMA lane group, STRIP_RS floats apart. The
+    // row stride is 64 / H words past a multiple of 64, so the H lane groups of a wave,
+    // which write the same rows' sums into H different rows, hit different banks.
     static constexpr int STRIP_STAGE = 64;
-    static constexpr int STRIP_FLOATS = 2 * KG * STRIP_STAGE + KG * MfmaShape<MB>::H * BM;
+    static constexpr int STRIP_RS = (BM + 63) / 64 * 64 + 64 / MfmaShape<MB>::H;
+    static constexpr int STRIP_FLOATS = 2 * KG * STRIP_STAGE + KG * MfmaShape<MB>::H * STRIP_RS;
     static constexpr bool STRIP_OK = BM <= kGroupThreads * KG && BK <= 64 &&
                                      RED <= 2 * KG * STAGE &&
                                      (2 * KG * STAGE + STRIP_FLOATS) * 4 <= 160 * 1024;
@@ -532,18 +535,22 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     // after the direct loads of a panel have landed: zero the elements past the K range in
     // this lane's A chunks (their LDS slots are 16 (tid + l NT) bytes into the A tile). The
-    // branch is uniform and taken only in the panel that holds the end of the range (or,
-    // with K-groups, lies past it).
+    // branch is uniform and taken only in the panel that holds the end of the range; a
+    // panel wholly past it (with K-groups) read zeros already, through its empty resource.
+    // Each chunk is read and written whole: neighbouring lanes' chunks are neighbouring 16
+    // bytes, so the accesses are free of bank conflicts (element stores, 16 bytes apart
+    // across the lanes, are not).
     auto fix_k_tail = [&](float *As) __attribute__((always_inline)) {
-        if (k_load + BK > lK) {
+        if (k_load < lK && k_load + BK > lK) {
             const int kc = k_load + 4 * a_q;
             if (kc + 4 > lK) {
 #pragma unroll
                 for (int l = 0; l < A_CH; ++l) {
-                    float *chunk = As + (tid + l * NT) * 4;
+                    f32x4 *chunk = reinterpret_cast<f32x4 *>(As + (tid + l * NT) * 4);
+                    f32x4 v = *chunk;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (kc + e >= lK) chunk[e] = 0.0f;
+                    for (int e = 0; e < 4; ++e) v[e] = kc + e < lK ? v[e] : 0.0f;
+                    *chunk = v;
                 }
             }
         }
@@ -686,12 +693,17 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
         }
     };
 
+    // NEXT (next_tag 1 or 2): the panel stages the next one; 2 (NextTail): that next panel
+    // is its group's last, which may hold the end of the K range (fix_k_tail applies to it;
+    // no other panel's code carries the tail's branch).
     // NS: the k-steps of the panel that run. A group's last panel runs only the k-groups
     // (4 steps each) that hold values of k inside its range; every other panel runs all.
     // STRIP: the panel also loads the next panel's strip values and computes this one's.
+    using NextTail = std::integral_constant<int, 2>;
     auto panel = [&](auto cur_tag, auto next_tag, auto ns_tag, auto strip_tag) __attribute__((always_inline)) {
         constexpr bool STRIP = decltype(strip_tag)::value;
-        constexpr bool NEXT = decltype(next_tag)::value;
+        constexpr bool NEXT = decltype(next_tag)::value != 0;
+        constexpr bool TAIL_NEXT = decltype(next_tag)::value == 2;
         constexpr int cur = decltype(cur_tag)::value;   // -1: the stage parity known at run time
         constexpr int NS = decltype(ns_tag)::value;
         static_assert(NS % 4 == 0 && NS <= STEPS && (NS == STEPS || !NEXT), "steps of a panel");
@@ -743,7 +755,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
                 // direct loads land in LDS when vmcnt counts them done
                 if constexpr (DL) {
                     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                    fix_k_tail(Anext);
+                    if constexpr (TAIL_NEXT) fix_k_tail(Anext);
                 }
                 __syncthreads();
                 read_a(Anext, 0, a[0]);
@@ -974,36 +986,43 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
             // the last round stages nothing; a group whose last panel lies past the K range
             // loads only zeros for it
             const int rounds = ((lK + BK - 1) / BK + KG - 1) / KG;
+            // The loops never stage the last round's panel: the last two rounds run after
+            // them, with the LDS stage known at run time, so the tail's code (the panel that
+            // stages the last round's panel, and the trimmed copies of the last panel)
+            // exists once and no loop iteration carries it.
+            using SR = std::integral_constant<int, -1>;
+            int r = 0;
             if constexpr (PAIR) {
                 // two panels per iteration, so each one's LDS stage is a constant and its
                 // operand reads carry the stage in their immediate offsets (no address
                 // arithmetic on the vector ALU between the MFMAs)
                 using S0 = std::integral_constant<int, 0>;
                 using S1 = std::integral_constant<int, 1>;
-                int r = 0;
-                for (; r + 2 < rounds; r += 2) {
+                for (; r + 3 < rounds; r += 2) {
                     setp(((r + 1) * KG + kg) * BK);
                     panel(S0{}, std::true_type{}, AllSteps{}, strip_tag);
                     setp(((r + 2) * KG + kg) * BK);
                     panel(S1{}, std::true_type{}, AllSteps{}, strip_tag);
                 }
-                if (r + 1 < rounds) {
+                if (r + 3 == rounds) {
                     setp(((r + 1) * KG + kg) * BK);
                     panel(S0{}, std::true_type{}, AllSteps{}, strip_tag);
-                    last_panel(S1{}, rounds, strip_tag);
-                } else {
-                    last_panel(S0{}, rounds, strip_tag);
+                    ++r;
                 }
             } else {
-                using SR = std::integral_constant<int, -1>;
-                for (int r = 0; r + 1 < rounds; ++r) {
+                for (; r + 2 < rounds; ++r) {
                     setp(((r + 1) * KG + kg) * BK);
                     panel_parity = r;
                     panel(SR{}, std::true_type{}, AllSteps{}, strip_tag);
                 }
-                panel_parity = rounds - 1;
-                last_panel(SR{}, rounds, strip_tag);
             }
+            if (r + 1 < rounds) {
+                setp(((r + 1) * KG + kg) * BK);
+                panel_parity = r;
+                panel(SR{}, NextTail{}, AllSteps{}, strip_tag);
+            }
+            panel_parity = rounds - 1;
+            last_panel(SR{}, rounds, strip_tag);
             finish();
             if constexpr (STRIP) {
                 // the wn = 0 waves' partial sums of each (K-group, lane group) for each row,
@@ -1011,13 +1030,14 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
                 if (wn == 0) {
 #pragma unroll
                     for (int r = 0; r < RB; ++r)
-                        strip_red[(kg * S::H + hi) * BM + wm * WM + r * MB + lo] = sacc[r];
+                        strip_red[(kg * S::H + hi) * T::STRIP_RS + wm * WM + r * MB + lo] =
+                            sacc[r];
                 }
                 __syncthreads();
                 const int row = threadIdx.x;
                 if (row < BM && lm0 + row < M) {
                     float v = 0.0f;
-                    for (int g = 0; g < KG * S::H; ++g) v += strip_red[g * BM + row];
+                    for (int g = 0; g < KG * S::H; ++g) v += strip_red[g * T::STRIP_RS + row];
                     p.C[int64_t(lm0 + row) * ldc + p.strip_n0] = v;
                 }
             }
