@@ -20,6 +20,11 @@
 
 namespace sgemm {
 
+// The stream-K price's default multiplier. The rates above were fitted before the plain
+// kernels gained 2-5 % (measured at steady state on eleven shapes from 512^2 x 8192 to 6000^3,
+// against the prices the model gives); stream-K forms measured at their price.
+constexpr double kStreamkPrice = 1.03;
+
 struct Variant {
     const char *name;
     int BM, BN, BK;
@@ -38,6 +43,9 @@ struct Variant {
     // a one-column remainder of N past the last whole tile column may be computed by the
     // tiles of the last tile column, on the vector ALUs (the kernel's column strip)
     bool strip = false;
+    // multiplier on the stream-K price (streamk_cost) of this variant's stream-K form; 0: the
+    // form is not planned (it still runs when forced)
+    double sk_price = kStreamkPrice;
 };
 
 struct Operands {
@@ -143,8 +151,9 @@ inline double streamk_cost(const Variant &v, const Operands &o, int cus, const S
     // contributors of the most shared tile: its units over a range's length, plus one
     const double contrib = double(g.panels) * g.G / double(g.iters) + 2.0;
     const double batches = contrib / kFixupBatch + 1.0;
-    return work + (kFixupUs + batches * kFixupBatchUs + double(ws_bytes) / kPartialBytesPerUs) *
-                      kUnitsPerUs;
+    return (work + (kFixupUs + batches * kFixupBatchUs + double(ws_bytes) / kPartialBytesPerUs) *
+                       kUnitsPerUs) *
+           (v.sk_price > 0.0 ? v.sk_price : 1.0);
 }
 
 template <int NV>

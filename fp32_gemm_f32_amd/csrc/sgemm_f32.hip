@@ -78,7 +78,7 @@ struct VariantEntry {
 template <int BM, int BN, int BK, int WGM, int WGN, int KACC, int KG, bool DL, bool PLANNED,
           int MB = 32>
 constexpr VariantEntry entry(const char *name, int wg_per_cu, double rate, double overhead,
-                             double solo)
+                             double solo, double sk_price = kStreamkPrice)
 {
     MfmaKernel sk = nullptr, fix = nullptr;
     if constexpr (PLANNED) {
@@ -91,6 +91,7 @@ constexpr VariantEntry entry(const char *name, int wg_per_cu, double rate, doubl
         64 * WGM * WGN * KG, MB, KG, "mfma"};
     // the kernel's column strip (kernel_mfma.hpp): direct loads and room in LDS
     e.v.strip = DL && MfmaTile<BM, BN, BK, WGM, WGN, KACC, KG, MB>::STRIP_OK;
+    e.v.sk_price = sk_price;
     return e;
 }
 
@@ -99,10 +100,14 @@ constexpr VariantEntry entry(const char *name, int wg_per_cu, double rate, doubl
 // the smaller tiles win.
 VariantEntry regpanel_entry(const char *name, double rate, double overhead)
 {
-    return VariantEntry{
+    VariantEntry e{
         Variant{name, 256, 256, 32, 2, 2, 1, rate, overhead, 1.0, false, true, false},
         regpanel_kernel(), regpanel_streamk_kernel(), &k_streamk_fixup<256, 256>, 256, 32, 1,
         "regpanel"};
+    // its stream-K form runs about 2 % over its price (4500^2 x 8192, 3000^2 x 8192,
+    // 2500^2 x 16384, measured at steady state), besides the plain model's drift
+    e.v.sk_price = 1.06;
+    return e;
 }
 
 // The persistent kernel (kernel_persist.hpp): 128 x 256 tiles of four 64 x 128 waves (one
@@ -145,7 +150,10 @@ const VariantEntry kVariants[] = {
     entry<128, 256, 16, 2, 2, 1, 1, true, true>("mfma_128x256x16_w2x2_dl", 2, 1.045, 0, 0.88),
     entry<128, 128, 32, 2, 2, 1, 1, true, true>("mfma_128x128x32_w2x2_dl", 2, 1.070, 12, 0.90),
     entry<64, 64, 32, 2, 1, 2, 4, true, false>("mfma_64x64x32_w2x1_acc2_kg4_dl", 1, 0.880, 212, 1.0),
-    entry<64, 64, 32, 2, 1, 1, 2, true, true>("mfma_64x64x32_w2x1_kg2_dl", 2, 1.015, 92, 0.78),
+    // its stream-K form is not planned: at 1536^2 x 4096 it ran 25 % slower than the plain
+    // plan that its price matched (it still runs when forced)
+    entry<64, 64, 32, 2, 1, 1, 2, true, true>("mfma_64x64x32_w2x1_kg2_dl", 2, 1.015, 92, 0.78,
+                                              0.0),
     entry<256, 256, 32, 4, 2, 1, 1, false, false>("mfma_256x256x32_w4x2", 1, 1.045, 52, 1.0),
     entry<80, 64, 32, 1, 2, 1, 4, true, true, 16>("mfma16_80x64x32_w1x2_kg4_dl", 1, 0.985, 236, 1.0),
     entry<80, 64, 32, 1, 2, 1, 2, true, true, 16>("mfma16_80x64x32_w1x2_kg2_dl", 2, 1.025, 64, 0.84),
@@ -248,10 +256,15 @@ int choose_streamk(const Operands &o, int cus, bool *sk)
         if (!v.planned || !variant_allowed(v, o)) continue;
         const double c_dp = variant_cost(v, o, cus);
         if (best < 0 || c_dp < best_cost) { best = i; best_cost = c_dp; *sk = false; }
-        if (!kVariants[i].kern_sk) continue;
+        if (!kVariants[i].kern_sk || v.sk_price <= 0.0) continue;
         double c_sk = 0.0;
         const SkGeom g = streamk_geometry(v, o, cus, &c_sk);
         if (g.tiles_sk == 0) continue;
+        // With two workgroups per CU, stream-K paid off only where some tiles still ran
+        // whole (measured at steady state: 4200^3, 6000^3 and 6000^2 x 4096, 0.6-2 % faster
+        // than plain); with every tile shared it ran 12 % slower (2500^2 x 16384, 128 x 128)
+        // and 25 % slower (1536^2 x 4096, 64 x 64 x 32) than the plain plans it was priced at.
+        if (v.wg_per_cu > 1 && g.tiles_dp == 0) continue;
         if (c_sk < best_cost) { best = i; best_cost = c_sk; *sk = true; }
     }
     return best;
@@ -629,7 +642,17 @@ extern "C" int sgemm_f32_streamk_describe(int M, int N, int K, int variant, int 
     const int vi = plan_streamk(variant < 0 ? -1 : variant, o, cus, &sk);
     if (vi < 0) return vi;
     const Variant &v = kVariants[vi].v;
-    const SkGeom g = streamk_geometry(v, o, cus);
+    double c_sk = 0.0;
+    const SkGeom g = streamk_geometry(v, o, cus, &c_sk);
+    // the plan's prices, in microseconds at the cost model's unit rate: the cheapest plain
+    // plan, and this variant as stream-K (0 when it has no shared tiles)
+    double c_plain = -1.0;
+    for (int i = 0; i < kNumVariants; ++i) {
+        const Variant &w = g_table[i];
+        if (!w.planned || !variant_allowed(w, o)) continue;
+        const double c = variant_cost(w, o, cus);
+        if (c_plain < 0.0 || c < c_plain) c_plain = c;
+    }
     // a plain plan may leave a thin remainder of N to the last tile column (strip_cols)
     const int strip = sk || kVariants[vi].persistent ? 0 : strip_cols(v, o, cus);
     // walk every stream-K range with the kernels' own functions: each unit must belong to
@@ -679,7 +702,8 @@ extern "C" int sgemm_f32_streamk_describe(int M, int N, int K, int variant, int 
                            "\"tiles_sk\": %d, \"panels\": %d, \"units\": %lld, "
                            "\"shared_tiles\": %lld, \"max_contributors\": %lld, "
                            "\"max_segments\": %lld, \"workspace_bytes\": %zu, "
-                           "\"partition_ok\": %s, \"strip_cols\": %d}",
+                           "\"partition_ok\": %s, \"strip_cols\": %d, "
+                           "\"plain_cost_us\": %.2f, \"streamk_cost_us\": %.2f}",
                            vi, v.name, sk ? "true" : "false", v.BM, v.BN, v.BK, cus, g.G,
                            (long long)(int64_t((M + v.BM - 1) / v.BM) *
                                        ((N - strip + v.BN - 1) / v.BN)),
@@ -687,7 +711,7 @@ extern "C" int sgemm_f32_streamk_describe(int M, int N, int K, int variant, int 
                            (long long)(sk ? g.iters : 0), (long long)shared,
                            (long long)max_contrib, (long long)max_segments,
                            sk ? streamk_workspace_bytes(v, g) : size_t(0), ok ? "true" : "false",
-                           strip);
+                           strip, c_plain / kUnitsPerUs, g.tiles_sk ? c_sk / kUnitsPerUs : 0.0);
     if (n < 0 || n >= buflen) return SGEMM_EINVAL_ARG;
     return vi;
 }

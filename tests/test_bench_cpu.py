@@ -46,7 +46,9 @@ def test_committed_traffic_entries_are_well_formed():
         if name.startswith("_"):
             continue
         assert entry["bytes_per_launch"] >= entry["compulsory_bytes"] * 0.9, name
-        assert len(entry["kernel_code_sha"]) == 16 and entry["variant"].startswith("mfma")
+        # a tile variant's name, or a stream-K plan's ("streamk_" + the variant's)
+        variant = entry["variant"].removeprefix("streamk_")
+        assert len(entry["kernel_code_sha"]) == 16 and variant.startswith("mfma")
         assert entry["kernel_symbol"].startswith(("_ZN5sgemm12k_sgemm_mfma",
                                                   "_ZN5sgemm16k_sgemm_regpanel",
                                                   "_ZN5sgemm15k_sgemm_persist"))

@@ -109,12 +109,13 @@ def test_streamk_workloads_float(gpu, name):
 
 
 def test_streamk_large_ragged_sampled(gpu):
-    """The ragged 4500x4500x8192 workload: its plan shares every 256 x 256 tile of the
-    register-panel kernel out as stream-K units (18 x 18 tiles on 256 workgroups). Sampled
-    rows, each over every column, against the oracle: first and last rows of tile rows and
-    the ragged last tile row."""
+    """The ragged 4500x4500x8192 workload with the register-panel kernel's stream-K form
+    forced: every 256 x 256 tile shared out as stream-K units (18 x 18 tiles on 256
+    workgroups). Sampled rows, each over every column, against the oracle: first and last
+    rows of tile rows and the ragged last tile row."""
     A, B = wl.operands("rk")
-    C, d = run_streamk(gpu, A, B)
+    rp = g.variant_names().index("mfma_256x256x32_w2x2_rp")
+    C, d = run_streamk(gpu, A, B, rp)
     assert d["streamk"] and d["name"] == "mfma_256x256x32_w2x2_rp", d
     rng = np.random.default_rng(7)
     rows = sorted({0, 1, 255, 256, 2047, 4095, 4096, 4351, 4352, 4480, 4498, 4499,

@@ -69,7 +69,7 @@ def _check(A, B, C, kind):
 
 # (M, N, K, forced variant name or None): the first call is the larger one; each plan
 # shares tiles, so its partial sums go through the scratch
-CALLS = [(1536, 1536, 4096, None), (300, 200, 5000, None),
+CALLS = [(512, 512, 8192, None), (300, 200, 5000, None),
          (1023, 1025, 1027, "mfma_64x64x32_w2x1_kg2_dl")]
 
 
