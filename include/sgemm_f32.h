@@ -170,9 +170,12 @@ size_t sgemm_f32_streamk_noalloc_scratch_bytes(void);
  * are shared and by at most how many workgroups, segments per workgroup, workspace bytes,
  * "partition_ok": the result of walking every range with the kernels' own partition
  * functions (every unit in exactly one range, every partial slot the fixup reads written
- * once for that tile), and for a plain plan the columns its last tile column computes as a
- * strip ("strip_cols"; the tile count then leaves them out). num_cus > 0 plans for that many compute units (no GPU needed);
- * num_cus <= 0 queries the current device. M, N and K must be positive (else
+ * once for that tile), for a plain plan the columns its last tile column computes as a
+ * strip ("strip_cols"; the tile count then leaves them out), and the two prices the choice
+ * compares, in microseconds at the cost model's unit rate: the cheapest plain plan
+ * ("plain_cost_us") and this variant as stream-K ("streamk_cost_us", 0 when it shares no
+ * tile). num_cus > 0 plans for that many compute units (no GPU needed); num_cus <= 0
+ * queries the current device. M, N and K must be positive (else
  * SGEMM_EINVAL_DIM). Returns the variant index, or a negative sgemm_status.
  */
 int sgemm_f32_streamk_describe(int M, int N, int K, int variant, int num_cus,
