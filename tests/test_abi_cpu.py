@@ -7,6 +7,7 @@ import re
 import pytest
 
 import fp32_gemm_f32_amd as g
+import workloads as wl
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sgemm_f32.h")
@@ -344,3 +345,37 @@ def test_one_hip_runtime_in_the_process():
     n = int(r.stdout.split()[0])
     assert n == 1, r.stdout
 
+
+
+# The plan's choices for the named workloads on 256 compute units (the kernels each
+# committed profile under profiles/ was taken on). A change to the cost model that moves
+# one of them needs new measurements.
+WORKLOAD_PLANS = {
+    "c1": ("mfma_128x256x16_w2x2_dl", 0),
+    "c2": ("mfma16_64x64x64_w2x2_kg2_dl", 0),
+    "c3": ("mfma16_64x64x64_w2x2_kg2_dl", 1),
+    "c4": ("mfma_256x256x32_w2x2_rp", 0),
+    "c5": ("mfma_128x256x32_w2x4_ps", 0),
+    "sk": ("mfma16_48x64x32_w1x2_kg4_dl", 0),
+    "rk": ("mfma16_80x64x32_w1x2_kg2_dl", 0),
+}
+
+
+@pytest.mark.parametrize("name", sorted(WORKLOAD_PLANS))
+def test_workload_plans(name):
+    w = wl.WORKLOADS[name]
+    plan = g.sgemm_f32_plan_describe(w.M, w.N, w.K, num_cus=256)
+    assert (plan["name"], plan["strip_cols"]) == WORKLOAD_PLANS[name], plan
+
+
+def test_workload_streamk_plans():
+    """Stream-K shares tiles where it pays (the under-filled 256 x 256 x 32768) and keeps
+    the plain grid on the ragged shapes, where the strip or the plain 80 x 64 grid wins."""
+    sk = wl.WORKLOADS["sk"]
+    d = g.sgemm_f32_streamk_describe(sk.M, sk.N, sk.K, num_cus=256)
+    assert d["streamk"] and d["name"] == "mfma16_64x64x64_w2x2_kg2_dl", d
+    assert d["streamk_cost_us"] < d["plain_cost_us"]
+    for name in ("c3", "rk"):
+        w = wl.WORKLOADS[name]
+        d = g.sgemm_f32_streamk_describe(w.M, w.N, w.K, num_cus=256)
+        assert not d["streamk"], d
