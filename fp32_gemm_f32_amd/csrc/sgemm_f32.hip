@@ -162,6 +162,10 @@ const VariantEntry kVariants[] = {
     regpanel_entry("mfma_256x256x32_w2x2_rp", 1.105, 20),
     persist_entry("mfma_128x256x32_w2x2_ps", 4, false, 1.05, 0),
     persist_entry("mfma_128x256x32_w2x4_ps", 8, true, 1.10, 0),
+    // 64 x 64 in 16-row blocks, two K-groups of four 32 x 32 waves, 32-deep panels (forced
+    // use only)
+    entry<64, 64, 32, 2, 2, 1, 2, true, false, 16>("mfma16_64x64x32_w2x2_kg2_dl", 2, 1.0, 26,
+                                                   0.887),
 };
 constexpr int kNumVariants = int(sizeof(kVariants) / sizeof(kVariants[0]));
 
