@@ -230,54 +230,97 @@ PLAN_SWEEP_SHAPES = [
     (1000, 1000, 4000), (2000, 2000, 512), (1536, 3072, 1024), (3072, 3072, 2048)]
 
 
-def plan_sweep(spec: str) -> int:
-    """The plan's choice against every planned variant forced, per shape, at steady state:
-    after at least 50 ms of launches, each candidate runs for about 1 ms of launches back to
-    back (at least 5), in two passes (the second in reverse order), each after the same 5 ms
-    of load; the faster pass counts. The regret is the plan's
-    variant's time over the fastest one's; the call through sgemm_f32 (the same kernel) is
-    timed last in each pass and reported beside. Operands are seeded normal draws made on
-    the device. One JSON line per shape, then a summary line."""
-    import torch
+class SteadyTimer:
+    """Times calls at steady state on cuda:0: at least 50 ms of a reference load first
+    (2048^3 through sgemm_f32, on operands of its own), then each candidate runs for about
+    1 ms of launches back to back (at least 5), in two passes (the second in reverse
+    order), each after the same 5 ms of load; the faster pass counts. Over a pass the card
+    warms and later candidates run at a lower clock, and the clock after a kernel depends
+    on that kernel's power draw for some milliseconds: the reverse pass and the equal
+    load before each candidate keep both from favouring a position."""
 
-    import fp32_gemm_f32_amd as g
-    shapes = (PLAN_SWEEP_SHAPES if spec == "default"
-              else [tuple(int(x) for x in t.split("x")) for t in spec.split(",")])
-    lib = g.library()
-    names = g.variant_names()
-    cands = g.planned_variants()
-    dev = torch.device("cuda:0")
-    stream = torch.cuda.current_stream(dev)
-    sp = stream.cuda_stream
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(17)
+    H = 2048
 
-    def timed(call, n):
+    def __init__(self):
+        import torch
+
+        import fp32_gemm_f32_amd as g
+        self.torch = torch
+        self.lib = g.library()
+        self.dev = torch.device("cuda:0")
+        self.stream = torch.cuda.current_stream(self.dev)
+        self.sp = self.stream.cuda_stream
+        self.gen = torch.Generator(device=self.dev)
+        self.gen.manual_seed(17)
+        H = self.H
+        self.heat_ab = torch.randn((H, H), device=self.dev, generator=self.gen)
+        self.heat_c = torch.empty((H, H), device=self.dev)
+        self.timed(self.heat, 600)
+
+    def heat(self):
+        H = self.H
+        assert self.heat_ab.numel() == H * H and self.heat_c.numel() == H * H
+        return self.lib.sgemm_f32(H, H, H, self.heat_ab.data_ptr(), H, self.heat_ab.data_ptr(),
+                                  H, self.heat_c.data_ptr(), H, self.sp)
+
+    def timed(self, call, n):
+        torch = self.torch
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
-        start.record(stream)
+        start.record(self.stream)
         for _ in range(n):
             call()
-        end.record(stream)
-        torch.cuda.synchronize(dev)
+        end.record(self.stream)
+        torch.cuda.synchronize(self.dev)
         return start.elapsed_time(end) * 1e3 / n
 
-    # the reference load has operands of its own (the shape loop below rebinds A, B and C)
-    H = 2048
-    heat_ab = torch.randn((H, H), device=dev, generator=gen)
-    heat_c = torch.empty((H, H), device=dev)
+    def operands(self, M, N, K):
+        """Seeded normal A (M x K) and B (K x N) made on the device, and C (M x N)."""
+        torch = self.torch
+        A = torch.randn((M, K), device=self.dev, generator=self.gen)
+        B = torch.randn((K, N), device=self.dev, generator=self.gen)
+        return A, B, torch.empty((M, N), device=self.dev)
 
-    def heat():
-        assert heat_ab.numel() == H * H and heat_c.numel() == H * H
-        return lib.sgemm_f32(H, H, H, heat_ab.data_ptr(), H, heat_ab.data_ptr(), H,
-                             heat_c.data_ptr(), H, sp)
+    def times(self, calls, n):
+        """{name: microseconds per call} (None for a call that returns an error)."""
+        times = {}
+        for rnd in range(2):
+            items = list(calls.items())
+            for name, call in (items if rnd == 0 else items[::-1]):
+                self.timed(self.heat, 40)
+                if call() != 0:
+                    times[name] = None
+                    continue
+                for _ in range(max(1, n // 4)):
+                    call()
+                t = self.timed(call, n)
+                times[name] = t if times.get(name) is None else min(times[name], t)
+        return times
 
-    timed(heat, 600)
+
+def _sweep_shapes(spec: str):
+    return (PLAN_SWEEP_SHAPES if spec == "default"
+            else [tuple(int(x) for x in t.split("x")) for t in spec.split(",")])
+
+
+def plan_sweep(spec: str, extra: str = "") -> int:
+    """The plan's choice against every planned variant forced (and the variants named in
+    `extra`, comma-separated, or every variant for 'all'), per shape, at steady state
+    (SteadyTimer). The regret is the plan's variant's time over the fastest one's; the call
+    through sgemm_f32 (the same kernel) is timed last in the first pass and reported
+    beside. One JSON line per shape, then a summary line."""
+    import fp32_gemm_f32_amd as g
+    st = SteadyTimer()
+    lib, sp = st.lib, st.sp
+    names = g.variant_names()
+    cands = g.planned_variants()
+    if extra == "all":
+        cands = list(range(len(names)))
+    elif extra:
+        cands += [names.index(x) for x in extra.split(",") if names.index(x) not in cands]
     regrets = []
-    for (M, N, K) in shapes:
-        A = torch.randn((M, K), device=dev, generator=gen)
-        B = torch.randn((K, N), device=dev, generator=gen)
-        C = torch.empty((M, N), device=dev)
+    for (M, N, K) in _sweep_shapes(spec):
+        A, B, C = st.operands(M, N, K)
         n = max(5, min(400, int(3e12 / (2.0 * M * N * K))))
 
         def gemm(v, A=A, B=B, C=C, M=M, N=N, K=K):
@@ -291,22 +334,7 @@ def plan_sweep(spec: str) -> int:
 
         calls = {names[v]: (lambda v=v: gemm(v)) for v in cands}
         calls["auto"] = lambda: gemm(-1)
-        times = {}
-        for rnd in range(2):
-            # the second pass runs in reverse order: over a pass the card warms and later
-            # candidates run at a lower clock, so each candidate gets one early slot
-            items = list(calls.items())
-            for name, call in (items if rnd == 0 else items[::-1]):
-                # the same 5 ms of load before every candidate: the clock after a kernel
-                # depends on that kernel's power draw for some milliseconds
-                timed(heat, 40)
-                if call() != 0:
-                    times[name] = None
-                    continue
-                for _ in range(max(1, n // 4)):
-                    call()
-                t = timed(call, n)
-                times[name] = t if times.get(name) is None else min(times[name], t)
+        times = st.times(calls, n)
         # the regret of the plan: its variant (forced, timed like the others) against the
         # fastest; the call through sgemm_f32 runs the same kernel and is reported beside
         plan = g.sgemm_f32_plan_describe(M, N, K)["name"]
@@ -323,6 +351,65 @@ def plan_sweep(spec: str) -> int:
     print(json.dumps({"plan_sweep": {"shapes": len(srt), "max_regret": round(srt[-1], 4),
                                      "median_regret": round(srt[len(srt) // 2], 4),
                                      "within_1pct": sum(r <= 0.01 for r in srt)}}), flush=True)
+    return 0
+
+
+SPLIT_SWEEP_SHAPES = [
+    (256, 256, 32768), (512, 512, 8192), (256, 256, 8192), (128, 128, 65536),
+    (1024, 256, 16384), (512, 512, 32768), (384, 384, 16384), (640, 640, 8192),
+    (2048, 256, 8192), (1024, 1024, 8192)]
+
+
+def split_sweep(spec: str, splits: str) -> int:
+    """Split-K's automatic split count (sgemm_f32_splitk with splits = 0) against the
+    counts listed in `splits`, the plain plan (sgemm_f32) and stream-K's automatic choice,
+    per shape, at steady state (SteadyTimer); each call includes its reduce or fixup
+    kernel. The regret is the automatic count's time over the fastest split count's
+    (1 being the plain plan). One JSON line per shape, then a summary line."""
+    import fp32_gemm_f32_amd as g
+    st = SteadyTimer()
+    lib, sp, torch = st.lib, st.sp, st.torch
+    counts = [int(x) for x in splits.split(",")]
+    shapes = SPLIT_SWEEP_SHAPES if spec == "default" else _sweep_shapes(spec)
+    regrets = []
+    for (M, N, K) in shapes:
+        A, B, C = st.operands(M, N, K)
+        auto = lib.sgemm_f32_splitk_workspace_size(M, N, K, 0) // (4 * M * N) or 1
+        need = max([lib.sgemm_f32_splitk_workspace_size(M, N, K, s) for s in counts + [auto]])
+        ws = torch.empty(max(need // 4, 1), device=st.dev)
+        sk_bytes = lib.sgemm_f32_streamk_workspace_size(M, N, K, K, N, N, -1)
+        sw = torch.empty(max(sk_bytes // 4, 1), device=st.dev)
+        n = max(5, min(400, int(3e12 / (2.0 * M * N * K))))
+
+        def split(s, A=A, B=B, C=C, M=M, N=N, K=K, ws=ws):
+            assert A.shape == (M, K) and B.shape == (K, N) and C.shape == (M, N)
+            return lib.sgemm_f32_splitk(M, N, K, A.data_ptr(), K, B.data_ptr(), N, C.data_ptr(),
+                                        N, s, ws.data_ptr(), ws.numel() * 4, sp)
+
+        def streamk(A=A, B=B, C=C, M=M, N=N, K=K, sw=sw):
+            assert A.shape == (M, K) and B.shape == (K, N) and C.shape == (M, N)
+            return lib.sgemm_f32_streamk(M, N, K, A.data_ptr(), K, B.data_ptr(), N,
+                                         C.data_ptr(), N, -1, sw.data_ptr(), sw.numel() * 4, sp)
+
+        calls = {"plain": lambda: split(1)}
+        calls.update({f"splitk{s}": (lambda s=s: split(s)) for s in counts if s > 1})
+        calls["splitk_auto"] = lambda: split(0)
+        calls["streamk_auto"] = streamk
+        times = st.times(calls, n)
+        split_times = {k: t for k, t in times.items()
+                       if k not in ("splitk_auto", "streamk_auto") and t is not None}
+        best = min((t, k) for k, t in split_times.items())
+        regret = times["splitk_auto"] / best[0] - 1.0
+        regrets.append(regret)
+        print(json.dumps({"shape": [M, N, K], "auto_splits": auto,
+                          "auto_us": round(times["splitk_auto"], 2), "best": best[1],
+                          "best_us": round(best[0], 2), "regret": round(regret, 4),
+                          "times_us": {k: (round(t, 2) if t is not None else None)
+                                       for k, t in times.items()}}), flush=True)
+    srt = sorted(regrets)
+    print(json.dumps({"split_sweep": {"shapes": len(srt), "max_regret": round(srt[-1], 4),
+                                      "median_regret": round(srt[len(srt) // 2], 4),
+                                      "within_2pct": sum(r <= 0.02 for r in srt)}}), flush=True)
     return 0
 
 
@@ -393,6 +480,17 @@ def main() -> int:
     ap.add_argument("--plan-sweep", default="",
                     help="time the plan's choice against every planned variant at steady "
                          "state on 'default' (40 shapes) or a list MxNxK,MxNxK,...")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="with --kernel splitk: the split count (0: the library's choice)")
+    ap.add_argument("--split-sweep", default="",
+                    help="time split-K's automatic split count against --sweep-splits, the "
+                         "plain plan and stream-K on 'default' (10 under-filled shapes) or a "
+                         "list MxNxK,...")
+    ap.add_argument("--sweep-splits", default="2,4,8,16,32",
+                    help="with --split-sweep: the split counts to time")
+    ap.add_argument("--sweep-variants", default="",
+                    help="with --plan-sweep: also time these variants (names, comma-separated; "
+                         "'all' for every variant)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run a plain device copy of this size instead (counter scaling)")
     args = ap.parse_args()
@@ -402,7 +500,9 @@ def main() -> int:
             "product would shard C by output tiles, each GPU running this kernel on its share)")
         return 2
     if args.plan_sweep:
-        return plan_sweep(args.plan_sweep)
+        return plan_sweep(args.plan_sweep, args.sweep_variants)
+    if args.split_sweep:
+        return split_sweep(args.split_sweep, args.sweep_splits)
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib, max(args.steps, 1))
         return 0
@@ -436,11 +536,12 @@ def main() -> int:
     gemm = call_args[:-1]
     ws = None
     if kern == "splitk":
-        ws_bytes = lib.sgemm_f32_splitk_workspace_size(M, N, K, 0)
+        ws_bytes = lib.sgemm_f32_splitk_workspace_size(M, N, K, args.splits)
         ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device=dev)
         plan["splitk_workspace_bytes"] = ws_bytes
         plan["splits"] = ws_bytes // (4 * M * N) if ws_bytes else 1
-        plan["name"] = f"splitk{plan['splits']}+reduce"
+        plan["name"] = (f"splitk{plan['splits']}+reduce" if plan["splits"] > 1
+                        else "splitk1 (the plain plan)")
         plan["BM"] = plan["BN"] = plan["BK"] = plan["grid"] = None   # chosen per split count
     if kern == "streamk":
         sk_plan = g.sgemm_f32_streamk_describe(M, N, K, args.variant)
@@ -464,7 +565,8 @@ def main() -> int:
             rc = (lib.sgemm_f32(*call_args) if args.variant < 0
                   else lib.sgemm_f32_variant(args.variant, *call_args))
         elif kern == "splitk":
-            rc = lib.sgemm_f32_splitk(*gemm, 0, ws.data_ptr(), plan["splitk_workspace_bytes"], sp)
+            rc = lib.sgemm_f32_splitk(*gemm, plan["splits"], ws.data_ptr(),
+                                      plan["splitk_workspace_bytes"], sp)
         elif kern == "streamk":
             rc = lib.sgemm_f32_streamk(*gemm, args.variant, ws.data_ptr(),
                                        plan["streamk_workspace_bytes"], sp)

@@ -20,7 +20,8 @@
 //    hardware form of the pages' (TM + TN) reads per TM * TN multiply-adds.
 //  * Software pipelining ("Shared Memory Tiling", "What tiling does not fix"): two LDS
 //    stages; the global loads of panel p+1 are in flight while the MFMAs consume panel
-//    p, so each panel costs one barrier instead of two.
+//    p, so each panel costs one barrier instead of two. NSTG = 3 makes a ring of three
+//    stages, with the loads of panel p+2 in flight during panel p.
 //
 // gfx950 specifics:
 //  * Loads use buffer resources. A lane whose element lies outside the matrix gets the
@@ -150,6 +151,28 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc32(const float *base, uint32_t
 __device__ inline f32x4 load_b128(__amdgpu_buffer_rsrc_t r, uint32_t voff)
 {
     return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
+// s_waitcnt vmcnt(N): all but the last N vector memory loads this wave issued have landed
+// (the gfx9 family counts them done in issue order).
+template <int N>
+__device__ inline void wait_vmcnt()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt holds 6 bits");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// wait_vmcnt<N_FIRST> in the wave where `first` holds (wave-uniform), wait_vmcnt<N_OTHER> in
+// the others
+template <int N_FIRST, int N_OTHER>
+__device__ inline void wait_vmcnt_split(bool first)
+{
+    if constexpr (N_FIRST == N_OTHER) {
+        wait_vmcnt<N_OTHER>();
+    } else {
+        if (first) wait_vmcnt<N_FIRST>();
+        else wait_vmcnt<N_OTHER>();
+    }
 }
 
 // Calls f(std::integral_constant<int, I>) for I = BEGIN .. END-1, so I is a constant
@@ -301,7 +324,8 @@ template <> struct MfmaShape<16> {
     static constexpr int row(int v) { return v; }
 };
 
-template <int BM, int BN, int BK, int WGM, int WGN, int KACC = 1, int KG = 1, int MB = 32>
+template <int BM, int BN, int BK, int WGM, int WGN, int KACC = 1, int KG = 1, int MB = 32,
+          int NSTG = 2>
 struct MfmaTile {
     static constexpr int kGroupThreads = 64 * WGM * WGN;   // one K-group of waves
     static constexpr int kThreads = kGroupThreads * KG;
@@ -328,14 +352,15 @@ struct MfmaTile {
     // which write the same rows' sums into H different rows, hit different banks.
     static constexpr int STRIP_STAGE = 64;
     static constexpr int STRIP_RS = (BM + 63) / 64 * 64 + 64 / MfmaShape<MB>::H;
-    static constexpr int STRIP_FLOATS = 2 * KG * STRIP_STAGE + KG * MfmaShape<MB>::H * STRIP_RS;
-    static constexpr bool STRIP_OK = BM <= kGroupThreads * KG && BK <= 64 &&
-                                     RED <= 2 * KG * STAGE &&
-                                     (2 * KG * STAGE + STRIP_FLOATS) * 4 <= 160 * 1024;
-    static constexpr int BASE_FLOATS = 2 * KG * STAGE > RED ? 2 * KG * STAGE : RED;
+    static constexpr int STRIP_FLOATS =
+        NSTG * KG * STRIP_STAGE + KG * MfmaShape<MB>::H * STRIP_RS;
+    // NSTG LDS stages per K-group
+    static constexpr int STAGES = NSTG * KG * STAGE;
+    static constexpr bool STRIP_OK = BM <= kGroupThreads * KG && BK <= 64 && RED <= STAGES &&
+                                     (STAGES + STRIP_FLOATS) * 4 <= 160 * 1024;
+    static constexpr int BASE_FLOATS = STAGES > RED ? STAGES : RED;
     static constexpr int LDS_FLOATS =
-        STRIP_OK && 2 * KG * STAGE + STRIP_FLOATS > BASE_FLOATS ? 2 * KG * STAGE + STRIP_FLOATS
-                                                                 : BASE_FLOATS;
+        STRIP_OK && STAGES + STRIP_FLOATS > BASE_FLOATS ? STAGES + STRIP_FLOATS : BASE_FLOATS;
     static constexpr int LDS_BYTES = LDS_FLOATS * 4;
     static_assert(WM % MB == 0 && WN % MB == 0, "wave tile is made of MB x MB blocks");
     static_assert(WN % (MB * CI) == 0, "column groups");
@@ -366,10 +391,11 @@ struct MfmaTile {
 // range of K-panel units (streamk.hpp): whole tiles go to C, partial ones to its two
 // workspace slots.
 template <int BM, int BN, int BK, int WGM, int WGN, int KACC, int KG, bool DL, bool SK = false,
-          int MB = 32>
+          int MB = 32, int NSTG = 2>
 __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
 {
-    using T = MfmaTile<BM, BN, BK, WGM, WGN, KACC, KG, MB>;
+    static_assert(NSTG == 2 || (NSTG == 3 && DL), "two LDS stages, or three with direct loads");
+    using T = MfmaTile<BM, BN, BK, WGM, WGN, KACC, KG, MB, NSTG>;
     using S = MfmaShape<MB>;
     typedef typename S::acc_t acc_t;
     constexpr int NT = T::kGroupThreads, WM = T::WM, WN = T::WN, RB = T::RB, CI = T::CI,
@@ -634,7 +660,8 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     // two K-groups, and slower for the short-K 128 x 256 x 16 tile (whose epilogue
     // dominates), the 256 x 256 ones (which then spill) and four K-groups (few panels each).
     constexpr bool PAIR = DL && BK >= 32 && BM * BN <= 128 * 128 && KG <= 2;
-    int panel_parity = 0;   // the stage of the current panel is panel_parity & 1 (no PAIR)
+    // the stage of the current panel is panel_parity % NSTG where the stage is not a constant
+    int panel_parity = 0;
     constexpr int LS = SGEMM_LOAD_STEPS;
     constexpr int WS = SGEMM_WRITE_STEPS;
     constexpr int PER_LOAD = (NL + LS - 1) / LS;
@@ -656,8 +683,8 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     // the others. Spreading the strip's rows over every tile of a row costs every tile
     // about that much, which is worse once the tiles take more than one round.)
     constexpr bool CAN_STRIP = !SK && DL && T::STRIP_OK;
-    float *const strip_lds = lds_all + 2 * KG * T::STAGE;
-    float *const strip_red = strip_lds + 2 * KG * T::STRIP_STAGE;
+    float *const strip_lds = lds_all + T::STAGES;
+    float *const strip_red = strip_lds + NSTG * KG * T::STRIP_STAGE;
     __amdgpu_buffer_rsrc_t rss;
     uint32_t s_off = kOob;
     float sacc[RB];
@@ -693,24 +720,41 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
         }
     };
 
-    // NEXT (next_tag 1 or 2): the panel stages the next one; 2 (NextTail): that next panel
-    // is its group's last, which may hold the end of the K range (fix_k_tail applies to it;
-    // no other panel's code carries the tail's branch).
+    // NEXT (next_tag 1 or 2): a next panel follows, whose step 0 this one reads after its
+    // barrier; 2 (NextTail): that next panel is its group's last, which may hold the end of
+    // the K range (fix_k_tail applies to it; no other panel's code carries the tail's
+    // branch). LOADS: the panel issues the global loads of a later one, into the stage read
+    // longest ago: with two stages the next panel (every NEXT panel), with three the panel
+    // after next (next_tag 1 only: the last but one panel loads nothing), so that two
+    // panels' loads are in flight and each has two panels' time to land.
     // NS: the k-steps of the panel that run. A group's last panel runs only the k-groups
     // (4 steps each) that hold values of k inside its range; every other panel runs all.
     // STRIP: the panel also loads the next panel's strip values and computes this one's.
     using NextTail = std::integral_constant<int, 2>;
+    // The barrier after a panel, once the wave's loads of the next one have landed. With
+    // three stages __syncthreads() would also wait for the loads still in flight (the
+    // panel after next); only the LDS accesses need ordering there: each wave waits for its
+    // own loads before it, and for its LDS reads and fix_k_tail's writes in it.
+    auto stage_barrier = [&]() __attribute__((always_inline)) {
+        if constexpr (NSTG == 2) __syncthreads();
+        else asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
     auto panel = [&](auto cur_tag, auto next_tag, auto ns_tag, auto strip_tag) __attribute__((always_inline)) {
         constexpr bool STRIP = decltype(strip_tag)::value;
         constexpr bool NEXT = decltype(next_tag)::value != 0;
         constexpr bool TAIL_NEXT = decltype(next_tag)::value == 2;
-        constexpr int cur = decltype(cur_tag)::value;   // -1: the stage parity known at run time
+        constexpr bool LOADS = NSTG == 2 ? NEXT : decltype(next_tag)::value == 1;
+        constexpr int cur = decltype(cur_tag)::value;   // -1: the stage known at run time
         constexpr int NS = decltype(ns_tag)::value;
         static_assert(NS % 4 == 0 && NS <= STEPS && (NS == STEPS || !NEXT), "steps of a panel");
-        const int cur_stage = cur < 0 ? (panel_parity & 1) : cur;
+        const int cur_stage = cur >= 0 ? cur : NSTG == 2 ? (panel_parity & 1) : panel_parity % 3;
         const float *As = smem + cur_stage * SSTRIDE;
         const float *Bs = As + T::A_TILE;
-        float *Anext = smem + (cur_stage ^ 1) * SSTRIDE;
+        // the stage read after the barrier (Anext), and the one the loads go to (load_stage,
+        // Aload); with two stages both are the other stage
+        float *Anext = smem + (NSTG == 2 ? cur_stage ^ 1 : cur_stage == 2 ? 0 : cur_stage + 1) * SSTRIDE;
+        const int load_stage = NSTG == 2 ? cur_stage ^ 1 : cur_stage == 0 ? 2 : cur_stage - 1;
+        float *Aload = NSTG == 2 ? Anext : smem + load_stage * SSTRIDE;
         const float *Ss = strip_lds + (cur_stage * KG + kg) * T::STRIP_STAGE;
         static_for<0, NS>([&](auto tc) {
             constexpr int t = decltype(tc)::value;
@@ -719,32 +763,32 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
             constexpr bool next_a = s == 0 && 4 * (kb + 1) < NS;
             constexpr int w0 = t - (STEPS - 1 - WS);            // write group of this step
             constexpr int l_first = t * PER_LOAD;
-            constexpr int n_load = (NEXT && t < LS)
+            constexpr int n_load = (LOADS && t < LS)
                 ? ((t + 1) * PER_LOAD < NL ? PER_LOAD : (NL - t * PER_LOAD > 0 ? NL - t * PER_LOAD : 0))
                 : 0;
             constexpr int w_first = (w0 > 0 ? w0 : 0) * PER_WRITE;
-            constexpr int n_write = (NEXT && !DL && w0 >= 0 && w0 < WS)
+            constexpr int n_write = (LOADS && !DL && w0 >= 0 && w0 < WS)
                 ? ((w0 + 1) * PER_WRITE < NL ? PER_WRITE
                                              : (NL - w0 * PER_WRITE > 0 ? NL - w0 * PER_WRITE : 0))
                 : 0;
             if constexpr (n_load > 0) {
 #pragma unroll
                 for (int l = l_first; l < l_first + n_load; ++l) {
-                    if constexpr (DL) load_direct(Anext, l); else load_slot(l);
+                    if constexpr (DL) load_direct(Aload, l); else load_slot(l);
                 }
             }
             // strip: the next panel's B values with the first loads; k-group kb's B values
             // read at its first step and its products added at its third
-            constexpr int n_sload = (STRIP && NEXT && t == 0) ? 1 : 0;
+            constexpr int n_sload = (STRIP && LOADS && t == 0) ? 1 : 0;
             constexpr bool s_rd = STRIP && s == 0;
             constexpr bool s_fma = STRIP && s == 2;
-            if constexpr (n_sload > 0) strip_load(cur_stage ^ 1);
+            if constexpr (n_sload > 0) strip_load(NSTG == 2 ? cur_stage ^ 1 : load_stage);
             if constexpr (s_fma) strip_fma(a[kb & 1]);
             if constexpr (s_rd)
                 sbv = *reinterpret_cast<const f32x4 *>(Ss + 4 * (S::H * kb + hi));
             if constexpr (n_write > 0) {
 #pragma unroll
-                for (int l = w_first; l < w_first + n_write; ++l) write_slot(Anext, l);
+                for (int l = w_first; l < w_first + n_write; ++l) write_slot(Aload, l);
             }
             if constexpr (next_b) read_b(Bs, t + 1, b[(t + 1) & 1]);
             if constexpr (next_a) read_a(As, kb + 1, a[(kb + 1) & 1]);
@@ -754,10 +798,13 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
                 __builtin_amdgcn_sched_barrier(0);
                 // direct loads land in LDS when vmcnt counts them done
                 if constexpr (DL) {
-                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                    if constexpr (NSTG == 3 && LOADS)
+                        wait_vmcnt_split<STRIP ? NL + 1 : NL, NL>(wave_u == 0);
+                    else
+                        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                     if constexpr (TAIL_NEXT) fix_k_tail(Anext);
                 }
-                __syncthreads();
+                stage_barrier();
                 read_a(Anext, 0, a[0]);
                 read_b(Anext + T::A_TILE, 0, b[0]);
             }
@@ -966,33 +1013,87 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
             };
             set_item();
             if constexpr (STRIP) set_strip_item();
+            // rounds of panels of this group; a group whose last panel lies past the K range
+            // loads only zeros for it
+            auto group_rounds = [&]() { return ((lK + BK - 1) / BK + KG - 1) / KG; };
             setp(kg * BK);
             if constexpr (DL) {
 #pragma unroll
                 for (int l = 0; l < NL; ++l) load_direct(smem, l);
                 if constexpr (STRIP) strip_load(0);
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                fix_k_tail(smem);
+                if constexpr (NSTG == 3) {
+                    if (group_rounds() > 1) {
+                        // the second panel's loads too, left in flight (the first panel is
+                        // not its group's last, so it holds no end of the K range)
+                        setp((KG + kg) * BK);
+#pragma unroll
+                        for (int l = 0; l < NL; ++l) load_direct(smem + SSTRIDE, l);
+                        if constexpr (STRIP) strip_load(1);
+                        wait_vmcnt_split<STRIP ? NL + 1 : NL, NL>(wave_u == 0);
+                    } else {
+                        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                        fix_k_tail(smem);
+                    }
+                } else {
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                    fix_k_tail(smem);
+                }
             } else {
 #pragma unroll
                 for (int l = 0; l < NL; ++l) load_slot(l);
 #pragma unroll
                 for (int l = 0; l < NL; ++l) write_slot(smem, l);
             }
-            __syncthreads();
+            stage_barrier();
             read_a(smem, 0, a[0]);
             read_b(smem + T::A_TILE, 0, b[0]);
 
-            // the last round stages nothing; a group whose last panel lies past the K range
-            // loads only zeros for it
-            const int rounds = ((lK + BK - 1) / BK + KG - 1) / KG;
+            const int rounds = group_rounds();
             // The loops never stage the last round's panel: the last two rounds run after
             // them, with the LDS stage known at run time, so the tail's code (the panel that
-            // stages the last round's panel, and the trimmed copies of the last panel)
-            // exists once and no loop iteration carries it.
+            // reads the last round's panel first, and the trimmed copies of the last panel)
+            // exists once and no loop iteration carries it. The last round stages nothing,
+            // and with three stages neither does the one before it.
             using SR = std::integral_constant<int, -1>;
             int r = 0;
-            if constexpr (PAIR) {
+            if constexpr (NSTG == 3) {
+                // panel r loads panel r + 2; unrolled by three (constant stages) as PAIR is
+                // by two
+                using S0 = std::integral_constant<int, 0>;
+                using S1 = std::integral_constant<int, 1>;
+                using S2 = std::integral_constant<int, 2>;
+                if constexpr (PAIR) {
+                    for (; r + 4 < rounds; r += 3) {
+                        setp(((r + 2) * KG + kg) * BK);
+                        panel(S0{}, std::true_type{}, AllSteps{}, strip_tag);
+                        setp(((r + 3) * KG + kg) * BK);
+                        panel(S1{}, std::true_type{}, AllSteps{}, strip_tag);
+                        setp(((r + 4) * KG + kg) * BK);
+                        panel(S2{}, std::true_type{}, AllSteps{}, strip_tag);
+                    }
+                    if (r + 2 < rounds) {
+                        setp(((r + 2) * KG + kg) * BK);
+                        panel(S0{}, std::true_type{}, AllSteps{}, strip_tag);
+                        ++r;
+                    }
+                    if (r + 2 < rounds) {
+                        setp(((r + 2) * KG + kg) * BK);
+                        panel(S1{}, std::true_type{}, AllSteps{}, strip_tag);
+                        ++r;
+                    }
+                } else {
+                    for (; r + 2 < rounds; ++r) {
+                        setp(((r + 2) * KG + kg) * BK);
+                        panel_parity = r;
+                        panel(SR{}, std::true_type{}, AllSteps{}, strip_tag);
+                    }
+                }
+                // the last round's loads were issued two panels ago (or in the prologue)
+                if (r + 1 < rounds) {
+                    panel_parity = r;
+                    panel(SR{}, NextTail{}, AllSteps{}, strip_tag);
+                }
+            } else if constexpr (PAIR) {
                 // two panels per iteration, so each one's LDS stage is a constant and its
                 // operand reads carry the stage in their immediate offsets (no address
                 // arithmetic on the vector ALU between the MFMAs)
@@ -1016,10 +1117,12 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
                     panel(SR{}, std::true_type{}, AllSteps{}, strip_tag);
                 }
             }
-            if (r + 1 < rounds) {
-                setp(((r + 1) * KG + kg) * BK);
-                panel_parity = r;
-                panel(SR{}, NextTail{}, AllSteps{}, strip_tag);
+            if constexpr (NSTG == 2) {
+                if (r + 1 < rounds) {
+                    setp(((r + 1) * KG + kg) * BK);
+                    panel_parity = r;
+                    panel(SR{}, NextTail{}, AllSteps{}, strip_tag);
+                }
             }
             panel_parity = rounds - 1;
             last_panel(SR{}, rounds, strip_tag);

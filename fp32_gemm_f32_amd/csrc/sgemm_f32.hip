@@ -71,27 +71,29 @@ struct VariantEntry {
     const char *kernel;     // kernel family: "mfma" (kernel_mfma.hpp), "regpanel", "persist"
     bool persistent = false;       // one workgroup per CU walks the tiles (kernel_persist.hpp)
     MfmaKernel kern_ktail = nullptr;   // its form for a K that is not a multiple of BK
+    int stages = 2;                    // LDS stages per K-group (the template kernel)
 };
 
 // PLANNED variants also get a stream-K form and its fixup kernel; the others are never
 // planned and are instantiated in their plain form only.
 template <int BM, int BN, int BK, int WGM, int WGN, int KACC, int KG, bool DL, bool PLANNED,
-          int MB = 32>
+          int MB = 32, int NSTG = 2>
 constexpr VariantEntry entry(const char *name, int wg_per_cu, double rate, double overhead,
                              double solo, double sk_price = kStreamkPrice)
 {
     MfmaKernel sk = nullptr, fix = nullptr;
     if constexpr (PLANNED) {
-        sk = &k_sgemm_mfma<BM, BN, BK, WGM, WGN, KACC, KG, DL, true, MB>;
+        sk = &k_sgemm_mfma<BM, BN, BK, WGM, WGN, KACC, KG, DL, true, MB, NSTG>;
         fix = &k_streamk_fixup<BM, BN>;
     }
     VariantEntry e{
         Variant{name, BM, BN, BK, WGM, WGN, wg_per_cu, rate, overhead, solo, DL, PLANNED},
-        &k_sgemm_mfma<BM, BN, BK, WGM, WGN, KACC, KG, DL, false, MB>, sk, fix,
+        &k_sgemm_mfma<BM, BN, BK, WGM, WGN, KACC, KG, DL, false, MB, NSTG>, sk, fix,
         64 * WGM * WGN * KG, MB, KG, "mfma"};
     // the kernel's column strip (kernel_mfma.hpp): direct loads and room in LDS
-    e.v.strip = DL && MfmaTile<BM, BN, BK, WGM, WGN, KACC, KG, MB>::STRIP_OK;
+    e.v.strip = DL && MfmaTile<BM, BN, BK, WGM, WGN, KACC, KG, MB, NSTG>::STRIP_OK;
     e.v.sk_price = sk_price;
+    e.stages = NSTG;
     return e;
 }
 
@@ -128,8 +130,9 @@ VariantEntry persist_entry(const char *name, int waves, bool planned, double rat
 
 // Rates (throughput at 8192^3 relative to 140 TFLOP/s), per-tile overheads (in units of K)
 // and solo factors are fitted on MI355X to runs that timed every variant on 19 shapes from
-// 1023 x 1025 x 1027 to 16384^2 x 64; the plan then picks a variant within 1 % of the
-// measured best on all of them. The template kernel's planned variants load their panels
+// 1023 x 1025 x 1027 to 16384^2 x 64, and checked at steady state on 40 shapes (bench.py
+// --plan-sweep): the plan's pick is within 1 % of the fastest variant on 37 of them and
+// within 3.2 % on all. The template kernel's planned variants load their panels
 // straight into LDS ("_dl"), which measured as fast as or faster than staging through
 // registers on every one of those shapes.
 //  * 256 x 256, one wave per SIMD ("_rp", kernel_regpanel.hpp): long K and many tiles
@@ -166,6 +169,13 @@ const VariantEntry kVariants[] = {
     // use only)
     entry<64, 64, 32, 2, 2, 1, 2, true, false, 16>("mfma16_64x64x32_w2x2_kg2_dl", 2, 1.0, 26,
                                                    0.887),
+    // the same tile and the 32 x 32 one of two K-groups with three LDS stages per K-group:
+    // each panel's loads are issued two panels ahead (96 KiB of LDS, one workgroup per CU;
+    // forced use only)
+    entry<64, 64, 32, 2, 2, 1, 2, true, false, 16, 3>("mfma16_64x64x32_w2x2_kg2_s3_dl", 1, 1.0,
+                                                      26, 1.0),
+    entry<64, 64, 32, 2, 1, 1, 2, true, false, 32, 3>("mfma_64x64x32_w2x1_kg2_s3_dl", 1, 1.0, 92,
+                                                      1.0),
 };
 constexpr int kNumVariants = int(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -348,17 +358,31 @@ void splitk_geometry(int K, int BK, int splits, int *eff, int *k_chunk)
     *eff = (K + *k_chunk - 1) / *k_chunk;
 }
 
-// Splits chosen automatically: enough items to give every CU about two, each range at
-// least four panels long, at most kMaxSplits.
+// Splits chosen automatically: the count the cost model prices lowest, each range at least
+// four 64-deep panels long, at most kMaxSplits. A count's price is the hot kernel's (the
+// busiest CU's time for the variant the plan takes with that many items per tile) plus
+// the reduce's, which reads the partial slices and writes C. Measured at steady state on
+// eight under-filled shapes from 128^2 x 65536 to 640^2 x 8192, the prices follow the
+// times within a few per cent.
 constexpr int kMaxSplits = 32;
+constexpr double kReduceUs = 2.0;              // the reduce kernel's launch and latency
+constexpr double kReduceBytesPerUs = 4e6;      // the rate at which it streams the slices
 int auto_splits(const Operands &o, int cus)
 {
-    const int64_t tiles = ((int64_t(o.M) + 63) / 64) * ((int64_t(o.N) + 63) / 64);
-    int64_t s = (2 * int64_t(cus) + tiles - 1) / tiles;
-    const int64_t by_k = o.K / (4 * 64);
-    if (s > by_k) s = by_k;
-    if (s > kMaxSplits) s = kMaxSplits;
-    return s < 1 ? 1 : int(s);
+    int64_t by_k = o.K / (4 * 64);
+    if (by_k > kMaxSplits) by_k = kMaxSplits;
+    int best = 1;
+    double best_us = -1.0;
+    for (int s = 1; s <= by_k || s == 1; ++s) {
+        Operands q = o;
+        q.splits = s;
+        const int vi = choose_variant(g_table, q, cus);
+        if (vi < 0) continue;
+        double us = variant_cost(g_table[vi], q, cus) / kUnitsPerUs;
+        if (s > 1) us += kReduceUs + double(s + 1) * double(o.M) * o.N * 4.0 / kReduceBytesPerUs;
+        if (best_us < 0.0 || us < best_us) { best = s; best_us = us; }
+    }
+    return best;
 }
 
 int run_splitk(int splits, const Operands &o0, const float *A, const float *B, float *C,
@@ -818,13 +842,13 @@ extern "C" int sgemm_f32_variant_info(int variant, char *buf, int buflen)
                            "\"direct_loads\": %s, \"planned\": %s, \"streamk\": %s, "
                            "\"rate\": %.3f, \"overhead\": %.1f, \"solo\": %.2f, "
                            "\"kernel\": \"%s\", \"splitk\": %s, \"persistent\": %s, "
-                           "\"whole_tiles\": %s, \"strip\": %s}",
+                           "\"whole_tiles\": %s, \"strip\": %s, \"lds_stages\": %d}",
                            variant, v.name, v.BM, v.BN, v.BK, v.wgm, v.wgn, e.kg, e.threads, e.mb,
                            e.mb, e.mb == 32 ? 2 : 4, v.wg_per_cu, v.direct ? "true" : "false",
                            v.planned ? "true" : "false", e.kern_sk ? "true" : "false", v.rate,
                            v.overhead, v.solo, e.kernel, v.splitk ? "true" : "false",
                            e.persistent ? "true" : "false", v.whole_tiles ? "true" : "false",
-                           v.strip ? "true" : "false");
+                           v.strip ? "true" : "false", e.stages);
     if (n < 0 || n >= buflen) return SGEMM_EINVAL_ARG;
     return SGEMM_OK;
 }

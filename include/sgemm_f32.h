@@ -77,8 +77,10 @@ int sgemm_f32(int M, int N, int K,
  * K is cut into `splits` ranges of whole K-panels; the hot kernel computes each
  * (tile, range) item into its own M x N slice of `workspace` (packed rows of N floats),
  * and a second kernel sums the slices in ascending range order into C, so repeated calls
- * give identical bits. splits = 0 lets the library choose (about two items per compute
- * unit, ranges of at least four panels); splits = 1 is sgemm_f32. At most 32.
+ * give identical bits. splits = 0 lets the library choose: the count whose estimated time
+ * (the busiest compute unit's items, plus the reduce's pass over the slices) is lowest,
+ * with ranges of at least four 64-deep panels; it may be 1, which runs sgemm_f32's plan.
+ * splits = 1 is sgemm_f32. At most 32.
  * workspace is a caller-owned device buffer of at least splits * M * N * 4 bytes
  * (sgemm_f32_splitk_workspace_size) that must not overlap A, B or C (SGEMM_EINVAL_PTR if
  * NULL or misaligned, SGEMM_EINVAL_ARG if too small, SGEMM_EALIAS on overlap; checked
@@ -271,8 +273,10 @@ const char *sgemm_f32_variant_name(int variant);
  * ("mfma": the LDS-double-buffered template; "regpanel": the one-wave-per-SIMD kernel;
  * "persist": the persistent kernel), whether split-K may use it, whether it runs one
  * workgroup per CU over the tiles ("persistent"), whether it only takes whole tiles
- * ("whole_tiles") and whether the tiles of its last tile column can also compute one
- * column of N past it, on the vector ALUs ("strip"). Host-only, no GPU needed. Returns SGEMM_OK, or
+ * ("whole_tiles"), whether the tiles of its last tile column can also compute one
+ * column of N past it, on the vector ALUs ("strip"), and the LDS stages per K-group of the
+ * template kernel ("lds_stages": 2, or 3 where each panel's loads are issued two panels
+ * ahead; "Shared Memory Tiling", "What tiling does not fix"). Host-only, no GPU needed. Returns SGEMM_OK, or
  * SGEMM_EINVAL_ARG for a bad index or a buffer too small.
  */
 int sgemm_f32_variant_info(int variant, char *buf, int buflen);

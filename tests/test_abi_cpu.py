@@ -323,6 +323,10 @@ def test_variant_info():
             assert info["streamk"] == info["planned"]
         assert info["direct_loads"] == name.endswith("_dl")
         assert f"{info['BM']}x{info['BN']}x{info['BK']}" in name
+        # three LDS stages only in the template kernel with direct loads, named _s3
+        assert info["lds_stages"] == (3 if "_s3_" in name else 2)
+        if info["lds_stages"] == 3:
+            assert info["kernel"] == "mfma" and info["direct_loads"] and not info["planned"]
     with pytest.raises(g.SgemmError):
         g.sgemm_f32_variant_info(len(names))
     buf = ctypes.create_string_buffer(8)

@@ -54,6 +54,16 @@ def test_committed_traffic_entries_are_well_formed():
                                                   "_ZN5sgemm15k_sgemm_persist"))
 
 
+def test_default_workload_traffic_is_current():
+    """The default bench line (8192^3) reports measured HBM traffic only while the counters
+    were taken on the machine code that runs now: the committed record must match the
+    current build's kernel and plan."""
+    import fp32_gemm_f32_amd as g
+    plan = g.sgemm_f32_plan_describe(8192, 8192, 8192, 1 << 40, None, (1 << 40) + (1 << 30),
+                                     None, (1 << 40) + (1 << 31), None, num_cus=256)
+    assert bench.measured_traffic("c4", plan["name"]) is not None
+
+
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, cwd=ROOT, timeout=120)
