@@ -1,7 +1,9 @@
 // sgemm_persist.hip -- the persistent store-overlapped kernel (kernel_persist.hpp) in a
-// translation unit of its own: its two sets of 128 accumulators per lane live in AGPRs,
-// which the build options of the rest of the library rule out (they keep MFMA accumulators
-// in VGPRs).
+// translation unit of its own. Its 4-wave form (one 64 x 128 wave per SIMD) holds two sets
+// of 128 accumulators per lane, which fit only with the accumulators in AGPRs, and the
+// build options of the rest of the library rule that out (they keep MFMA accumulators in
+// VGPRs). The 8-wave form's two sets of 64 per lane (two 64 x 64 waves per SIMD) fit in
+// VGPRs, where the compiler keeps them (238 VGPRs, no AGPRs).
 #include <hip/hip_runtime.h>
 
 #include "kernel_persist.hpp"
