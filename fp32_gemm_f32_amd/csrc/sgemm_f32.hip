@@ -131,8 +131,8 @@ VariantEntry persist_entry(const char *name, int waves, bool planned, double rat
 // Rates (throughput at 8192^3 relative to 140 TFLOP/s), per-tile overheads (in units of K)
 // and solo factors are fitted on MI355X to runs that timed every variant on 19 shapes from
 // 1023 x 1025 x 1027 to 16384^2 x 64, and checked at steady state on 40 shapes (bench.py
-// --plan-sweep): the plan's pick is within 1 % of the fastest variant on 37 of them and
-// within 3.2 % on all. The template kernel's planned variants load their panels
+// --plan-sweep): the plan's pick is within 1 % of the fastest variant on 39 of them and
+// within 3.0 % on all. The template kernel's planned variants load their panels
 // straight into LDS ("_dl"), which measured as fast as or faster than staging through
 // registers on every one of those shapes.
 //  * 256 x 256, one wave per SIMD ("_rp", kernel_regpanel.hpp): long K and many tiles
@@ -176,6 +176,17 @@ const VariantEntry kVariants[] = {
                                                       26, 1.0),
     entry<64, 64, 32, 2, 1, 1, 2, true, false, 32, 3>("mfma_64x64x32_w2x1_kg2_s3_dl", 1, 1.0, 92,
                                                       1.0),
+    // Tiles of one 32 x 32 block per wave for products with few 64 x 64 tiles (under one per
+    // CU): 32 x 32 as eight K-groups of one wave (two per SIMD) with three LDS stages, whose
+    // 16-deep panels are too short for two stages to hide a load (the two-stage form stays as
+    // the measured comparison, forced use only); and 32 x 64 as four K-groups of two waves.
+    // Fitted at steady state on 512^2 x 2048 .. 8192, 384^2 x 4096, 1024 x 512 x 2048 and
+    // 640^2 x 4096. Their stream-K forms are not planned (not calibrated).
+    entry<32, 32, 16, 1, 1, 1, 8, true, true, 32, 3>("mfma_32x32x16_w1x1_kg8_s3_dl", 1, 0.8125,
+                                                     1082, 1.0, 0.0),
+    entry<32, 32, 16, 1, 1, 1, 8, true, false>("mfma_32x32x16_w1x1_kg8_dl", 1, 0.8125, 1082, 1.0),
+    entry<32, 64, 32, 1, 2, 1, 4, true, true>("mfma_32x64x32_w1x2_kg4_dl", 1, 0.935, 549, 1.0,
+                                              0.0),
 };
 constexpr int kNumVariants = int(sizeof(kVariants) / sizeof(kVariants[0]));
 

@@ -326,7 +326,7 @@ def test_variant_info():
         # three LDS stages only in the template kernel with direct loads, named _s3
         assert info["lds_stages"] == (3 if "_s3_" in name else 2)
         if info["lds_stages"] == 3:
-            assert info["kernel"] == "mfma" and info["direct_loads"] and not info["planned"]
+            assert info["kernel"] == "mfma" and info["direct_loads"]
     with pytest.raises(g.SgemmError):
         g.sgemm_f32_variant_info(len(names))
     buf = ctypes.create_string_buffer(8)
@@ -360,7 +360,7 @@ WORKLOAD_PLANS = {
     "c3": ("mfma16_64x64x64_w2x2_kg2_dl", 1),
     "c4": ("mfma_256x256x32_w2x2_rp", 0),
     "c5": ("mfma_128x256x32_w2x4_ps", 0),
-    "sk": ("mfma16_48x64x32_w1x2_kg4_dl", 0),
+    "sk": ("mfma_32x32x16_w1x1_kg8_s3_dl", 0),
     "rk": ("mfma16_80x64x32_w1x2_kg2_dl", 0),
 }
 
