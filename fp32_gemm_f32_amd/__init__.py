@@ -18,6 +18,7 @@ Raw layer (same names and arguments as the C ABI; pointers are integers):
     sgemm_f32_lds_transpose(rows, cols, src, ldi, dst, ldo, tile=32, pad=0, stream=0)
     sgemm_f32_variant(variant, M, N, K, A, lda, B, ldb, C, ldc, stream=0)
     sgemm_f32_plan_describe(M, N, K, A, lda, B, ldb, C, ldc, num_cus=0) -> dict
+    sgemm_f32_variant_describe(variant, M, N, K, lda, ldb, ldc, num_cus=0) -> dict
     sgemm_f32_variant_info(variant) -> dict, planned_variants() -> [index],
     streamk_variants() -> [index]
 Tensor layer (torch tensors on the GPU, launched on torch's current stream):
@@ -99,6 +100,8 @@ def _load():
         lib.sgemm_f32_status_string.restype = ctypes.c_char_p
         lib.sgemm_f32_plan_describe.argtypes = gemm + [i, ctypes.c_char_p, i]
         lib.sgemm_f32_plan_describe.restype = i
+        lib.sgemm_f32_variant_describe.argtypes = [i] * 8 + [ctypes.c_char_p, i]
+        lib.sgemm_f32_variant_describe.restype = i
         lib.sgemm_f32_abi_version.argtypes = []
         lib.sgemm_f32_abi_version.restype = i
         _lib = lib
@@ -220,6 +223,19 @@ def sgemm_f32_plan_describe(M, N, K, A=0, lda=None, B=0, ldb=None, C=0, ldc=None
                                          ldc, num_cus, buf, len(buf))
     if rc < 0:
         raise SgemmError(rc, "sgemm_f32_plan_describe")
+    return json.loads(buf.value.decode())
+
+
+def sgemm_f32_variant_describe(variant, M, N, K, lda=None, ldb=None, ldc=None,
+                               num_cus=0) -> dict:
+    lda = K if lda is None else lda
+    ldb = N if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    buf = ctypes.create_string_buffer(1024)
+    rc = _load().sgemm_f32_variant_describe(variant, M, N, K, lda, ldb, ldc, num_cus, buf,
+                                            len(buf))
+    if rc < 0:
+        raise SgemmError(rc, "sgemm_f32_variant_describe")
     return json.loads(buf.value.decode())
 
 

@@ -119,10 +119,13 @@ struct GemmArgs {
     SkGeom sk;
     float *W;
     // Column strip (plain kernels only): when strip_cols > 0, the tiles cover columns
-    // [0, strip_n0), and the workgroups of the last tile column also compute the
-    // strip_cols = N - strip_n0 (at most kStripCols) columns past it, on the vector ALUs.
+    // [0, strip_n0), and the strip_cols = N - strip_n0 (at most kStripCols) columns past
+    // them are computed on the vector ALUs, by the tiles of each row: with strip_rows = r
+    // > 0, tile column t computes rows [t r, (t + 1) r) of its tile row's strip; with 0,
+    // the last tile column computes all of them.
     int strip_n0;
     int strip_cols;
+    int strip_rows;
 };
 
 // Most columns a strip may hold: a one-column remainder of N past the last whole tile column.
@@ -342,9 +345,14 @@ struct MfmaTile {
     static constexpr int A_TILE = BM * BK;       // floats per A stage
     static constexpr int B_TILE = BK * BN;       // floats per B stage
     static constexpr int STAGE = A_TILE + B_TILE;
-    // partial sums of K-groups 1 .. KG-1, handed to group 0 after the last panel; they reuse
-    // the stages' memory
-    static constexpr int RED = (KG - 1) * kGroupThreads * NACC * ACC;
+    // The tile's stores are shared by the K-groups: store unit (r, g, q), the quad q of
+    // accumulator registers (4 rows) of row block r and column group g (CI blocks side by
+    // side), belongs to K-group u KG / UNITS for unit index u = (r CG + g) ACC/4 + q. After
+    // the last panel each group passes its partial sums of the others' units through LDS
+    // (one f32x4 per block and lane, in a slot per writing group and unit), reusing the
+    // stages' memory, and the owner adds them.
+    static constexpr int UNITS = RB * CG * (ACC / 4);
+    static constexpr int RED = KG > 1 ? KG * kGroupThreads * NACC * ACC : 0;
     // Column strip (see the kernel): per stage, 64 floats of the strip's B column (one per
     // value of k of the panel), loaded with the panel; then a reduction area for the lanes'
     // partial sums: one row per K-group and MFMA lane group, STRIP_RS floats apart. The
@@ -352,8 +360,10 @@ struct MfmaTile {
     // which write the same rows' sums into H different rows, hit different banks.
     static constexpr int STRIP_STAGE = 64;
     static constexpr int STRIP_RS = (BM + 63) / 64 * 64 + 64 / MfmaShape<MB>::H;
-    static constexpr int STRIP_FLOATS =
-        NSTG * KG * STRIP_STAGE + KG * MfmaShape<MB>::H * STRIP_RS;
+    static constexpr int STRIP_RED = KG * MfmaShape<MB>::H * STRIP_RS > KG * kGroupThreads
+                                         ? KG * MfmaShape<MB>::H * STRIP_RS
+                                         : KG * kGroupThreads;
+    static constexpr int STRIP_FLOATS = NSTG * KG * STRIP_STAGE + STRIP_RED;
     // NSTG LDS stages per K-group
     static constexpr int STAGES = NSTG * KG * STAGE;
     static constexpr bool STRIP_OK = BM <= kGroupThreads * KG && BK <= 64 && RED <= STAGES &&
@@ -372,9 +382,10 @@ struct MfmaTile {
 
 // KG > 1 splits K inside the workgroup: KG groups of WGM x WGN waves compute the same
 // tile, group g taking K-panels g, g + KG, g + 2 KG, ..., each with its own LDS stages;
-// at the end of a tile groups 1 .. KG-1 pass their sums through LDS to group 0, which adds
-// them in ascending group order (deterministic) and stores C. This puts KG waves on each
-// SIMD for tiles too small to fill the GPU otherwise.
+// at the end of a tile the groups pass their sums through LDS and each adds, in ascending
+// group order (deterministic), and stores its share of the tile's store units
+// (MfmaTile::UNITS). This puts KG waves on each SIMD for tiles too small to fill the GPU
+// otherwise, and spreads the tile's final sums and stores over all of them.
 //
 // DL selects direct global -> LDS loads: each 16-byte buffer load writes its lane's chunk
 // straight into LDS (lane l of a wave at the wave's base + 16 l), so the next panel needs
@@ -668,20 +679,26 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     constexpr int PER_WRITE = (NL + WS - 1) / WS;
     static_assert(LS + WS < STEPS, "loads and LDS writes of a panel need separate steps");
 
-    // ---- column strip: the workgroups of the last tile column also compute the column of C
-    // past it (strip_cols = 1), instead of a column of tiles that would hold one valid
-    // column. The strip's B values of a panel (zeros past the K range) are loaded straight
-    // into LDS with the panel, stage s of group kg at strip_lds + (s KG + kg) STRIP_STAGE,
-    // value k of the panel at + k, by the group's first wave. The MFMA's A operands already
-    // hold, in each lane, four consecutive values of k of each of the lane's rows (k-group
-    // kb: 4 (H kb + hi) .. + 3); a lane multiplies them by the strip's four B values for
-    // those k (one 16-byte LDS read per k-group, the same address for all lanes of a lane
-    // group) into sacc, on the vector ALU between the MFMAs. Waves that differ only in wn
-    // hold the same rows, so only the wn = 0 waves' sums are used; after the last panel the
-    // lane groups and K-groups are added in a fixed order. (Vector work among the MFMAs
-    // costs the matrix pipe time on gfx950: the strip tiles run a few per cent longer than
-    // the others. Spreading the strip's rows over every tile of a row costs every tile
-    // about that much, which is worse once the tiles take more than one round.)
+    // ---- column strip: the tiles also compute the column of C past the last tile column
+    // (strip_cols = 1), instead of a column of tiles that would hold one valid column. The
+    // strip's B values of a panel (zeros past the K range) are loaded straight into LDS
+    // with the panel, stage s of group kg at strip_lds + (s KG + kg) STRIP_STAGE, value k
+    // of the panel at + k, by the group's first wave. Two forms:
+    //  * spread (strip_rows > 0): each tile of a row computes strip_rows of the row's strip
+    //    rows, from the A panel in LDS (below, set_spread_item);
+    //  * last column (strip_rows = 0): the tiles of the last tile column compute all of
+    //    them. The MFMA's A operands already hold, in each lane, four consecutive values of
+    //    k of each of the lane's rows (k-group kb: 4 (H kb + hi) .. + 3); a lane multiplies
+    //    them by the strip's four B values for those k (one 16-byte LDS read per k-group,
+    //    the same address for all lanes of a lane group) into sacc, on the vector ALU
+    //    between the MFMAs. Waves that differ only in wn hold the same rows, so only the
+    //    wn = 0 waves' sums are used; after the last panel the lane groups and K-groups are
+    //    added in a fixed order.
+    // Vector and LDS work among the MFMAs costs the matrix pipe time on gfx950. The spread
+    // form costs each tile two LDS reads and four FMAs per panel and wave, against four
+    // reads and 4 RB FMAs per k-group in the last column, so the plan uses it wherever a
+    // K-group's threads cover a tile's share of the rows and few rounds of tiles make
+    // that cheaper than the last-column form (strip_form_rows).
     constexpr bool CAN_STRIP = !SK && DL && T::STRIP_OK;
     float *const strip_lds = lds_all + T::STAGES;
     float *const strip_red = strip_lds + NSTG * KG * T::STRIP_STAGE;
@@ -719,6 +736,22 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
             asm volatile("" : "+v"(sacc[r]));
         }
     };
+    // Spread strip (strip_rows > 0): every tile of the row computes strip_rows rows of the
+    // strip. Thread tid of a K-group owns chunk tid % CPR (four values of k) of row slot
+    // tid / CPR; per panel it reads that A chunk and the strip's four B values for it from
+    // LDS (two 16-byte reads) and adds their four products (four FMAs), in one step of the
+    // panel. Slots past strip_rows, or rows past the tile, read row 0 and are never stored.
+    int sp_aoff = 0, sp_boff = 0;
+    float sp_acc = 0.0f;
+    f32x4 sp_a, sp_b;
+    auto set_spread_item = [&]() __attribute__((always_inline)) {
+        const int q = tid / CPR, c = tid % CPR;
+        const int row = (ln0 / BN) * p.strip_rows + q;
+        const int lr = q < p.strip_rows && row < BM ? row : 0;
+        sp_aoff = lr * BK + 4 * (c ^ a_swizzle<CPR>(lr));
+        sp_boff = 4 * c;
+        sp_acc = 0.0f;
+    };
 
     // NEXT (next_tag 1 or 2): a next panel follows, whose step 0 this one reads after its
     // barrier; 2 (NextTail): that next panel is its group's last, which may hold the end of
@@ -740,7 +773,10 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
         else asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     };
     auto panel = [&](auto cur_tag, auto next_tag, auto ns_tag, auto strip_tag) __attribute__((always_inline)) {
-        constexpr bool STRIP = decltype(strip_tag)::value;
+        constexpr int SMODE = decltype(strip_tag)::value;
+        constexpr bool STRIP = SMODE != 0;          // the panel loads strip values
+        constexpr bool COLS = SMODE == 1;           // last tile column: the whole strip
+        constexpr bool SPREAD = SMODE == 2;         // a share of the strip's rows
         constexpr bool NEXT = decltype(next_tag)::value != 0;
         constexpr bool TAIL_NEXT = decltype(next_tag)::value == 2;
         constexpr bool LOADS = NSTG == 2 ? NEXT : decltype(next_tag)::value == 1;
@@ -780,12 +816,22 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
             // strip: the next panel's B values with the first loads; k-group kb's B values
             // read at its first step and its products added at its third
             constexpr int n_sload = (STRIP && LOADS && t == 0) ? 1 : 0;
-            constexpr bool s_rd = STRIP && s == 0;
-            constexpr bool s_fma = STRIP && s == 2;
+            constexpr bool s_rd = COLS && s == 0;
+            constexpr bool s_fma = COLS && s == 2;
+            constexpr int n_sprd = SPREAD && t == 0 ? 2 : 0;
             if constexpr (n_sload > 0) strip_load(NSTG == 2 ? cur_stage ^ 1 : load_stage);
             if constexpr (s_fma) strip_fma(a[kb & 1]);
             if constexpr (s_rd)
                 sbv = *reinterpret_cast<const f32x4 *>(Ss + 4 * (S::H * kb + hi));
+            if constexpr (SPREAD && t == 3) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sp_acc += sp_a[e] * sp_b[e];
+                asm volatile("" : "+v"(sp_acc));
+            }
+            if constexpr (n_sprd > 0) {
+                sp_a = *reinterpret_cast<const f32x4 *>(As + sp_aoff);
+                sp_b = *reinterpret_cast<const f32x4 *>(Ss + sp_boff);
+            }
             if constexpr (n_write > 0) {
 #pragma unroll
                 for (int l = w_first; l < w_first + n_write; ++l) write_slot(Aload, l);
@@ -814,9 +860,9 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
 
             if constexpr (n_write > 0)
                 __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, n_write, 0);
-            if constexpr (next_b || next_a)
+            if constexpr (next_b || next_a || n_sprd > 0)
                 __builtin_amdgcn_sched_group_barrier(
-                    kSchedDsRead, (next_b ? CG : 0) + (next_a ? RB : 0), 0);
+                    kSchedDsRead, (next_b ? CG : 0) + (next_a ? RB : 0) + n_sprd, 0);
             if constexpr (t == STEPS - 1 && NEXT)
                 __builtin_amdgcn_sched_group_barrier(kSchedDsRead, RB + CG, 0);
             __builtin_amdgcn_sched_group_barrier(kSchedMfma, RB * CG * CI, 0);
@@ -866,7 +912,17 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
 
     // ---- epilogue of one tile: accumulators to C through a buffer resource ----
     const int ldc = p.ldc;
-    // Sum the accumulator sets, then (KG > 1) the K-groups, into group 0's acc[0].
+    // K-group owning store unit (r, g, q) (MfmaTile::UNITS), and the LDS slot (one f32x4 per
+    // lane) of writing group w's partial sums of block (r, g CI + c), quad q
+    auto unit_owner = [](int r, int g, int q) constexpr {
+        return ((r * CG + g) * (T::ACC / 4) + q) * KG / T::UNITS;
+    };
+    auto red_slot = [&](int w, int r, int j, int q) __attribute__((always_inline)) {
+        return reinterpret_cast<f32x4 *>(
+            red + (((w * T::NACC + r * CI * CG + j) * (T::ACC / 4) + q) * NT + tid) * 4);
+    };
+    // Sum the accumulator sets into acc[0]; then (KG > 1) each group adds the other groups'
+    // sums of its own store units, in ascending group order, into its acc[0].
     auto finish = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int h = 1; h < KACC; ++h)
@@ -876,40 +932,50 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
                 for (int j = 0; j < CI * CG; ++j) acc[0][i][j] += acc[h][i][j];
         if constexpr (KG > 1) {
             // every group has read its stages for the last time before red overwrites them;
-            // then group g > 0 writes quad q of its sums at
-            // red[((g-1) * NACC * ACC / 4 + q) * NT + tid]
+            // then each writes its sums of the units other groups own
             __syncthreads();
-            if (kg > 0) {
+            static_for<0, RB>([&](auto ic) {
+                constexpr int i = decltype(ic)::value;
+                static_for<0, CG>([&](auto gc) {
+                    constexpr int g = decltype(gc)::value;
+                    static_for<0, T::ACC / 4>([&](auto qc) {
+                        constexpr int q = decltype(qc)::value;
+                        if (unit_owner(i, g, q) != kg) {
 #pragma unroll
-                for (int i = 0; i < RB; ++i)
-#pragma unroll
-                    for (int j = 0; j < CI * CG; ++j)
-#pragma unroll
-                        for (int q = 0; q < T::ACC / 4; ++q) {
-                            const acc_t &x = acc[0][i][j];
-                            const f32x4 v = {x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
-                            const int quad =
-                                ((kg - 1) * T::NACC + i * CI * CG + j) * (T::ACC / 4) + q;
-                            *reinterpret_cast<f32x4 *>(red + (quad * NT + tid) * 4) = v;
-                        }
-            }
-            __syncthreads();
-            if (kg == 0) {
-                for (int g = 1; g < KG; ++g)
-#pragma unroll
-                    for (int i = 0; i < RB; ++i)
-#pragma unroll
-                        for (int j = 0; j < CI * CG; ++j)
-#pragma unroll
-                            for (int q = 0; q < T::ACC / 4; ++q) {
-                                const int quad =
-                                    ((g - 1) * T::NACC + i * CI * CG + j) * (T::ACC / 4) + q;
-                                const f32x4 v =
-                                    *reinterpret_cast<const f32x4 *>(red + (quad * NT + tid) * 4);
-#pragma unroll
-                                for (int e = 0; e < 4; ++e) acc[0][i][j][4 * q + e] += v[e];
+                            for (int c = 0; c < CI; ++c) {
+                                const acc_t &x = acc[0][i][g * CI + c];
+                                *red_slot(kg, i, g * CI + c, q) =
+                                    f32x4{x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
                             }
-            }
+                        }
+                    });
+                });
+            });
+            __syncthreads();
+            static_for<0, RB>([&](auto ic) {
+                constexpr int i = decltype(ic)::value;
+                static_for<0, CG>([&](auto gc) {
+                    constexpr int g = decltype(gc)::value;
+                    static_for<0, T::ACC / 4>([&](auto qc) {
+                        constexpr int q = decltype(qc)::value;
+                        if (unit_owner(i, g, q) == kg) {
+#pragma unroll
+                            for (int c = 0; c < CI; ++c) {
+                                acc_t &x = acc[0][i][g * CI + c];
+                                const f32x4 own = {x[4 * q], x[4 * q + 1], x[4 * q + 2],
+                                                   x[4 * q + 3]};
+                                // the slot of the owner itself holds nothing; its sums come
+                                // from registers
+                                f32x4 sum = kg == 0 ? own : *red_slot(0, i, g * CI + c, q);
+                                for (int w = 1; w < KG; ++w)
+                                    sum += w == kg ? own : *red_slot(w, i, g * CI + c, q);
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) x[4 * q + e] = sum[e];
+                            }
+                        }
+                    });
+                });
+            });
         }
     };
 
@@ -933,6 +999,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
                 const bool col_full = col + CI <= cols_left;
 #pragma unroll
                 for (int v = 0; v < T::ACC; ++v) {
+                    if (unit_owner(r, g, v / 4) != kg) continue;
                     const int dr = S::row(v);
                     bvec out;
 #pragma unroll
@@ -957,6 +1024,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
                     const bool partial = col < cols_left && col + CI > cols_left;
 #pragma unroll
                     for (int v = 0; v < T::ACC; ++v) {
+                        if (unit_owner(r, g, v / 4) != kg) continue;
                         const int dr = S::row(v);
                         const bool ok = partial && lrow + dr < rows_left;
 #pragma unroll
@@ -1006,13 +1074,15 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
         // and the epilogue, into C or (a partial stream-K tile) into workspace slot `slot`;
         // with STRIP also the column strip's rows of this tile
         auto run_item = [&](auto strip_tag) __attribute__((always_inline)) {
-            constexpr bool STRIP = decltype(strip_tag)::value;
+            constexpr int SMODE = decltype(strip_tag)::value;
+            constexpr bool STRIP = SMODE != 0;
             auto setp = [&](int k0) __attribute__((always_inline)) {
                 set_panel(k0);
                 if constexpr (STRIP) set_strip_panel(k0);
             };
             set_item();
             if constexpr (STRIP) set_strip_item();
+            if constexpr (SMODE == 2) set_spread_item();
             // rounds of panels of this group; a group whose last panel lies past the K range
             // loads only zeros for it
             auto group_rounds = [&]() { return ((lK + BK - 1) / BK + KG - 1) / KG; };
@@ -1126,8 +1196,23 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
             }
             panel_parity = rounds - 1;
             last_panel(SR{}, rounds, strip_tag);
+            // the spread strip's partial sums go to LDS before the K-group sums, whose
+            // barriers (KG > 1) then order them before the reads below
+            if constexpr (SMODE == 2) strip_red[kg * NT + tid] = sp_acc;
             finish();
-            if constexpr (STRIP) {
+            if constexpr (SMODE == 2) {
+                // each row's chunk sums, K-group by K-group, in ascending order of both
+                if constexpr (KG == 1) __syncthreads();
+                const int q = threadIdx.x;
+                const int row = (ln0 / BN) * p.strip_rows + q;
+                if (q < p.strip_rows && row < BM && lm0 + row < M) {
+                    float v = 0.0f;
+                    for (int g = 0; g < KG; ++g)
+                        for (int c = 0; c < CPR; ++c) v += strip_red[g * NT + q * CPR + c];
+                    p.C[int64_t(lm0 + row) * ldc + p.strip_n0] = v;
+                }
+            }
+            if constexpr (SMODE == 1) {
                 // the wn = 0 waves' partial sums of each (K-group, lane group) for each row,
                 // then their sum in ascending order of both, stored to C (rows past M are not)
                 if (wn == 0) {
@@ -1145,16 +1230,18 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
                 }
             }
         };
-        bool strip_here = false;
-        if constexpr (CAN_STRIP)
-            strip_here = p.strip_cols > 0 && ln0 + BN == p.strip_n0;
+        using NoStrip = std::integral_constant<int, 0>;
         if constexpr (CAN_STRIP) {
-            if (strip_here) run_item(std::true_type{});
-            else run_item(std::false_type{});
+            if (p.strip_cols > 0 && p.strip_rows > 0)
+                run_item(std::integral_constant<int, 2>{});
+            else if (p.strip_cols > 0 && ln0 + BN == p.strip_n0)
+                run_item(std::integral_constant<int, 1>{});
+            else
+                run_item(NoStrip{});
         } else {
-            run_item(std::false_type{});
+            run_item(NoStrip{});
         }
-        if (kg == 0) {
+        {   // every K-group stores its own units of the tile
             if (!to_workspace) {
                 const int64_t ec = ls * p.c_split_stride + int64_t(lm0) * ldc + ln0;
                 epilogue(make_rsrc(p.C + ec, p.c_bytes - ec * 4), uint32_t(ldc) * 4u, M - lm0,

@@ -77,6 +77,18 @@ inline int strip_eligible(const Variant &v, const Operands &o)
     return r >= 1 && r <= kStripColsMax ? r : 0;
 }
 
+// Rows of the strip each tile computes when the strip's rows are spread over the tiles of
+// a row: ceil(BM / whole tile columns), if one K-group's threads hold a (row, 16-byte
+// chunk of a panel row) pair each (64 wgm wgn threads, BK / 4 chunks per row); else 0,
+// and the tiles of the last tile column compute the whole strip.
+inline int strip_spread_rows(const Variant &v, const Operands &o)
+{
+    const int tn = o.N / v.BN;
+    if (tn <= 0) return 0;
+    const int rows = (v.BM + tn - 1) / tn;
+    return rows * (v.BK / 4) <= 64 * v.wgm * v.wgn ? rows : 0;
+}
+
 inline bool variant_allowed(const Variant &v, const Operands &o)
 {
     if (v.whole_tiles &&
@@ -87,10 +99,16 @@ inline bool variant_allowed(const Variant &v, const Operands &o)
 
 // Cost units: one multiply-add on one CU at rate 1 (140 TFLOP/s over 256 CUs).
 constexpr double kUnitsPerUs = 140e12 / 2 / 256 * 1e-6;
-// The tiles of the last tile column also compute the strip, on the vector ALUs between
-// their MFMAs; they run a few per cent longer than the others (measured: 7 % at
-// 1023 x 1025 x 1027 with 64 x 64 tiles).
-constexpr double kStripShare = 0.03;
+// The strip's products run on the vector ALUs between the MFMAs of the tiles that compute
+// it. Spread over the tiles of each row, every tile runs about 1-5 % longer; in the last
+// tile column alone, those tiles run 7-11 % longer and the others not at all (measured at
+// steady state against the same shapes without the column: 1023 x 1025 x 1027 and
+// 1024 x 1025 x 1024 with 64 x 64 tiles, 2048 x 2049 x 2048, 4096 x 4097 x 4096 and
+// 8192 x 8193 x 1024 with 128 x 128 tiles). So the spread form wins while each CU runs
+// few tiles, the last-column form once the strip tiles are a small share of many rounds
+// (8192 x 8193 x 1024: 64 strip tiles among 4096).
+constexpr double kStripSpreadShare = 0.02;
+constexpr double kStripColumnShare = 0.10;
 
 // Busiest-CU estimate for variant v with tn tile columns, in multiply-adds at rate 1.
 inline double tiles_cost(const Variant &v, const Operands &o, int cus, int64_t tn)
@@ -106,10 +124,30 @@ inline double tiles_cost(const Variant &v, const Operands &o, int cus, int64_t t
     return double(per_cu) * double(v.BM) * v.BN * (k / rate + v.overhead);
 }
 
-// The same with a column strip of the last N mod BN columns (strip_eligible).
+// The busiest CU's share of the strip when the last tile column computes it: one heavier
+// tile per round of strip tiles, over its per_cu tiles.
+inline double strip_column_share(const Variant &v, const Operands &o, int cus)
+{
+    const int64_t tm = (int64_t(o.M) + v.BM - 1) / v.BM;
+    const int64_t per_cu = (tm * (o.N / v.BN) + cus - 1) / cus;
+    return kStripColumnShare * double((tm + cus - 1) / cus) / double(per_cu > 0 ? per_cu : 1);
+}
+
+// Rows per tile of the strip's form for o: strip_spread_rows where spreading the rows is
+// priced below the last-column form, else 0 (the last tile column computes them).
+inline int strip_form_rows(const Variant &v, const Operands &o, int cus)
+{
+    const int rows = strip_spread_rows(v, o);
+    return rows > 0 && kStripSpreadShare < strip_column_share(v, o, cus) ? rows : 0;
+}
+
+// The same with a column strip of the last N mod BN columns (strip_eligible), in the form
+// strip_form_rows picks.
 inline double strip_cost(const Variant &v, const Operands &o, int cus)
 {
-    return tiles_cost(v, o, cus, o.N / v.BN) * (1.0 + kStripShare);
+    const double share = strip_form_rows(v, o, cus) > 0 ? kStripSpreadShare
+                                                        : strip_column_share(v, o, cus);
+    return tiles_cost(v, o, cus, o.N / v.BN) * (1.0 + share);
 }
 
 // Columns variant v leaves to the strip for o: those of strip_eligible when the strip is

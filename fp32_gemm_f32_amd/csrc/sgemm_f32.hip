@@ -242,6 +242,7 @@ GemmArgs plain_args(const VariantEntry &e, const Operands &o, const float *A, co
     p.c_split_stride = 0;
     p.strip_n0 = o.N - r;
     p.strip_cols = r;
+    p.strip_rows = r > 0 ? strip_form_rows(e.v, o, cus) : 0;
     return p;
 }
 
@@ -881,28 +882,23 @@ extern "C" const char *sgemm_f32_status_string(int status)
     }
 }
 
-extern "C" int sgemm_f32_plan_describe(int M, int N, int K, const float *A, int lda,
-                                       const float *B, int ldb, const float *C, int ldc,
-                                       int num_cus, char *buf, int buflen)
+namespace {
+// The JSON plan description of variant vi run plainly on o with `cus` compute units (the
+// variant's tiles, grid and column strip), for sgemm_f32_plan_describe and
+// sgemm_f32_variant_describe. Returns vi, or SGEMM_EINVAL_ARG if buf is too small.
+int describe_plan(int vi, const Operands &o, int cus, char *buf, int buflen)
 {
-    if (!buf || buflen <= 0) return SGEMM_EINVAL_ARG;
-    (void)A; (void)B; (void)C;
-    const int vs = validate_shape(M, N, K, lda, ldb, ldc);
-    if (vs != SGEMM_OK) return vs;
-    const Operands o = make_operands(M, N, K, lda, ldb, ldc);
-    int cus = num_cus;
-    if (cus <= 0) {
-        const int qs = device_cus(&cus);
-        if (qs != SGEMM_OK) return qs;
-    }
-    const int vi = choose_variant(g_table, o, cus);
-    if (vi < 0) return SGEMM_ETOO_LARGE;
+    const int M = o.M, N = o.N, K = o.K;
     const Variant &v = kVariants[vi].v;
     const int strip = kVariants[vi].persistent ? 0 : strip_cols(v, o, cus);
     const int64_t tm = (int64_t(M) + v.BM - 1) / v.BM,
                   tn = (int64_t(N) - strip + v.BN - 1) / v.BN;
-    // one workgroup per tile (and per strip row block), or for the persistent variant one
-    // per CU over its tiles
+    // workgroups computing rows of the strip: every tile column holding some of its rows
+    // (spread), or the last tile column
+    const int srows = strip ? strip_form_rows(v, o, cus) : 0;
+    const int64_t strip_tiles =
+        !strip ? 0 : srows ? tm * std::min<int64_t>(tn, (v.BM + srows - 1) / srows) : tm;
+    // one workgroup per tile, or for the persistent variant one per CU over its tiles
     const int64_t grid = kVariants[vi].persistent ? std::min<int64_t>(tm * tn, cus)
                                                   : tm * tn;
     // operand bytes the tiles request: every A row panel once per tile column and every
@@ -913,13 +909,55 @@ extern "C" int sgemm_f32_plan_describe(int M, int N, int K, const float *A, int 
                            "\"BK\": %d, \"waves\": [%d, %d], \"threads\": %d, \"grid\": %lld, "
                            "\"tiles\": [%lld, %lld], \"cus\": %d, \"wg_per_cu\": %d, "
                            "\"direct_loads\": %s, \"tile_request_bytes\": %lld, "
-                           "\"strip_cols\": %d, \"strip_tiles\": %lld}",
+                           "\"strip_cols\": %d, \"strip_rows\": %d, \"strip_tiles\": %lld}",
                            vi, v.name, v.BM, v.BN, v.BK, v.wgm, v.wgn, kVariants[vi].threads,
                            (long long)grid, (long long)tm, (long long)tn, cus, v.wg_per_cu,
                            v.direct ? "true" : "false", (long long)tile_bytes, strip,
-                           (long long)(strip ? tm : 0));
+                           srows, (long long)strip_tiles);
     if (n < 0 || n >= buflen) return SGEMM_EINVAL_ARG;
     return vi;
+}
+}  // namespace
+
+// The shape checks and CU count both describe entry points share.
+static int describe_args(int M, int N, int K, int lda, int ldb, int ldc, int num_cus,
+                         char *buf, int buflen, Operands *o, int *cus)
+{
+    if (!buf || buflen <= 0) return SGEMM_EINVAL_ARG;
+    const int vs = validate_shape(M, N, K, lda, ldb, ldc);
+    if (vs != SGEMM_OK) return vs;
+    *o = make_operands(M, N, K, lda, ldb, ldc);
+    *cus = num_cus;
+    if (*cus <= 0) return device_cus(cus);
+    return SGEMM_OK;
+}
+
+extern "C" int sgemm_f32_plan_describe(int M, int N, int K, const float *A, int lda,
+                                       const float *B, int ldb, const float *C, int ldc,
+                                       int num_cus, char *buf, int buflen)
+{
+    (void)A; (void)B; (void)C;
+    Operands o{};
+    int cus = 0;
+    const int st = describe_args(M, N, K, lda, ldb, ldc, num_cus, buf, buflen, &o, &cus);
+    if (st != SGEMM_OK) return st;
+    const int vi = choose_variant(g_table, o, cus);
+    if (vi < 0) return SGEMM_ETOO_LARGE;
+    return describe_plan(vi, o, cus, buf, buflen);
+}
+
+extern "C" int sgemm_f32_variant_describe(int variant, int M, int N, int K, int lda, int ldb,
+                                          int ldc, int num_cus, char *buf, int buflen)
+{
+    if (variant >= kNumVariants) return SGEMM_EINVAL_ARG;
+    Operands o{};
+    int cus = 0;
+    const int st = describe_args(M, N, K, lda, ldb, ldc, num_cus, buf, buflen, &o, &cus);
+    if (st != SGEMM_OK) return st;
+    const int vi = variant >= 0 ? variant : choose_variant(g_table, o, cus);
+    if (vi < 0) return SGEMM_ETOO_LARGE;
+    if (!offsets_fit(kVariants[vi].v, o)) return SGEMM_ETOO_LARGE;
+    return describe_plan(vi, o, cus, buf, buflen);
 }
 
 extern "C" int sgemm_f32_abi_version(void) { return kAbiVersion; }

@@ -289,8 +289,10 @@ const char *sgemm_f32_status_string(int status);
  * arguments into buf (at most buflen bytes including the NUL): variant, tile shape,
  * waves, grid, workgroups resident per CU, whether panels load straight into LDS, the
  * operand bytes the tiles request, and the column strip: "strip_cols" (the column past
- * the last whole tile column that the tiles of that column also compute, 0 or 1) and
- * "strip_tiles" (how many tiles do). The plan is the pages' tile-size trade-off: reuse
+ * the last whole tile column that the tiles also compute, 0 or 1), "strip_rows" (the
+ * strip rows each tile of a row computes when they are spread over the row's tiles; 0
+ * when the last tile column computes them all) and "strip_tiles" (how many tiles compute
+ * some). The plan is the pages' tile-size trade-off: reuse
  * per staged element against the parallelism left ("Shared Memory Tiling", "Choosing a
  * tile size"). Dimensions and leading dimensions are validated as in sgemm_f32
  * (SGEMM_EINVAL_DIM, SGEMM_EINVAL_LD); pointers are used for their alignment only and
@@ -303,6 +305,19 @@ int sgemm_f32_plan_describe(int M, int N, int K,
                             const float *B, int ldb,
                             const float *C, int ldc,
                             int num_cus, char *buf, int buflen);
+
+/*
+ * The same description for a tile variant forced as sgemm_f32_variant runs it (variant
+ * < 0: the plan's choice, as sgemm_f32_plan_describe), with the leading dimensions given:
+ * which variant, its grid and whether its tiles compute a column strip and how. Host-only,
+ * no pointers. Returns the variant index, SGEMM_EINVAL_ARG for an unknown variant or a
+ * buffer too small, SGEMM_EINVAL_DIM / SGEMM_EINVAL_LD as sgemm_f32, SGEMM_ETOO_LARGE if
+ * the variant's buffer offsets cannot reach the operands, SGEMM_ELAUNCH if num_cus <= 0
+ * and no device answers. The tile-size trade-off it reports is that of "Shared Memory
+ * Tiling", "Choosing a tile size".
+ */
+int sgemm_f32_variant_describe(int variant, int M, int N, int K, int lda, int ldb, int ldc,
+                               int num_cus, char *buf, int buflen);
 
 /* Version of this ABI (incremented on any incompatible change). */
 int sgemm_f32_abi_version(void);

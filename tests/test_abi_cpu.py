@@ -112,11 +112,21 @@ def test_plan(shape, expect_tile):
         plan["strip_cols"] == 0 and plan["tiles"][1] * plan["BN"] >= N)
     if plan["strip_cols"]:
         assert info["strip"] and 1 <= plan["strip_cols"] <= 4
-        assert plan["strip_tiles"] == plan["tiles"][0]
+        rows = plan["strip_rows"]
+        if rows:
+            # spread: every tile column holding some of the strip's rows computes them,
+            # each tile a share that one K-group's threads cover
+            assert rows * plan["tiles"][1] >= plan["BM"] > (rows - 1) * plan["tiles"][1]
+            assert rows * plan["BK"] // 4 <= 64 * plan["waves"][0] * plan["waves"][1]
+            assert plan["strip_tiles"] == plan["tiles"][0] * min(
+                plan["tiles"][1], -(-plan["BM"] // rows))
+        else:
+            assert plan["strip_tiles"] == plan["tiles"][0]
     if shape == (1023, 1025, 1027):
         # the ragged workload: 256 whole 64 x 64 tiles and a one-column strip, instead of
-        # a 17th column of nearly empty tiles
+        # a 17th column of nearly empty tiles; its rows spread four to a tile
         assert plan["strip_cols"] == 1 and tiles == 256
+        assert plan["strip_rows"] == 4 and plan["strip_tiles"] == 256
     if expect_tile:
         assert plan["BM"] == plan["BN"] == expect_tile
     elif M * N >= 1 << 20:
@@ -383,3 +393,37 @@ def test_workload_streamk_plans():
         w = wl.WORKLOADS[name]
         d = g.sgemm_f32_streamk_describe(w.M, w.N, w.K, num_cus=256)
         assert not d["streamk"], d
+
+
+def test_variant_describe_strip_forms():
+    """A forced variant's plan, as sgemm_f32_variant runs it: the column strip spread over
+    the tiles of each row where one K-group's threads cover a tile's share of the rows,
+    else computed by the last tile column; no strip where the masked tile column costs no
+    extra round. variant -1 describes the plan's own choice."""
+    cus = 256
+    for v in range(len(g.variant_names())):
+        info = g.sgemm_f32_variant_info(v)
+        if not info["strip"]:
+            continue
+        bm, bn, bk = info["BM"], info["BN"], info["BK"]
+        nt = 64 * info["waves"][0] * info["waves"][1]
+        for (M, N, K, tn) in [(16 * bm - 3, 16 * bn + 1, 33, 16), (15 * bm, 17 * bn + 1, 72, 17),
+                              (cus * bm - 5, bn + 1, 40, 1)]:
+            d = g.sgemm_f32_variant_describe(v, M, N, K, K + 1, N + 3, N + 2, num_cus=cus)
+            assert d["variant"] == v and d["strip_cols"] == 1, (info["name"], d)
+            rows = -(-bm // tn)
+            if rows * bk // 4 <= nt:
+                assert d["strip_rows"] == rows, (info["name"], d)
+                assert d["strip_tiles"] == d["tiles"][0] * min(tn, -(-bm // rows))
+            else:
+                assert d["strip_rows"] == 0 and d["strip_tiles"] == d["tiles"][0], d
+        # a handful of tiles: the masked column costs no extra round, so no strip
+        d = g.sgemm_f32_variant_describe(v, 63, 5 * bn + 1, 33, num_cus=cus)
+        assert d["strip_cols"] == 0 and d["tiles"][1] == 6, d
+    for (M, N, K) in [(1023, 1025, 1027), (8192, 8192, 8192), (6, 6, 9)]:
+        assert (g.sgemm_f32_variant_describe(-1, M, N, K, num_cus=cus) ==
+                g.sgemm_f32_plan_describe(M, N, K, num_cus=cus))
+    with pytest.raises(g.SgemmError):
+        g.sgemm_f32_variant_describe(len(g.variant_names()), 64, 64, 64, num_cus=cus)
+    with pytest.raises(g.SgemmError):
+        g.sgemm_f32_variant_describe(0, 64, 64, 64, 63, 64, 64, num_cus=cus)

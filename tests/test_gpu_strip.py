@@ -1,9 +1,11 @@
 """The column strip through the C ABI: when N leaves one column past the last whole tile
-column, the workgroups of the last tile column also compute that column, on the vector
-ALUs between their MFMAs, from the A operands they read for the MFMAs. Checked
-against the oracle (exact on small integers, within the normalised tolerance on floats)
-with NaN-poisoned row padding and guard bands around C, for every strip-capable variant
-forced, for the automatic plan, and for run-to-run determinism."""
+column, the tiles also compute that column, on the vector ALUs between their MFMAs: spread
+over the tiles of each row (each tile a few of the row's strip rows, from its A panels in
+LDS), or, when the tile columns are too few for that, by the last tile column from the A
+operands it reads for the MFMAs. Checked against the oracle (exact on small integers,
+within the normalised tolerance on floats) with NaN-poisoned row padding and guard bands
+around C, for every strip-capable variant forced (both forms), for the automatic plan, and
+for run-to-run determinism."""
 import numpy as np
 import pytest
 
@@ -29,17 +31,30 @@ def strip_variants():
 
 
 def shapes_for(v):
-    """(M, N, K) with N = (whole tile columns) + 1: enough tile columns that every tile takes
-    a share of the strip's rows (five or more; 17 gives shares that end inside the tiles),
-    K on both sides of the panel depth and of K-group rounds (with partial last panels),
-    M ragged; and two products without a strip (a wider remainder, too few tile columns)."""
+    """(M, N, K) with N = (whole tile columns) + 1 (or + 2), K on both sides of the panel
+    depth and of K-group rounds (with partial last panels), M ragged: products of a few
+    tiles, where a strip would save no round of tiles, so the plan masks a last tile
+    column that holds one or two valid columns instead (the strip forms are covered by
+    test_strip_forced_both_forms)."""
     bn = g.sgemm_f32_variant_info(v)["BN"]
     return [(63, 5 * bn + 1, 33), (130, 8 * bn + 1, 256), (200, 5 * bn + 1, 257),
             (65, 17 * bn + 1, 300), (257, 5 * bn + 1, 5), (129, 6 * bn + 1, 1),
             (70, 5 * bn + 1, 2050), (17, 9 * bn + 1, 4353), (100, 5 * bn + 1, 37),
-            (33, 7 * bn + 1, 64),
-            # no strip: a remainder wider than it, or too few tile columns to share its rows
-            (130, 5 * bn + 2, 256), (65, bn + 1, 300)]
+            (33, 7 * bn + 1, 64), (65, bn + 1, 300), (130, 2 * bn + 1, 129),
+            (130, 5 * bn + 2, 256)]
+
+
+def forced_strip_shapes(v, cus):
+    """Shapes on which variant v, forced, computes a column strip, for a device of `cus`
+    compute units: one tile per CU with a one-column remainder, whose masked 17th (or
+    second) tile column would take a second round. Sixteen tile columns spread the strip's
+    rows four or eight to a tile, seventeen leave the last tile column without rows, and
+    one tile column leaves them all to it (the last-column form)."""
+    info = g.sgemm_f32_variant_info(v)
+    bm, bn = info["BM"], info["BN"]
+    return [((cus // 16) * bm - 3, 16 * bn + 1, 33, "spread"),
+            ((cus // 17) * bm, 17 * bn + 1, 72, "spread"),
+            (cus * bm - 5, bn + 1, 40, "column")]
 
 
 def _check(A, B, C, kind, what):
@@ -59,7 +74,7 @@ def test_strip_variants_exist():
         assert info["direct_loads"] and info["kernel"] == "mfma", info
 
 
-def test_strip_shapes_forced(gpu):
+def test_masked_last_column_forced(gpu):
     for v in strip_variants():
         _strip_shapes(gpu, v)
 
@@ -71,6 +86,8 @@ def _strip_shapes(gpu, v):
         A = wl.draw(rng, (M, K), "int")
         B = wl.draw(rng, (K, N), "int")
         for lda, ldb, ldc in [(K + 3, N + 5, N + 2), (K, N, N)]:
+            d = g.sgemm_f32_variant_describe(v, M, N, K, lda, ldb, ldc)
+            assert d["strip_cols"] == 0 and d["tiles"][1] * d["BN"] >= N, (name, d)
             _, dA, _ = device_matrix(A, lda)
             _, dB, _ = device_matrix(B, ldb)
             c = GuardedC(M, N, ldc)
@@ -80,6 +97,30 @@ def _strip_shapes(gpu, v):
             _check(A, B, c.result(), "int", (name, M, N, K, lda, ldb, ldc))
 
 
+def test_strip_forced_both_forms(gpu):
+    """Every strip-capable variant forced where its plan computes the strip: spread over
+    the tile rows and in the last tile column, as variant_describe reports; exact on
+    integers with padded leading dimensions and guard bands."""
+    cus = gpu.cuda.get_device_properties(0).multi_processor_count
+    for v in strip_variants():
+        name = g.variant_names()[v]
+        for (M, N, K, form) in forced_strip_shapes(v, cus):
+            lda, ldb, ldc = K + 1, N + 3, N + 2
+            d = g.sgemm_f32_variant_describe(v, M, N, K, lda, ldb, ldc)
+            assert d["variant"] == v and d["strip_cols"] == 1, (name, M, N, K, d)
+            assert (d["strip_rows"] > 0) == (form == "spread"), (name, M, N, K, d)
+            rng = np.random.default_rng(M + 3 * N + 7 * K)
+            A = wl.draw(rng, (M, K), "int")
+            B = wl.draw(rng, (K, N), "int")
+            _, dA, _ = device_matrix(A, lda)
+            _, dB, _ = device_matrix(B, ldb)
+            c = GuardedC(M, N, ldc)
+            print(f"[strip] {name} {M}x{N}x{K} {form} rows={d['strip_rows']}", flush=True)
+            run_kernel(f"v{v}", M, N, K, dA, lda, dB, ldb, c)
+            gpu.cuda.synchronize()
+            _check(A, B, c.result(), "int", (name, M, N, K, form))
+
+
 @pytest.mark.parametrize("kind", ["int", "float"])
 def test_ragged_workload_plan_uses_strip(gpu, kind):
     """The ragged 1023 x 1025 x 1027 workload: the plan puts its last column in a strip, and
@@ -87,8 +128,9 @@ def test_ragged_workload_plan_uses_strip(gpu, kind):
     M, N, K = 1023, 1025, 1027
     plan = g.sgemm_f32_plan_describe(M, N, K)
     print(f"[strip] plan {plan}", flush=True)
-    # the tiles of the last tile column (one per tile row) compute the strip
-    assert plan["strip_cols"] == 1 and plan["strip_tiles"] == plan["tiles"][0]
+    # every tile computes four of its row's 64 strip rows
+    assert plan["strip_cols"] == 1 and plan["strip_rows"] == 4
+    assert plan["strip_tiles"] == plan["tiles"][0] * plan["tiles"][1]
     A, B = wl.operands("c3", kind)
     _, dA, lda = device_matrix(A, K + 1)
     _, dB, ldb = device_matrix(B)
