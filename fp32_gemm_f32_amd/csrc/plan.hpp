@@ -36,9 +36,9 @@ struct Variant {
     bool direct;            // direct global -> LDS loads
     bool planned;           // candidate for the automatic choice (else forced use only)
     bool splitk = true;     // candidate for split-K items too
-    // planned only for products of whole BM x BN tiles and more than one K-panel (the
-    // persistent kernel; forced on other shapes it computes their whole-tile part and
-    // leaves the rest to the plan)
+    // computes whole BM x BN tiles only, with more than one K-panel (the persistent
+    // kernel): on other shapes it runs on their whole-tile part and the right and bottom
+    // edges go to the plan, as launches of their own
     bool whole_tiles = false;
     // a one-column remainder of N past the last whole tile column may be computed by the
     // tiles of the last tile column, on the vector ALUs (the kernel's column strip)
@@ -89,12 +89,27 @@ inline int strip_spread_rows(const Variant &v, const Operands &o)
     return rows * (v.BK / 4) <= 64 * v.wgm * v.wgn ? rows : 0;
 }
 
+// A whole-tile variant (the persistent kernel) also needs rows of C that start on 32-byte
+// boundaries (ldc a multiple of 8): it stores C as 4-byte lane stores from the
+// accumulators, 128 bytes of a row per 32 lanes, and on rows off those boundaries they cost
+// it far more than the other tiles' 16-byte stores. Measured at 16384^2 x 64 against the
+// 128 x 256 x 16 tile (steady state): ldc = 16384 0.92x its time, 16392 0.97x, 16388 1.18x,
+// 16385 1.48x; rows of A or B off 16-byte boundaries cost neither kernel (0.92-0.93x).
 inline bool variant_allowed(const Variant &v, const Operands &o)
 {
     if (v.whole_tiles &&
-        (o.M % v.BM != 0 || o.N % v.BN != 0 || o.K <= v.BK || o.splits != 1))
+        (o.M < v.BM || o.N < v.BN || o.K <= v.BK || o.splits != 1 || o.ldc % 8 != 0))
         return false;
     return offsets_fit(v, o);
+}
+
+// The whole-tile part of o for a whole-tile variant: M and N rounded down to its tiles.
+inline Operands whole_part(const Variant &v, const Operands &o)
+{
+    Operands w = o;
+    w.M = o.M / v.BM * v.BM;
+    w.N = o.N / v.BN * v.BN;
+    return w;
 }
 
 // Cost units: one multiply-add on one CU at rate 1 (140 TFLOP/s over 256 CUs).
@@ -194,6 +209,54 @@ inline double streamk_cost(const Variant &v, const Operands &o, int cus, const S
            (v.sk_price > 0.0 ? v.sk_price : 1.0);
 }
 
+// The launch and latency of one more kernel on the stream, in microseconds: a whole-tile
+// variant runs a ragged product's right and bottom edges as kernels of their own after its
+// own, in stream order.
+constexpr double kEdgeLaunchUs = 4.0;
+
+// Busiest-CU estimate of the cheapest plan for o among the planned variants that take any
+// shape (the edges of a whole-tile variant's product), plus one launch.
+template <int NV>
+inline double edge_cost(const Variant (&table)[NV], const Operands &o, int cus)
+{
+    double best = -1.0;
+    for (int i = 0; i < NV; ++i) {
+        const Variant &v = table[i];
+        if (!v.planned || v.whole_tiles || !variant_allowed(v, o)) continue;
+        const double c = variant_cost(v, o, cus);
+        if (best < 0.0 || c < best) best = c;
+    }
+    return (best < 0.0 ? 0.0 : best) + kEdgeLaunchUs * kUnitsPerUs;
+}
+
+// Price of running variant i of the table on o as the plain entry does: variant_cost, or for
+// a whole-tile variant its whole-tile part plus the right edge (all rows, the columns past
+// the last whole tile column) and the bottom edge (the rows past the last whole tile row,
+// the whole tile columns), each priced as the plan would run it.
+template <int NV>
+inline double plan_cost(const Variant (&table)[NV], int i, const Operands &o, int cus)
+{
+    const Variant &v = table[i];
+    if (!v.whole_tiles) return variant_cost(v, o, cus);
+    // its panels run whole: a K that is not a multiple of BK costs the last one in full
+    // (16384^2 x 65: 1.05x the 128 x 256 x 16 tile's time, against 0.92x at K = 64)
+    Operands w = whole_part(v, o);
+    w.K = (o.K + v.BK - 1) / v.BK * v.BK;
+    double c = variant_cost(v, w, cus);
+    if (w.N < o.N) {
+        Operands r = o;
+        r.N = o.N - w.N;
+        c += edge_cost(table, r, cus);
+    }
+    if (w.M < o.M) {
+        Operands b = o;
+        b.M = o.M - w.M;
+        b.N = w.N;
+        c += edge_cost(table, b, cus);
+    }
+    return c;
+}
+
 template <int NV>
 inline int choose_variant(const Variant (&table)[NV], const Operands &o, int cus)
 {
@@ -202,7 +265,7 @@ inline int choose_variant(const Variant (&table)[NV], const Operands &o, int cus
     for (int i = 0; i < NV; ++i) {
         const Variant &v = table[i];
         if (!v.planned || !variant_allowed(v, o) || (o.splits > 1 && !v.splitk)) continue;
-        const double c = variant_cost(v, o, cus);
+        const double c = plan_cost(table, i, o, cus);
         if (best < 0 || c < best_cost) { best = i; best_cost = c; }
     }
     return best;

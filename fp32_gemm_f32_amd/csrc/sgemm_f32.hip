@@ -114,8 +114,9 @@ VariantEntry regpanel_entry(const char *name, double rate, double overhead)
 
 // The persistent kernel (kernel_persist.hpp): 128 x 256 tiles of four 64 x 128 waves (one
 // per SIMD) or eight 64 x 64 waves (two per SIMD), one workgroup per CU, each tile's C
-// stored among the next tile's MFMAs. Whole tiles only, at least two K-panels; no split-K
-// or stream-K form.
+// stored among the next tile's MFMAs. Whole tiles only, at least two K-panels (the edges of
+// a ragged product run through the plan after it, run_persistent); no split-K or stream-K
+// form.
 VariantEntry persist_entry(const char *name, int waves, bool planned, double rate,
                            double overhead)
 {
@@ -280,7 +281,7 @@ int choose_streamk(const Operands &o, int cus, bool *sk)
     for (int i = 0; i < kNumVariants; ++i) {
         const Variant &v = g_table[i];
         if (!v.planned || !variant_allowed(v, o)) continue;
-        const double c_dp = variant_cost(v, o, cus);
+        const double c_dp = plan_cost(g_table, i, o, cus);
         if (best < 0 || c_dp < best_cost) { best = i; best_cost = c_dp; *sk = false; }
         if (!kVariants[i].kern_sk || v.sk_price <= 0.0) continue;
         double c_sk = 0.0;
@@ -390,7 +391,7 @@ int auto_splits(const Operands &o, int cus)
         q.splits = s;
         const int vi = choose_variant(g_table, q, cus);
         if (vi < 0) continue;
-        double us = variant_cost(g_table[vi], q, cus) / kUnitsPerUs;
+        double us = plan_cost(g_table, vi, q, cus) / kUnitsPerUs;
         if (s > 1) us += kReduceUs + double(s + 1) * double(o.M) * o.N * 4.0 / kReduceBytesPerUs;
         if (best_us < 0.0 || us < best_us) { best = s; best_us = us; }
     }
@@ -690,7 +691,7 @@ extern "C" int sgemm_f32_streamk_describe(int M, int N, int K, int variant, int 
     for (int i = 0; i < kNumVariants; ++i) {
         const Variant &w = g_table[i];
         if (!w.planned || !variant_allowed(w, o)) continue;
-        const double c = variant_cost(w, o, cus);
+        const double c = plan_cost(g_table, i, o, cus);
         if (c_plain < 0.0 || c < c_plain) c_plain = c;
     }
     // a plain plan may leave a thin remainder of N to the last tile column (strip_cols)
@@ -890,30 +891,35 @@ int describe_plan(int vi, const Operands &o, int cus, char *buf, int buflen)
 {
     const int M = o.M, N = o.N, K = o.K;
     const Variant &v = kVariants[vi].v;
-    const int strip = kVariants[vi].persistent ? 0 : strip_cols(v, o, cus);
-    const int64_t tm = (int64_t(M) + v.BM - 1) / v.BM,
-                  tn = (int64_t(N) - strip + v.BN - 1) / v.BN;
+    const bool pers = kVariants[vi].persistent;
+    const int strip = pers ? 0 : strip_cols(v, o, cus);
+    // a whole-tile variant's kernel covers the whole tiles; the edges run as launches of
+    // their own, planned for their shapes
+    const Operands w = pers ? whole_part(v, o) : o;
+    const int edges = pers ? int(w.M < M) + int(w.N < N) : 0;
+    const int64_t tm = (int64_t(w.M) + v.BM - 1) / v.BM,
+                  tn = (int64_t(w.N) - strip + v.BN - 1) / v.BN;
     // workgroups computing rows of the strip: every tile column holding some of its rows
     // (spread), or the last tile column
     const int srows = strip ? strip_form_rows(v, o, cus) : 0;
     const int64_t strip_tiles =
         !strip ? 0 : srows ? tm * std::min<int64_t>(tn, (v.BM + srows - 1) / srows) : tm;
     // one workgroup per tile, or for the persistent variant one per CU over its tiles
-    const int64_t grid = kVariants[vi].persistent ? std::min<int64_t>(tm * tn, cus)
-                                                  : tm * tn;
+    const int64_t grid = pers ? std::min<int64_t>(tm * tn, cus) : tm * tn;
     // operand bytes the tiles request: every A row panel once per tile column and every
     // B column panel once per tile row (before any cache reuse)
-    const int64_t tile_bytes = 4 * (int64_t(M) * K * tn + int64_t(K) * N * tm);
+    const int64_t tile_bytes = 4 * (int64_t(w.M) * K * tn + int64_t(K) * w.N * tm);
     const int n = snprintf(buf, size_t(buflen),
                            "{\"variant\": %d, \"name\": \"%s\", \"BM\": %d, \"BN\": %d, "
                            "\"BK\": %d, \"waves\": [%d, %d], \"threads\": %d, \"grid\": %lld, "
                            "\"tiles\": [%lld, %lld], \"cus\": %d, \"wg_per_cu\": %d, "
                            "\"direct_loads\": %s, \"tile_request_bytes\": %lld, "
-                           "\"strip_cols\": %d, \"strip_rows\": %d, \"strip_tiles\": %lld}",
+                           "\"strip_cols\": %d, \"strip_rows\": %d, \"strip_tiles\": %lld, "
+                           "\"edge_launches\": %d}",
                            vi, v.name, v.BM, v.BN, v.BK, v.wgm, v.wgn, kVariants[vi].threads,
                            (long long)grid, (long long)tm, (long long)tn, cus, v.wg_per_cu,
                            v.direct ? "true" : "false", (long long)tile_bytes, strip,
-                           srows, (long long)strip_tiles);
+                           srows, (long long)strip_tiles, edges);
     if (n < 0 || n >= buflen) return SGEMM_EINVAL_ARG;
     return vi;
 }
@@ -954,9 +960,15 @@ extern "C" int sgemm_f32_variant_describe(int variant, int M, int N, int K, int 
     int cus = 0;
     const int st = describe_args(M, N, K, lda, ldb, ldc, num_cus, buf, buflen, &o, &cus);
     if (st != SGEMM_OK) return st;
-    const int vi = variant >= 0 ? variant : choose_variant(g_table, o, cus);
+    int vi = variant >= 0 ? variant : choose_variant(g_table, o, cus);
     if (vi < 0) return SGEMM_ETOO_LARGE;
     if (!offsets_fit(kVariants[vi].v, o)) return SGEMM_ETOO_LARGE;
+    // as run_persistent: without a whole tile or a second K-panel the plan runs it all
+    const Variant &fv = kVariants[vi].v;
+    if (kVariants[vi].persistent && (M < fv.BM || N < fv.BN || K <= fv.BK)) {
+        vi = choose_variant(g_table, o, cus);
+        if (vi < 0) return SGEMM_ETOO_LARGE;
+    }
     return describe_plan(vi, o, cus, buf, buflen);
 }
 

@@ -291,8 +291,9 @@ const char *sgemm_f32_status_string(int status);
  * operand bytes the tiles request, and the column strip: "strip_cols" (the column past
  * the last whole tile column that the tiles also compute, 0 or 1), "strip_rows" (the
  * strip rows each tile of a row computes when they are spread over the row's tiles; 0
- * when the last tile column computes them all) and "strip_tiles" (how many tiles compute
- * some). The plan is the pages' tile-size trade-off: reuse
+ * when the last tile column computes them all), "strip_tiles" (how many tiles compute
+ * some) and "edge_launches" (0-2: the right and bottom edges a whole-tile variant leaves to
+ * kernels of their own). The plan is the pages' tile-size trade-off: reuse
  * per staged element against the parallelism left ("Shared Memory Tiling", "Choosing a
  * tile size"). Dimensions and leading dimensions are validated as in sgemm_f32
  * (SGEMM_EINVAL_DIM, SGEMM_EINVAL_LD); pointers are used for their alignment only and

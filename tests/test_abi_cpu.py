@@ -427,3 +427,29 @@ def test_variant_describe_strip_forms():
         g.sgemm_f32_variant_describe(len(g.variant_names()), 64, 64, 64, num_cus=cus)
     with pytest.raises(g.SgemmError):
         g.sgemm_f32_variant_describe(0, 64, 64, 64, 63, 64, 64, num_cus=cus)
+
+
+def test_persistent_plan_edges():
+    """The plan runs the persistent variant on the whole tiles of a ragged product and its
+    right and bottom edges as launches of their own, where that prices lowest; it keeps the
+    variant off rows of C that do not start on 32-byte boundaries and prices its panels
+    whole."""
+    ps = "mfma_128x256x32_w2x4_ps"
+    d = g.sgemm_f32_plan_describe(16383, 16384, 64, num_cus=256)
+    assert (d["name"], d["edge_launches"], d["tiles"], d["grid"]) == (ps, 1, [127, 64], 256), d
+    d = g.sgemm_f32_plan_describe(8200, 8200, 128, num_cus=256)
+    assert (d["name"], d["edge_launches"], d["tiles"]) == (ps, 2, [64, 32]), d
+    d = g.sgemm_f32_plan_describe(16384, 16384, 64, num_cus=256)
+    assert (d["name"], d["edge_launches"]) == (ps, 0), d
+    for ldc in (16385, 16388):
+        assert g.sgemm_f32_plan_describe(16384, 16384, 64, ldc=ldc, num_cus=256)["name"] != ps
+    assert g.sgemm_f32_plan_describe(16384, 16384, 64, ldc=16392, num_cus=256)["name"] == ps
+    assert g.sgemm_f32_plan_describe(16384, 16385, 64, num_cus=256)["name"] != ps
+    # K = 65 would run three whole 32-deep panels
+    assert g.sgemm_f32_plan_describe(16384, 16384, 65, num_cus=256)["name"] != ps
+    # forced on a product without a whole tile the variant leaves it all to the plan
+    v = g.variant_names().index(ps)
+    d = g.sgemm_f32_variant_describe(v, 100, 200, 64, num_cus=256)
+    assert d["name"] != ps and d["edge_launches"] == 0, d
+    d = g.sgemm_f32_variant_describe(v, 300, 600, 64, num_cus=256)
+    assert (d["name"], d["edge_launches"], d["tiles"]) == (ps, 2, [2, 2]), d

@@ -164,6 +164,32 @@ def test_persistent_variant_forced(gpu, M, N, K, name):
     assert rep["n_nonfinite"] == 0 and rep["n_inexact"] == 0, rep
 
 
+# Ragged products the plan gives to the persistent variant: its kernel on the whole tiles,
+# then the right edge (all rows, the columns past the last whole tile column) and the bottom
+# edge (the rows past the last whole tile row) as launches of their own, planned for their
+# shapes. Every row of the bottom edge is checked with sampled rows elsewhere, each across all
+# columns, so both edges are covered.
+PS_EDGE_PLANS = [(8200, 8200, 128, 2), (16383, 16384, 64, 1), (4096 + 77, 4096, 96, 1)]
+
+
+@pytest.mark.parametrize("M,N,K,edges", PS_EDGE_PLANS)
+def test_persistent_plan_with_edges(gpu, M, N, K, edges):
+    plan = g.sgemm_f32_plan_describe(M, N, K)
+    assert plan["name"] == "mfma_128x256x32_w2x4_ps" and plan["edge_launches"] == edges, plan
+    rng = np.random.default_rng(M + 3 * N + 5 * K)
+    A = wl.draw(rng, (M, K), "int")
+    B = wl.draw(rng, (K, N), "int")
+    _, dA, lda = device_matrix(A)
+    _, dB, ldb = device_matrix(B)
+    c = GuardedC(M, N)
+    print(f"[parity] {M}x{N}x{K} int auto (persistent, {edges} edge launches)", flush=True)
+    run_kernel("auto", M, N, K, dA, lda, dB, ldb, c)
+    gpu.cuda.synchronize()
+    rows = sorted(set(sample_rows(M, 16, seed=K) or []) | set(range(M // 128 * 128, M)))
+    rep = oracle.check(A, B, c.result(), rows=rows)
+    assert rep["n_nonfinite"] == 0 and rep["n_inexact"] == 0, rep
+
+
 # large shapes whose tile counts fall just past a whole round of 256 x 256 tiles
 STREAMK_PLAN_SHAPES = [(4500, 4500, 8192), (5000, 5000, 2048)]
 
