@@ -115,15 +115,26 @@ inline Operands whole_part(const Variant &v, const Operands &o)
 // Cost units: one multiply-add on one CU at rate 1 (140 TFLOP/s over 256 CUs).
 constexpr double kUnitsPerUs = 140e12 / 2 / 256 * 1e-6;
 // The strip's products run on the vector ALUs between the MFMAs of the tiles that compute
-// it. Spread over the tiles of each row, every tile runs about 1-5 % longer; in the last
-// tile column alone, those tiles run 7-11 % longer and the others not at all (measured at
-// steady state against the same shapes without the column: 1023 x 1025 x 1027 and
-// 1024 x 1025 x 1024 with 64 x 64 tiles, 2048 x 2049 x 2048, 4096 x 4097 x 4096 and
+// it. Spread over the tiles of each row, every tile runs about 1-5 % longer, in proportion
+// to its panels (each loads the panel's strip values); in the last tile column alone, those
+// tiles run 7-11 % longer and the others not at all (measured at steady state against the
+// same shapes without the column: 1023 x 1025 x 1027 and 1024 x 1025 x 1024 with 64 x 64
+// tiles of 64- and 32-deep panels, 2048 x 2049 x 2048, 4096 x 4097 x 4096 and
 // 8192 x 8193 x 1024 with 128 x 128 tiles). So the spread form wins while each CU runs
 // few tiles, the last-column form once the strip tiles are a small share of many rounds
-// (8192 x 8193 x 1024: 64 strip tiles among 4096).
+// (8192 x 8193 x 1024: 64 strip tiles among 4096). kStripSpreadShare is the share with
+// 64-deep panels; where two workgroups share each CU, the other one's MFMAs cover half of
+// it (128 x 128 tiles: 3.3 % at 2048 x 2049 x 2048, one tile per CU; 0.7 % at
+// 4096 x 4097 x 4096, four).
 constexpr double kStripSpreadShare = 0.02;
 constexpr double kStripColumnShare = 0.10;
+inline double strip_spread_share(const Variant &v, const Operands &o, int cus)
+{
+    const int64_t tm = (int64_t(o.M) + v.BM - 1) / v.BM;
+    const int64_t per_cu = (tm * (o.N / v.BN) + cus - 1) / cus;
+    const double share = kStripSpreadShare * 64.0 / v.BK;
+    return per_cu >= v.wg_per_cu ? share / v.wg_per_cu : share;
+}
 
 // Busiest-CU estimate for variant v with tn tile columns, in multiply-adds at rate 1.
 inline double tiles_cost(const Variant &v, const Operands &o, int cus, int64_t tn)
@@ -153,14 +164,14 @@ inline double strip_column_share(const Variant &v, const Operands &o, int cus)
 inline int strip_form_rows(const Variant &v, const Operands &o, int cus)
 {
     const int rows = strip_spread_rows(v, o);
-    return rows > 0 && kStripSpreadShare < strip_column_share(v, o, cus) ? rows : 0;
+    return rows > 0 && strip_spread_share(v, o, cus) < strip_column_share(v, o, cus) ? rows : 0;
 }
 
 // The same with a column strip of the last N mod BN columns (strip_eligible), in the form
 // strip_form_rows picks.
 inline double strip_cost(const Variant &v, const Operands &o, int cus)
 {
-    const double share = strip_form_rows(v, o, cus) > 0 ? kStripSpreadShare
+    const double share = strip_form_rows(v, o, cus) > 0 ? strip_spread_share(v, o, cus)
                                                         : strip_column_share(v, o, cus);
     return tiles_cost(v, o, cus, o.N / v.BN) * (1.0 + share);
 }

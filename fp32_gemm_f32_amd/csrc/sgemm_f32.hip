@@ -155,8 +155,12 @@ const VariantEntry kVariants[] = {
     entry<128, 128, 32, 2, 2, 1, 1, true, true>("mfma_128x128x32_w2x2_dl", 2, 1.070, 12, 0.95),
     entry<64, 64, 32, 2, 1, 2, 4, true, false>("mfma_64x64x32_w2x1_acc2_kg4_dl", 1, 0.880, 212, 1.0),
     // its stream-K form is not planned: at 1536^2 x 4096 it ran 25 % slower than the plain
-    // plan that its price matched (it still runs when forced)
-    entry<64, 64, 32, 2, 1, 1, 2, true, true>("mfma_64x64x32_w2x1_kg2_dl", 2, 1.015, 92, 0.78,
+    // plan that its price matched (it still runs when forced). With one tile per CU (one wave
+    // per SIMD) it runs 0.3-2.7 % ahead of the 64 x 64 x 64 tile up to K = 2048 and behind it
+    // from K = 3072, and behind it with a column strip (1024^2 x 512 .. 4096, 1000^3,
+    // 1023 x 1024 x 1027 against 1023 x 1025 x 1027, steady state); its solo factor of 0.92
+    // puts the two on those sides.
+    entry<64, 64, 32, 2, 1, 1, 2, true, true>("mfma_64x64x32_w2x1_kg2_dl", 2, 1.015, 92, 0.92,
                                               0.0),
     entry<256, 256, 32, 4, 2, 1, 1, false, false>("mfma_256x256x32_w4x2", 1, 1.045, 52, 1.0),
     entry<80, 64, 32, 1, 2, 1, 4, true, true, 16>("mfma16_80x64x32_w1x2_kg4_dl", 1, 0.985, 236, 1.0),

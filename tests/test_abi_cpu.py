@@ -366,7 +366,7 @@ def test_one_hip_runtime_in_the_process():
 # one of them needs new measurements.
 WORKLOAD_PLANS = {
     "c1": ("mfma_128x256x16_w2x2_dl", 0),
-    "c2": ("mfma16_64x64x64_w2x2_kg2_dl", 0),
+    "c2": ("mfma_64x64x32_w2x1_kg2_dl", 0),
     "c3": ("mfma16_64x64x64_w2x2_kg2_dl", 1),
     "c4": ("mfma_256x256x32_w2x2_rp", 0),
     "c5": ("mfma_128x256x32_w2x4_ps", 0),
