@@ -348,9 +348,9 @@ struct MfmaTile {
     // The tile's stores are shared by the K-groups: store unit (r, g, q), the quad q of
     // accumulator registers (4 rows) of row block r and column group g (CI blocks side by
     // side), belongs to K-group u KG / UNITS for unit index u = (r CG + g) ACC/4 + q. After
-    // the last panel each group passes its partial sums of the others' units through LDS
-    // (one f32x4 per block and lane, in a slot per writing group and unit), reusing the
-    // stages' memory, and the owner adds them.
+    // the last panel each group writes its partial sums of the other groups' units to LDS
+    // (one f32x4 per block, quad and lane, in a slot per writing group), reusing the stages'
+    // memory, and the owner of each unit adds them and its own in ascending group order.
     static constexpr int UNITS = RB * CG * (ACC / 4);
     static constexpr int RED = KG > 1 ? KG * kGroupThreads * NACC * ACC : 0;
     // Column strip (see the kernel): per stage, 64 floats of the strip's B column (one per
@@ -921,8 +921,8 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
         return reinterpret_cast<f32x4 *>(
             red + (((w * T::NACC + r * CI * CG + j) * (T::ACC / 4) + q) * NT + tid) * 4);
     };
-    // Sum the accumulator sets into acc[0]; then (KG > 1) each group adds the other groups'
-    // sums of its own store units, in ascending group order, into its acc[0].
+    // Sum the accumulator sets into acc[0]; then (KG > 1) each group adds all groups' sums
+    // of its own store units, in ascending group order, into its acc[0].
     auto finish = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int h = 1; h < KACC; ++h)
@@ -959,16 +959,23 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
                     static_for<0, T::ACC / 4>([&](auto qc) {
                         constexpr int q = decltype(qc)::value;
                         if (unit_owner(i, g, q) == kg) {
+                            // the owner's own slot is not written: its sums come from
+                            // registers, and in its place the loop reads (and drops) the
+                            // slot of another group, which is
+                            const int alt = kg == 0 ? 1 : 0;
 #pragma unroll
                             for (int c = 0; c < CI; ++c) {
                                 acc_t &x = acc[0][i][g * CI + c];
                                 const f32x4 own = {x[4 * q], x[4 * q + 1], x[4 * q + 2],
                                                    x[4 * q + 3]};
-                                // the slot of the owner itself holds nothing; its sums come
-                                // from registers
-                                f32x4 sum = kg == 0 ? own : *red_slot(0, i, g * CI + c, q);
-                                for (int w = 1; w < KG; ++w)
-                                    sum += w == kg ? own : *red_slot(w, i, g * CI + c, q);
+                                f32x4 sum;
+#pragma unroll
+                                for (int w = 0; w < KG; ++w) {
+                                    const f32x4 part = *red_slot(w == kg ? alt : w, i,
+                                                                 g * CI + c, q);
+                                    const f32x4 v = w == kg ? own : part;
+                                    sum = w == 0 ? v : sum + v;
+                                }
 #pragma unroll
                                 for (int e = 0; e < 4; ++e) x[4 * q + e] = sum[e];
                             }
