@@ -169,20 +169,25 @@ def test_persistent_variant_forced(gpu, M, N, K, name):
 # edge (the rows past the last whole tile row) as launches of their own, planned for their
 # shapes. Every row of the bottom edge is checked with sampled rows elsewhere, each across all
 # columns, so both edges are covered.
-PS_EDGE_PLANS = [(8200, 8200, 128, 2), (16383, 16384, 64, 1), (4096 + 77, 4096, 96, 1)]
+# The last case pads every row (A and B with NaN, C with guard cells; C's rows stay on 32-byte
+# boundaries, which the plan asks of this kernel).
+PS_EDGE_PLANS = [(8200, 8200, 128, 2, 0), (16383, 16384, 64, 1, 0), (4096 + 77, 4096, 96, 1, 0),
+                 (8200, 8300, 96, 2, 1)]
 
 
-@pytest.mark.parametrize("M,N,K,edges", PS_EDGE_PLANS)
-def test_persistent_plan_with_edges(gpu, M, N, K, edges):
-    plan = g.sgemm_f32_plan_describe(M, N, K)
+@pytest.mark.parametrize("M,N,K,edges,padded", PS_EDGE_PLANS)
+def test_persistent_plan_with_edges(gpu, M, N, K, edges, padded):
+    lda, ldb, ldc = (K + 3, N + 5, N + 12) if padded else (K, N, N)
+    plan = g.sgemm_f32_plan_describe(M, N, K, lda=lda, ldb=ldb, ldc=ldc)
     assert plan["name"] == "mfma_128x256x32_w2x4_ps" and plan["edge_launches"] == edges, plan
     rng = np.random.default_rng(M + 3 * N + 5 * K)
     A = wl.draw(rng, (M, K), "int")
     B = wl.draw(rng, (K, N), "int")
-    _, dA, lda = device_matrix(A)
-    _, dB, ldb = device_matrix(B)
-    c = GuardedC(M, N)
-    print(f"[parity] {M}x{N}x{K} int auto (persistent, {edges} edge launches)", flush=True)
+    _, dA, lda = device_matrix(A, lda)
+    _, dB, ldb = device_matrix(B, ldb)
+    c = GuardedC(M, N, ldc)
+    print(f"[parity] {M}x{N}x{K} int auto (persistent, {edges} edge launches, "
+          f"lda={lda} ldb={ldb} ldc={ldc})", flush=True)
     run_kernel("auto", M, N, K, dA, lda, dB, ldb, c)
     gpu.cuda.synchronize()
     rows = sorted(set(sample_rows(M, 16, seed=K) or []) | set(range(M // 128 * 128, M)))
