@@ -5,12 +5,14 @@
 // Tiling", "Choosing a tile size"; "Visual walkthrough - Memory hierarchy", Step 7). On
 // gfx950 the parallelism to fill is 256 compute units of 4 SIMDs. The choice below
 // estimates, for each variant the operands allow, the time of the busiest compute unit,
-//     ceil(tiles / CUs) x (work of one tile / the variant's measured rate + per-tile overhead),
-// and takes the smallest. The overhead (first-panel latency and epilogue stores not hidden
-// behind MFMAs) depends on the variant: with two resident workgroups per CU one's epilogue
-// overlaps the other's MFMAs. Such a variant runs slower when the busiest CU gets fewer
-// tiles than it can hold at once (it then lacks the second workgroup to overlap with); its
-// rate is scaled by `solo` in that case.
+//     ceil(tiles / CUs) x (work of one tile / the variant's measured rate + per-tile overhead)
+//     + the launch's latency,
+// and takes the smallest. The overhead (per-tile work that does not scale with K: the
+// K-group sums, the epilogue's stores as far as other tiles' MFMAs do not cover them)
+// and the latency (once per launch: the first panels' loads, which nothing overlaps, and
+// the last tiles' stores) depend on the variant. A variant with two resident workgroups
+// per CU runs slightly slower when the busiest CU gets fewer tiles than it can hold at
+// once; its rate is scaled by `solo` in that case.
 #pragma once
 
 #include <cstdint>
@@ -46,6 +48,8 @@ struct Variant {
     // multiplier on the stream-K price (streamk_cost) of this variant's stream-K form; 0: the
     // form is not planned (it still runs when forced)
     double sk_price = kStreamkPrice;
+    // the launch's fixed time, in microseconds (see above)
+    double latency = 0.0;
 };
 
 struct Operands {
@@ -215,7 +219,8 @@ inline double streamk_cost(const Variant &v, const Operands &o, int cus, const S
     // contributors of the most shared tile: its units over a range's length, plus one
     const double contrib = double(g.panels) * g.G / double(g.iters) + 2.0;
     const double batches = contrib / kFixupBatch + 1.0;
-    return (work + (kFixupUs + batches * kFixupBatchUs + double(ws_bytes) / kPartialBytesPerUs) *
+    return (work + (v.latency + kFixupUs + batches * kFixupBatchUs +
+                    double(ws_bytes) / kPartialBytesPerUs) *
                        kUnitsPerUs) *
            (v.sk_price > 0.0 ? v.sk_price : 1.0);
 }
@@ -243,12 +248,13 @@ inline double edge_cost(const Variant (&table)[NV], const Operands &o, int cus)
 // Price of running variant i of the table on o as the plain entry does: variant_cost, or for
 // a whole-tile variant its whole-tile part plus the right edge (all rows, the columns past
 // the last whole tile column) and the bottom edge (the rows past the last whole tile row,
-// the whole tile columns), each priced as the plan would run it.
+// the whole tile columns), each priced as the plan would run it; plus the variant's latency.
 template <int NV>
 inline double plan_cost(const Variant (&table)[NV], int i, const Operands &o, int cus)
 {
     const Variant &v = table[i];
-    if (!v.whole_tiles) return variant_cost(v, o, cus);
+    const double latency = v.latency * kUnitsPerUs;
+    if (!v.whole_tiles) return variant_cost(v, o, cus) + latency;
     // its panels run whole: a K that is not a multiple of BK costs the last one in full
     // (16384^2 x 65: 1.05x the 128 x 256 x 16 tile's time, against 0.92x at K = 64)
     Operands w = whole_part(v, o);
@@ -265,7 +271,7 @@ inline double plan_cost(const Variant (&table)[NV], int i, const Operands &o, in
         b.N = w.N;
         c += edge_cost(table, b, cus);
     }
-    return c;
+    return c + latency;
 }
 
 template <int NV>

@@ -79,7 +79,7 @@ struct VariantEntry {
 template <int BM, int BN, int BK, int WGM, int WGN, int KACC, int KG, bool DL, bool PLANNED,
           int MB = 32, int NSTG = 2>
 constexpr VariantEntry entry(const char *name, int wg_per_cu, double rate, double overhead,
-                             double solo, double sk_price = kStreamkPrice)
+                             double solo, double latency, double sk_price = kStreamkPrice)
 {
     MfmaKernel sk = nullptr, fix = nullptr;
     if constexpr (PLANNED) {
@@ -93,6 +93,7 @@ constexpr VariantEntry entry(const char *name, int wg_per_cu, double rate, doubl
     // the kernel's column strip (kernel_mfma.hpp): direct loads and room in LDS
     e.v.strip = DL && MfmaTile<BM, BN, BK, WGM, WGN, KACC, KG, MB, NSTG>::STRIP_OK;
     e.v.sk_price = sk_price;
+    e.v.latency = latency;
     e.stages = NSTG;
     return e;
 }
@@ -100,7 +101,7 @@ constexpr VariantEntry entry(const char *name, int wg_per_cu, double rate, doubl
 // The one-wave-per-SIMD kernel (kernel_regpanel.hpp): 256 x 256 tiles of four 128 x 128
 // waves, with a stream-K form. Split-K does not plan it: its shapes have few tiles, where
 // the smaller tiles win.
-VariantEntry regpanel_entry(const char *name, double rate, double overhead)
+VariantEntry regpanel_entry(const char *name, double rate, double overhead, double latency)
 {
     VariantEntry e{
         Variant{name, 256, 256, 32, 2, 2, 1, rate, overhead, 1.0, false, true, false},
@@ -109,6 +110,7 @@ VariantEntry regpanel_entry(const char *name, double rate, double overhead)
     // its stream-K form runs about 2 % over its price (4500^2 x 8192, 3000^2 x 8192,
     // 2500^2 x 16384, measured at steady state), besides the plain model's drift
     e.v.sk_price = 1.06;
+    e.v.latency = latency;
     return e;
 }
 
@@ -118,7 +120,7 @@ VariantEntry regpanel_entry(const char *name, double rate, double overhead)
 // a ragged product run through the plan after it, run_persistent); no split-K or stream-K
 // form.
 VariantEntry persist_entry(const char *name, int waves, bool planned, double rate,
-                           double overhead)
+                           double overhead, double latency)
 {
     VariantEntry e{Variant{name, 128, 256, 32, 2, waves / 2, 1, rate, overhead, 1.0, false, planned,
                            false},
@@ -126,14 +128,21 @@ VariantEntry persist_entry(const char *name, int waves, bool planned, double rat
     e.v.whole_tiles = true;
     e.persistent = true;
     e.kern_ktail = persist_ktail_kernel(waves);
+    e.v.latency = latency;
     return e;
 }
 
-// Rates (throughput at 8192^3 relative to 140 TFLOP/s), per-tile overheads (in units of K)
-// and solo factors are fitted on MI355X to runs that timed every variant on 19 shapes from
-// 1023 x 1025 x 1027 to 16384^2 x 64, and checked at steady state on 40 shapes (bench.py
-// --plan-sweep): the plan's pick is within 1 % of the fastest variant on 39 of them and
-// within 3.0 % on all. The template kernel's planned variants load their panels
+// Rates (throughput relative to 140 TFLOP/s), per-tile overheads (in units of K), solo
+// factors and launch latencies (microseconds) of the planned variants are fitted on MI355X
+// to steady-state times of every planned variant, forced, on 154 shapes (bench.py
+// --plan-sweep): 68 chosen ones (1024-class, ragged, mid-size, low K, one tile per CU and
+// many, K up to 32768) and 86 drawn at random (M and N log-uniform in 256..16384, K in
+// 32..8192, at most 2e11 multiply-adds). Each variant's four constants are fitted first to
+// its own times (least squares on the logarithm), then moved, from there, to lower the
+// plan's regret over those shapes while the picks for 1024^3, 1023 x 1025 x 1027, 8192^3,
+// 16384^2 x 64 and 256^2 x 32768 stay the fastest variants measured there. The forced-only
+// variants keep the constants of the earlier fit (19 shapes) and no latency: the plan never
+// prices them. The template kernel's planned variants load their panels
 // straight into LDS ("_dl"), which measured as fast as or faster than staging through
 // registers on every one of those shapes.
 //  * 256 x 256, one wave per SIMD ("_rp", kernel_regpanel.hpp): long K and many tiles
@@ -150,48 +159,55 @@ VariantEntry persist_entry(const char *name, int waves, bool planned, double rat
 // The last entry stages through registers; it is never planned and stays as the measured
 // comparison for the direct loads (forced through sgemm_f32_variant).
 const VariantEntry kVariants[] = {
-    entry<256, 256, 32, 4, 2, 1, 1, true, false>("mfma_256x256x32_w4x2_dl", 1, 1.085, 40, 1.0),
-    entry<128, 256, 16, 2, 2, 1, 1, true, true>("mfma_128x256x16_w2x2_dl", 2, 1.045, 0, 0.88),
-    entry<128, 128, 32, 2, 2, 1, 1, true, true>("mfma_128x128x32_w2x2_dl", 2, 1.070, 12, 0.95),
-    entry<64, 64, 32, 2, 1, 2, 4, true, false>("mfma_64x64x32_w2x1_acc2_kg4_dl", 1, 0.880, 212, 1.0),
+    entry<256, 256, 32, 4, 2, 1, 1, true, false>("mfma_256x256x32_w4x2_dl", 1, 1.085, 40, 1.0, 0.0),
+    entry<128, 256, 16, 2, 2, 1, 1, true, true>("mfma_128x256x16_w2x2_dl", 2, 1.099, 38, 0.972,
+                                                 3.30),
+    entry<128, 128, 32, 2, 2, 1, 1, true, true>("mfma_128x128x32_w2x2_dl", 2, 1.099, 46, 0.978,
+                                                 2.30),
+    entry<64, 64, 32, 2, 1, 2, 4, true, false>("mfma_64x64x32_w2x1_acc2_kg4_dl", 1, 0.880, 212, 1.0,
+                                                0.0),
     // its stream-K form is not planned: at 1536^2 x 4096 it ran 25 % slower than the plain
     // plan that its price matched (it still runs when forced). With one tile per CU (one wave
-    // per SIMD) it runs 0.3-2.7 % ahead of the 64 x 64 x 64 tile up to K = 2048 and behind it
-    // from K = 3072, and behind it with a column strip (1024^2 x 512 .. 4096, 1000^3,
-    // 1023 x 1024 x 1027 against 1023 x 1025 x 1027, steady state); its solo factor of 0.92
-    // puts the two on those sides.
-    entry<64, 64, 32, 2, 1, 1, 2, true, true>("mfma_64x64x32_w2x1_kg2_dl", 2, 1.015, 92, 0.92,
-                                              0.0),
-    entry<256, 256, 32, 4, 2, 1, 1, false, false>("mfma_256x256x32_w4x2", 1, 1.045, 52, 1.0),
-    entry<80, 64, 32, 1, 2, 1, 4, true, true, 16>("mfma16_80x64x32_w1x2_kg4_dl", 1, 0.985, 236, 1.0),
-    entry<80, 64, 32, 1, 2, 1, 2, true, true, 16>("mfma16_80x64x32_w1x2_kg2_dl", 2, 1.025, 64, 0.84),
-    entry<48, 64, 32, 1, 2, 1, 4, true, true, 16>("mfma16_48x64x32_w1x2_kg4_dl", 1, 0.975, 256, 1.0),
-    entry<64, 64, 64, 2, 2, 1, 2, true, true, 16>("mfma16_64x64x64_w2x2_kg2_dl", 1, 1.020, 196, 1.0),
-    regpanel_entry("mfma_256x256x32_w2x2_rp", 1.105, 20),
-    persist_entry("mfma_128x256x32_w2x2_ps", 4, false, 1.05, 0),
-    persist_entry("mfma_128x256x32_w2x4_ps", 8, true, 1.10, 0),
+    // per SIMD) it runs 0.3-3 % ahead of the 64 x 64 x 64 tile up to K = 1024, within 0.6 %
+    // of it at K = 1536-2048 and behind it from K = 3072, and behind it with a column strip
+    // (1024^2 x 512 .. 4096, 1000^3, 1023 x 1024 x 1027 against 1023 x 1025 x 1027, steady
+    // state).
+    entry<64, 64, 32, 2, 1, 1, 2, true, true>("mfma_64x64x32_w2x1_kg2_dl", 2, 1.039, 76, 0.993,
+                                              2.80, 0.0),
+    entry<256, 256, 32, 4, 2, 1, 1, false, false>("mfma_256x256x32_w4x2", 1, 1.045, 52, 1.0, 0.0),
+    entry<80, 64, 32, 1, 2, 1, 4, true, true, 16>("mfma16_80x64x32_w1x2_kg4_dl", 1, 1.041, 168, 1.0,
+                                                   2.00),
+    entry<80, 64, 32, 1, 2, 1, 2, true, true, 16>("mfma16_80x64x32_w1x2_kg2_dl", 2, 1.063, 75, 0.960,
+                                                   3.00),
+    entry<48, 64, 32, 1, 2, 1, 4, true, true, 16>("mfma16_48x64x32_w1x2_kg4_dl", 1, 0.975, 218, 1.0,
+                                                   1.80),
+    entry<64, 64, 64, 2, 2, 1, 2, true, true, 16>("mfma16_64x64x64_w2x2_kg2_dl", 1, 1.041, 161, 1.0,
+                                                   1.85),
+    regpanel_entry("mfma_256x256x32_w2x2_rp", 1.114, 51, 3.60),
+    persist_entry("mfma_128x256x32_w2x2_ps", 4, false, 1.05, 0, 0.0),
+    persist_entry("mfma_128x256x32_w2x4_ps", 8, true, 1.110, 29, 2.65),
     // 64 x 64 in 16-row blocks, two K-groups of four 32 x 32 waves, 32-deep panels (forced
     // use only)
     entry<64, 64, 32, 2, 2, 1, 2, true, false, 16>("mfma16_64x64x32_w2x2_kg2_dl", 2, 1.0, 26,
-                                                   0.887),
+                                                   0.887, 0.0),
     // the same tile and the 32 x 32 one of two K-groups with three LDS stages per K-group:
     // each panel's loads are issued two panels ahead (96 KiB of LDS, one workgroup per CU;
     // forced use only)
     entry<64, 64, 32, 2, 2, 1, 2, true, false, 16, 3>("mfma16_64x64x32_w2x2_kg2_s3_dl", 1, 1.0,
-                                                      26, 1.0),
+                                                      26, 1.0, 0.0),
     entry<64, 64, 32, 2, 1, 1, 2, true, false, 32, 3>("mfma_64x64x32_w2x1_kg2_s3_dl", 1, 1.0, 92,
-                                                      1.0),
+                                                      1.0, 0.0),
     // Tiles of one 32 x 32 block per wave for products with few 64 x 64 tiles (under one per
     // CU): 32 x 32 as eight K-groups of one wave (two per SIMD) with three LDS stages, whose
     // 16-deep panels are too short for two stages to hide a load (the two-stage form stays as
     // the measured comparison, forced use only); and 32 x 64 as four K-groups of two waves.
-    // Fitted at steady state on 512^2 x 2048 .. 8192, 384^2 x 4096, 1024 x 512 x 2048 and
-    // 640^2 x 4096. Their stream-K forms are not planned (not calibrated).
-    entry<32, 32, 16, 1, 1, 1, 8, true, true, 32, 3>("mfma_32x32x16_w1x1_kg8_s3_dl", 1, 0.8125,
-                                                     1082, 1.0, 0.0),
-    entry<32, 32, 16, 1, 1, 1, 8, true, false>("mfma_32x32x16_w1x1_kg8_dl", 1, 0.8125, 1082, 1.0),
-    entry<32, 64, 32, 1, 2, 1, 4, true, true>("mfma_32x64x32_w1x2_kg4_dl", 1, 0.935, 549, 1.0,
-                                              0.0),
+    // Their stream-K forms are not planned (not calibrated).
+    entry<32, 32, 16, 1, 1, 1, 8, true, true, 32, 3>("mfma_32x32x16_w1x1_kg8_s3_dl", 1, 0.787,
+                                                     583, 1.0, 1.65, 0.0),
+    entry<32, 32, 16, 1, 1, 1, 8, true, false>("mfma_32x32x16_w1x1_kg8_dl", 1, 0.8125, 1082, 1.0,
+                                               0.0),
+    entry<32, 64, 32, 1, 2, 1, 4, true, true>("mfma_32x64x32_w1x2_kg4_dl", 1, 0.895, 295, 1.0,
+                                              1.75, 0.0),
 };
 constexpr int kNumVariants = int(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -857,13 +873,13 @@ extern "C" int sgemm_f32_variant_info(int variant, char *buf, int buflen)
                            "\"BK\": %d, \"waves\": [%d, %d], \"k_groups\": %d, "
                            "\"threads\": %d, \"mfma\": \"%dx%dx%d\", \"wg_per_cu\": %d, "
                            "\"direct_loads\": %s, \"planned\": %s, \"streamk\": %s, "
-                           "\"rate\": %.3f, \"overhead\": %.1f, \"solo\": %.2f, "
+                           "\"rate\": %.3f, \"overhead\": %.1f, \"solo\": %.3f, \"latency_us\": %.2f, "
                            "\"kernel\": \"%s\", \"splitk\": %s, \"persistent\": %s, "
                            "\"whole_tiles\": %s, \"strip\": %s, \"lds_stages\": %d}",
                            variant, v.name, v.BM, v.BN, v.BK, v.wgm, v.wgn, e.kg, e.threads, e.mb,
                            e.mb, e.mb == 32 ? 2 : 4, v.wg_per_cu, v.direct ? "true" : "false",
                            v.planned ? "true" : "false", e.kern_sk ? "true" : "false", v.rate,
-                           v.overhead, v.solo, e.kernel, v.splitk ? "true" : "false",
+                           v.overhead, v.solo, v.latency, e.kernel, v.splitk ? "true" : "false",
                            e.persistent ? "true" : "false", v.whole_tiles ? "true" : "false",
                            v.strip ? "true" : "false", e.stages);
     if (n < 0 || n >= buflen) return SGEMM_EINVAL_ARG;

@@ -365,7 +365,7 @@ def test_one_hip_runtime_in_the_process():
 # committed profile under profiles/ was taken on). A change to the cost model that moves
 # one of them needs new measurements.
 WORKLOAD_PLANS = {
-    "c1": ("mfma_128x256x16_w2x2_dl", 0),
+    "c1": ("mfma_32x32x16_w1x1_kg8_s3_dl", 0),
     "c2": ("mfma_64x64x32_w2x1_kg2_dl", 0),
     "c3": ("mfma16_64x64x64_w2x2_kg2_dl", 1),
     "c4": ("mfma_256x256x32_w2x2_rp", 0),

@@ -92,7 +92,8 @@ def test_every_variant_on_configs(gpu, name):
 
 AT_SCALE = [(2048, 2048, 2048), (3000, 3000, 3000), (16384, 16384, 256), (4096, 4096, 4096),
             (1200, 1200, 500), (1279, 1279, 2000), (1100, 1100, 1100),
-            (1100, 1100, 4096), (512, 512, 4096), (1024, 512, 2048), (383, 385, 16387)]
+            (1100, 1100, 4096), (512, 512, 4096), (1024, 512, 2048), (383, 385, 16387),
+            (1516, 8811, 39)]
 
 
 @pytest.mark.parametrize("M,N,K", AT_SCALE)
