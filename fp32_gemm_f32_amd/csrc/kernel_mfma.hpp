@@ -128,8 +128,17 @@ struct GemmArgs {
     int strip_rows;
 };
 
-// Most columns a strip may hold: a one-column remainder of N past the last whole tile column.
-constexpr int kStripCols = 1;
+// Most columns a strip may hold: a remainder of N past the last whole tile column of up to
+// four columns (a tile's own limit is MfmaTile::STRIP_COLS_MAX; past one column only the
+// spread form computes it).
+constexpr int kStripCols = 4;
+
+// Strip columns loaded per panel by the kernel's strip modes: 1 the last tile column's
+// (one column), 2, 3 and 4 the spread form's one, two and four columns; 0 none.
+__host__ __device__ constexpr int strip_mode_cols(int smode)
+{
+    return smode == 3 ? 2 : smode == 4 ? 4 : smode >= 1 ? 1 : 0;
+}
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const float *base, int64_t bytes)
 {
@@ -358,17 +367,42 @@ struct MfmaTile {
     // partial sums: one row per K-group and MFMA lane group, STRIP_RS floats apart. The
     // row stride is 64 / H words past a multiple of 64, so the H lane groups of a wave,
     // which write the same rows' sums into H different rows, hit different banks.
+    // A strip of sc columns holds sc such columns per stage and K-group, and the spread
+    // form's reduction area one float per thread, K-group and column.
     static constexpr int STRIP_STAGE = 64;
     static constexpr int STRIP_RS = (BM + 63) / 64 * 64 + 64 / MfmaShape<MB>::H;
-    static constexpr int STRIP_RED = KG * MfmaShape<MB>::H * STRIP_RS > KG * kGroupThreads
-                                         ? KG * MfmaShape<MB>::H * STRIP_RS
-                                         : KG * kGroupThreads;
-    static constexpr int STRIP_FLOATS = NSTG * KG * STRIP_STAGE + STRIP_RED;
+    static constexpr int strip_red_for(int sc)
+    {
+        return KG * MfmaShape<MB>::H * STRIP_RS > KG * kGroupThreads * sc
+                   ? KG * MfmaShape<MB>::H * STRIP_RS
+                   : KG * kGroupThreads * sc;
+    }
+    static constexpr int strip_floats_for(int sc)
+    {
+        return NSTG * KG * STRIP_STAGE * sc + strip_red_for(sc);
+    }
     // NSTG LDS stages per K-group
     static constexpr int STAGES = NSTG * KG * STAGE;
-    static constexpr bool STRIP_OK = BM <= kGroupThreads * KG && BK <= 64 && RED <= STAGES &&
-                                     (STAGES + STRIP_FLOATS) * 4 <= 160 * 1024;
     static constexpr int BASE_FLOATS = STAGES > RED ? STAGES : RED;
+    static constexpr int lds_floats_for(int sc)
+    {
+        return STAGES + strip_floats_for(sc) > BASE_FLOATS ? STAGES + strip_floats_for(sc)
+                                                           : BASE_FLOATS;
+    }
+    // workgroups per CU that the LDS allows
+    static constexpr int lds_occupancy(int floats) { return 160 * 1024 / (floats * 4); }
+    static constexpr bool STRIP_OK = BM <= kGroupThreads * KG && BK <= 64 && RED <= STAGES &&
+                                     (STAGES + strip_floats_for(1)) * 4 <= 160 * 1024;
+    // The widest strip the tile takes: four columns, or two, where the room for them in LDS
+    // leaves as many workgroups per CU as one column does; else one.
+    static constexpr bool strip_fits(int sc)
+    {
+        return (STAGES + strip_floats_for(sc)) * 4 <= 160 * 1024 &&
+               lds_occupancy(lds_floats_for(sc)) == lds_occupancy(lds_floats_for(1));
+    }
+    static constexpr int STRIP_COLS_MAX = !STRIP_OK ? 0 : strip_fits(4) ? 4 : strip_fits(2) ? 2 : 1;
+    static constexpr int STRIP_RED = strip_red_for(STRIP_COLS_MAX > 0 ? STRIP_COLS_MAX : 1);
+    static constexpr int STRIP_FLOATS = strip_floats_for(STRIP_COLS_MAX > 0 ? STRIP_COLS_MAX : 1);
     static constexpr int LDS_FLOATS =
         STRIP_OK && STAGES + STRIP_FLOATS > BASE_FLOATS ? STAGES + STRIP_FLOATS : BASE_FLOATS;
     static constexpr int LDS_BYTES = LDS_FLOATS * 4;
@@ -679,15 +713,17 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     constexpr int PER_WRITE = (NL + WS - 1) / WS;
     static_assert(LS + WS < STEPS, "loads and LDS writes of a panel need separate steps");
 
-    // ---- column strip: the tiles also compute the column of C past the last tile column
-    // (strip_cols = 1), instead of a column of tiles that would hold one valid column. The
-    // strip's B values of a panel (zeros past the K range) are loaded straight into LDS
-    // with the panel, stage s of group kg at strip_lds + (s KG + kg) STRIP_STAGE, value k
-    // of the panel at + k, by the group's first wave. Two forms:
+    // ---- column strip: the tiles also compute the strip_cols (1 to STRIP_COLS_MAX)
+    // columns of C past the last tile column, instead of a column of tiles that would hold
+    // that many valid columns. The strip's B values of a panel (zeros past the K range and
+    // past strip_cols) are loaded straight into LDS with the panel, column j of stage s of
+    // group kg at strip_lds + ((s KG + kg) SCM + j) STRIP_STAGE, value k of the panel at
+    // + k, by the group's first wave. Two forms:
     //  * spread (strip_rows > 0): each tile of a row computes strip_rows of the row's strip
-    //    rows, from the A panel in LDS (below, set_spread_item);
-    //  * last column (strip_rows = 0): the tiles of the last tile column compute all of
-    //    them. The MFMA's A operands already hold, in each lane, four consecutive values of
+    //    rows, from the A panel in LDS (below, set_spread_item), for one, two or four
+    //    columns (three: four, the last one zero);
+    //  * last column (strip_rows = 0, one column): the tiles of the last tile column compute
+    //    all of them. The MFMA's A operands already hold, in each lane, four consecutive values of
     //    k of each of the lane's rows (k-group kb: 4 (H kb + hi) .. + 3); a lane multiplies
     //    them by the strip's four B values for those k (one 16-byte LDS read per k-group,
     //    the same address for all lanes of a lane group) into sacc, on the vector ALU
@@ -700,8 +736,9 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     // K-group's threads cover a tile's share of the rows and few rounds of tiles make
     // that cheaper than the last-column form (strip_form_rows).
     constexpr bool CAN_STRIP = !SK && DL && T::STRIP_OK;
+    constexpr int SCM = T::STRIP_COLS_MAX > 0 ? T::STRIP_COLS_MAX : 1;   // columns per stage
     float *const strip_lds = lds_all + T::STAGES;
-    float *const strip_red = strip_lds + NSTG * KG * T::STRIP_STAGE;
+    float *const strip_red = strip_lds + NSTG * KG * SCM * T::STRIP_STAGE;
     __amdgpu_buffer_rsrc_t rss;
     uint32_t s_off = kOob;
     float sacc[RB];
@@ -711,19 +748,26 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
 #pragma unroll
         for (int r = 0; r < RB; ++r) sacc[r] = 0.0f;
     };
-    // the strip's B resource for the panel at k0 of the item: it ends at the last row of the
-    // K range (rows past it read zeros)
+    // the strip's B resource for the panel at k0 of the item: it ends with the strip's
+    // columns of the last row of the K range (rows past it read zeros)
     auto set_strip_panel = [&](int k0) __attribute__((always_inline)) {
         const int rows = lK - k0;
         const int64_t es = int64_t(lkb + k0) * ldb + p.strip_n0;
-        const uint32_t ns = rows > 0 ? uint32_t((min(rows, BK) - 1) * ldb + 1) * 4u : 0u;
+        const uint32_t ns =
+            rows > 0 ? uint32_t((min(rows, BK) - 1) * ldb + p.strip_cols) * 4u : 0u;
         rss = make_rsrc32(p.B + es, ns);
     };
-    auto strip_load = [&](int stage) __attribute__((always_inline)) {
+    // sc loads, one per column; columns past strip_cols take the out-of-range offset (zeros)
+    auto strip_load = [&](int stage, auto sc_tag) __attribute__((always_inline)) {
+        constexpr int SC = decltype(sc_tag)::value;
         if (wave_u == 0) {
-            const uint32_t off = s_off;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rss, (lds_ptr)(strip_lds + (stage * KG + kg) * T::STRIP_STAGE), 4, off, 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < SC; ++j) {
+                const uint32_t off = j < p.strip_cols ? s_off + 4u * uint32_t(j) : kOob;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rss, (lds_ptr)(strip_lds + ((stage * KG + kg) * SCM + j) * T::STRIP_STAGE),
+                    4, off, 0, 0, 0);
+            }
         }
     };
     // The empty asm after the products keeps them at this step: left alone, the compiler
@@ -738,19 +782,21 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     };
     // Spread strip (strip_rows > 0): every tile of the row computes strip_rows rows of the
     // strip. Thread tid of a K-group owns chunk tid % CPR (four values of k) of row slot
-    // tid / CPR; per panel it reads that A chunk and the strip's four B values for it from
-    // LDS (two 16-byte reads) and adds their four products (four FMAs), in one step of the
-    // panel. Slots past strip_rows, or rows past the tile, read row 0 and are never stored.
+    // tid / CPR; per panel it reads that A chunk and each strip column's four B values for
+    // it from LDS (16-byte reads) and adds their four products per column, in one step of
+    // the panel. Slots past strip_rows, or rows past the tile, read row 0 and are never
+    // stored.
     int sp_aoff = 0, sp_boff = 0;
-    float sp_acc = 0.0f;
-    f32x4 sp_a, sp_b;
+    float sp_acc[SCM];
+    f32x4 sp_a, sp_b[SCM];
     auto set_spread_item = [&]() __attribute__((always_inline)) {
         const int q = tid / CPR, c = tid % CPR;
         const int row = (ln0 / BN) * p.strip_rows + q;
         const int lr = q < p.strip_rows && row < BM ? row : 0;
         sp_aoff = lr * BK + 4 * (c ^ a_swizzle<CPR>(lr));
         sp_boff = 4 * c;
-        sp_acc = 0.0f;
+#pragma unroll
+        for (int j = 0; j < SCM; ++j) sp_acc[j] = 0.0f;
     };
 
     // NEXT (next_tag 1 or 2): a next panel follows, whose step 0 this one reads after its
@@ -776,7 +822,8 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
         constexpr int SMODE = decltype(strip_tag)::value;
         constexpr bool STRIP = SMODE != 0;          // the panel loads strip values
         constexpr bool COLS = SMODE == 1;           // last tile column: the whole strip
-        constexpr bool SPREAD = SMODE == 2;         // a share of the strip's rows
+        constexpr bool SPREAD = SMODE >= 2;         // a share of the strip's rows
+        constexpr int SC = strip_mode_cols(SMODE);  // strip columns loaded per panel
         constexpr bool NEXT = decltype(next_tag)::value != 0;
         constexpr bool TAIL_NEXT = decltype(next_tag)::value == 2;
         constexpr bool LOADS = NSTG == 2 ? NEXT : decltype(next_tag)::value == 1;
@@ -791,7 +838,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
         float *Anext = smem + (NSTG == 2 ? cur_stage ^ 1 : cur_stage == 2 ? 0 : cur_stage + 1) * SSTRIDE;
         const int load_stage = NSTG == 2 ? cur_stage ^ 1 : cur_stage == 0 ? 2 : cur_stage - 1;
         float *Aload = NSTG == 2 ? Anext : smem + load_stage * SSTRIDE;
-        const float *Ss = strip_lds + (cur_stage * KG + kg) * T::STRIP_STAGE;
+        const float *Ss = strip_lds + (cur_stage * KG + kg) * SCM * T::STRIP_STAGE;
         static_for<0, NS>([&](auto tc) {
             constexpr int t = decltype(tc)::value;
             constexpr int kb = t >> 2, s = t & 3;
@@ -815,22 +862,28 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
             }
             // strip: the next panel's B values with the first loads; k-group kb's B values
             // read at its first step and its products added at its third
-            constexpr int n_sload = (STRIP && LOADS && t == 0) ? 1 : 0;
+            constexpr int n_sload = (STRIP && LOADS && t == 0) ? SC : 0;
             constexpr bool s_rd = COLS && s == 0;
             constexpr bool s_fma = COLS && s == 2;
-            constexpr int n_sprd = SPREAD && t == 0 ? 2 : 0;
-            if constexpr (n_sload > 0) strip_load(NSTG == 2 ? cur_stage ^ 1 : load_stage);
+            constexpr int n_sprd = SPREAD && t == 0 ? 1 + SC : 0;
+            if constexpr (n_sload > 0)
+                strip_load(NSTG == 2 ? cur_stage ^ 1 : load_stage, std::integral_constant<int, SC>{});
             if constexpr (s_fma) strip_fma(a[kb & 1]);
             if constexpr (s_rd)
                 sbv = *reinterpret_cast<const f32x4 *>(Ss + 4 * (S::H * kb + hi));
             if constexpr (SPREAD && t == 3) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sp_acc += sp_a[e] * sp_b[e];
-                asm volatile("" : "+v"(sp_acc));
+                for (int j = 0; j < SC; ++j) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sp_acc[j] += sp_a[e] * sp_b[j][e];
+                    asm volatile("" : "+v"(sp_acc[j]));
+                }
             }
             if constexpr (n_sprd > 0) {
                 sp_a = *reinterpret_cast<const f32x4 *>(As + sp_aoff);
-                sp_b = *reinterpret_cast<const f32x4 *>(Ss + sp_boff);
+#pragma unroll
+                for (int j = 0; j < SC; ++j)
+                    sp_b[j] = *reinterpret_cast<const f32x4 *>(Ss + j * T::STRIP_STAGE + sp_boff);
             }
             if constexpr (n_write > 0) {
 #pragma unroll
@@ -845,7 +898,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
                 // direct loads land in LDS when vmcnt counts them done
                 if constexpr (DL) {
                     if constexpr (NSTG == 3 && LOADS)
-                        wait_vmcnt_split<STRIP ? NL + 1 : NL, NL>(wave_u == 0);
+                        wait_vmcnt_split<NL + SC * STRIP, NL>(wave_u == 0);
                     else
                         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                     if constexpr (TAIL_NEXT) fix_k_tail(Anext);
@@ -1083,13 +1136,15 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
         auto run_item = [&](auto strip_tag) __attribute__((always_inline)) {
             constexpr int SMODE = decltype(strip_tag)::value;
             constexpr bool STRIP = SMODE != 0;
+            constexpr int SC = strip_mode_cols(SMODE);
+            using ScTag = std::integral_constant<int, SC>;
             auto setp = [&](int k0) __attribute__((always_inline)) {
                 set_panel(k0);
                 if constexpr (STRIP) set_strip_panel(k0);
             };
             set_item();
             if constexpr (STRIP) set_strip_item();
-            if constexpr (SMODE == 2) set_spread_item();
+            if constexpr (SMODE >= 2) set_spread_item();
             // rounds of panels of this group; a group whose last panel lies past the K range
             // loads only zeros for it
             auto group_rounds = [&]() { return ((lK + BK - 1) / BK + KG - 1) / KG; };
@@ -1097,7 +1152,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
             if constexpr (DL) {
 #pragma unroll
                 for (int l = 0; l < NL; ++l) load_direct(smem, l);
-                if constexpr (STRIP) strip_load(0);
+                if constexpr (STRIP) strip_load(0, ScTag{});
                 if constexpr (NSTG == 3) {
                     if (group_rounds() > 1) {
                         // the second panel's loads too, left in flight (the first panel is
@@ -1105,8 +1160,8 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
                         setp((KG + kg) * BK);
 #pragma unroll
                         for (int l = 0; l < NL; ++l) load_direct(smem + SSTRIDE, l);
-                        if constexpr (STRIP) strip_load(1);
-                        wait_vmcnt_split<STRIP ? NL + 1 : NL, NL>(wave_u == 0);
+                        if constexpr (STRIP) strip_load(1, ScTag{});
+                        wait_vmcnt_split<NL + SC, NL>(wave_u == 0);
                     } else {
                         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                         fix_k_tail(smem);
@@ -1205,18 +1260,25 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
             last_panel(SR{}, rounds, strip_tag);
             // the spread strip's partial sums go to LDS before the K-group sums, whose
             // barriers (KG > 1) then order them before the reads below
-            if constexpr (SMODE == 2) strip_red[kg * NT + tid] = sp_acc;
+            if constexpr (SMODE >= 2) {
+#pragma unroll
+                for (int j = 0; j < SC; ++j) strip_red[(j * KG + kg) * NT + tid] = sp_acc[j];
+            }
             finish();
-            if constexpr (SMODE == 2) {
-                // each row's chunk sums, K-group by K-group, in ascending order of both
+            if constexpr (SMODE >= 2) {
+                // each row's chunk sums, K-group by K-group, in ascending order of both, for
+                // each of the strip's columns
                 if constexpr (KG == 1) __syncthreads();
                 const int q = threadIdx.x;
                 const int row = (ln0 / BN) * p.strip_rows + q;
                 if (q < p.strip_rows && row < BM && lm0 + row < M) {
-                    float v = 0.0f;
-                    for (int g = 0; g < KG; ++g)
-                        for (int c = 0; c < CPR; ++c) v += strip_red[g * NT + q * CPR + c];
-                    p.C[int64_t(lm0 + row) * ldc + p.strip_n0] = v;
+                    for (int j = 0; j < SC && j < p.strip_cols; ++j) {
+                        float v = 0.0f;
+                        for (int g = 0; g < KG; ++g)
+                            for (int c = 0; c < CPR; ++c)
+                                v += strip_red[(j * KG + g) * NT + q * CPR + c];
+                        p.C[int64_t(lm0 + row) * ldc + p.strip_n0 + j] = v;
+                    }
                 }
             }
             if constexpr (SMODE == 1) {
@@ -1239,10 +1301,16 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
         };
         using NoStrip = std::integral_constant<int, 0>;
         if constexpr (CAN_STRIP) {
-            if (p.strip_cols > 0 && p.strip_rows > 0)
+            // the host gives strip_cols > 1 only with the spread form, and at most
+            // STRIP_COLS_MAX of them
+            if (p.strip_cols == 1 && p.strip_rows > 0)
                 run_item(std::integral_constant<int, 2>{});
-            else if (p.strip_cols > 0 && ln0 + BN == p.strip_n0)
+            else if (p.strip_cols == 1 && ln0 + BN == p.strip_n0)
                 run_item(std::integral_constant<int, 1>{});
+            else if (T::STRIP_COLS_MAX >= 2 && p.strip_cols == 2 && p.strip_rows > 0)
+                run_item(std::integral_constant<int, T::STRIP_COLS_MAX >= 2 ? 3 : 0>{});
+            else if (T::STRIP_COLS_MAX >= 4 && p.strip_cols > 2 && p.strip_rows > 0)
+                run_item(std::integral_constant<int, T::STRIP_COLS_MAX >= 4 ? 4 : 0>{});
             else
                 run_item(NoStrip{});
         } else {

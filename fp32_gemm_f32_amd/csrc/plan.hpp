@@ -42,9 +42,11 @@ struct Variant {
     // kernel): on other shapes it runs on their whole-tile part and the right and bottom
     // edges go to the plan, as launches of their own
     bool whole_tiles = false;
-    // a one-column remainder of N past the last whole tile column may be computed by the
-    // tiles of the last tile column, on the vector ALUs (the kernel's column strip)
+    // a remainder of N past the last whole tile column may be computed by the tiles beside
+    // the MFMAs, on the vector ALUs (the kernel's column strip): one column in either form,
+    // up to strip_cols_max columns spread over the tiles of each row
     bool strip = false;
+    int strip_cols_max = 1;
     // multiplier on the stream-K price (streamk_cost) of this variant's stream-K form; 0: the
     // form is not planned (it still runs when forced)
     double sk_price = kStreamkPrice;
@@ -68,18 +70,7 @@ inline bool offsets_fit(const Variant &v, const Operands &o)
 }
 
 // Most columns a strip may hold (the kernels' kStripCols).
-constexpr int kStripColsMax = 1;
-
-// Columns variant v could leave to the strip for o: N mod BN when that is 1 to
-// kStripColsMax and N holds at least one whole tile column, else 0 (the strip's B values
-// of a panel lie inside the panel's rows of B, so the offsets bound of offsets_fit covers
-// them). Whether the plan uses the strip is a choice priced by variant_cost (strip_cols).
-inline int strip_eligible(const Variant &v, const Operands &o)
-{
-    if (!v.strip || o.splits != 1 || o.N <= v.BN) return 0;
-    const int r = o.N % v.BN;
-    return r >= 1 && r <= kStripColsMax ? r : 0;
-}
+constexpr int kStripColsMax = 4;
 
 // Rows of the strip each tile computes when the strip's rows are spread over the tiles of
 // a row: ceil(BM / whole tile columns), if one K-group's threads hold a (row, 16-byte
@@ -92,6 +83,23 @@ inline int strip_spread_rows(const Variant &v, const Operands &o)
     const int rows = (v.BM + tn - 1) / tn;
     return rows * (v.BK / 4) <= 64 * v.wgm * v.wgn ? rows : 0;
 }
+
+// Columns variant v could leave to the strip for o: N mod BN when that is 1 to the
+// variant's strip_cols_max (past one column only where the spread form can take the
+// strip's rows) and N holds at least one whole tile column, else 0 (the strip's B values
+// of a panel lie inside the panel's rows of B, so the offsets bound of offsets_fit covers
+// them). Whether the plan uses the strip is a choice priced by variant_cost (strip_cols).
+inline int strip_eligible(const Variant &v, const Operands &o)
+{
+    if (!v.strip || o.splits != 1 || o.N <= v.BN) return 0;
+    const int r = o.N % v.BN;
+    if (r < 1 || r > v.strip_cols_max || r > kStripColsMax) return 0;
+    return r == 1 || strip_spread_rows(v, o) > 0 ? r : 0;
+}
+
+// Strip columns the kernel loads and multiplies per panel for a strip of r columns: one,
+// two or four (three take four, the last one zero).
+inline int strip_load_cols(int r) { return r <= 1 ? 1 : r == 2 ? 2 : 4; }
 
 // A whole-tile variant (the persistent kernel) also needs rows of C that start on 32-byte
 // boundaries (ldc a multiple of 8): it stores C as 4-byte lane stores from the
@@ -136,7 +144,10 @@ inline double strip_spread_share(const Variant &v, const Operands &o, int cus)
 {
     const int64_t tm = (int64_t(o.M) + v.BM - 1) / v.BM;
     const int64_t per_cu = (tm * (o.N / v.BN) + cus - 1) / cus;
-    const double share = kStripSpreadShare * 64.0 / v.BK;
+    // each column adds a 16-byte read and four FMAs per thread and panel to the A chunk's
+    // read (one column: two reads)
+    const int sc = strip_load_cols(strip_eligible(v, o));
+    const double share = kStripSpreadShare * 64.0 / v.BK * (1.0 + sc) / 2.0;
     return per_cu >= v.wg_per_cu ? share / v.wg_per_cu : share;
 }
 
@@ -164,10 +175,12 @@ inline double strip_column_share(const Variant &v, const Operands &o, int cus)
 }
 
 // Rows per tile of the strip's form for o: strip_spread_rows where spreading the rows is
-// priced below the last-column form, else 0 (the last tile column computes them).
+// priced below the last-column form or the strip holds more than one column, else 0 (the
+// last tile column computes them).
 inline int strip_form_rows(const Variant &v, const Operands &o, int cus)
 {
     const int rows = strip_spread_rows(v, o);
+    if (rows > 0 && strip_eligible(v, o) > 1) return rows;
     return rows > 0 && strip_spread_share(v, o, cus) < strip_column_share(v, o, cus) ? rows : 0;
 }
 

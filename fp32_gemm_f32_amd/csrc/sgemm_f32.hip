@@ -91,7 +91,9 @@ constexpr VariantEntry entry(const char *name, int wg_per_cu, double rate, doubl
         &k_sgemm_mfma<BM, BN, BK, WGM, WGN, KACC, KG, DL, false, MB, NSTG>, sk, fix,
         64 * WGM * WGN * KG, MB, KG, "mfma"};
     // the kernel's column strip (kernel_mfma.hpp): direct loads and room in LDS
-    e.v.strip = DL && MfmaTile<BM, BN, BK, WGM, WGN, KACC, KG, MB, NSTG>::STRIP_OK;
+    using Tile = MfmaTile<BM, BN, BK, WGM, WGN, KACC, KG, MB, NSTG>;
+    e.v.strip = DL && Tile::STRIP_OK;
+    e.v.strip_cols_max = e.v.strip ? Tile::STRIP_COLS_MAX : 0;
     e.v.sk_price = sk_price;
     e.v.latency = latency;
     e.stages = NSTG;
@@ -875,13 +877,14 @@ extern "C" int sgemm_f32_variant_info(int variant, char *buf, int buflen)
                            "\"direct_loads\": %s, \"planned\": %s, \"streamk\": %s, "
                            "\"rate\": %.3f, \"overhead\": %.1f, \"solo\": %.3f, \"latency_us\": %.2f, "
                            "\"kernel\": \"%s\", \"splitk\": %s, \"persistent\": %s, "
-                           "\"whole_tiles\": %s, \"strip\": %s, \"lds_stages\": %d}",
+                           "\"whole_tiles\": %s, \"strip\": %s, \"strip_cols_max\": %d, "
+                           "\"lds_stages\": %d}",
                            variant, v.name, v.BM, v.BN, v.BK, v.wgm, v.wgn, e.kg, e.threads, e.mb,
                            e.mb, e.mb == 32 ? 2 : 4, v.wg_per_cu, v.direct ? "true" : "false",
                            v.planned ? "true" : "false", e.kern_sk ? "true" : "false", v.rate,
                            v.overhead, v.solo, v.latency, e.kernel, v.splitk ? "true" : "false",
                            e.persistent ? "true" : "false", v.whole_tiles ? "true" : "false",
-                           v.strip ? "true" : "false", e.stages);
+                           v.strip ? "true" : "false", v.strip ? v.strip_cols_max : 0, e.stages);
     if (n < 0 || n >= buflen) return SGEMM_EINVAL_ARG;
     return SGEMM_OK;
 }

@@ -395,6 +395,41 @@ def test_workload_streamk_plans():
         assert not d["streamk"], d
 
 
+def test_variant_describe_wide_strips():
+    """Two to four strip columns: every strip-capable variant takes up to its
+    strip_cols_max of them, always in the spread form (the last-column form computes one
+    column only), where that form's rows fit a K-group; wider remainders, and remainders
+    past the variant's width, mask a last tile column instead. The plan gives the
+    1024-class products with N = 1026..1028 a spread strip."""
+    cus = 256
+    widths = set()
+    for v in range(len(g.variant_names())):
+        info = g.sgemm_f32_variant_info(v)
+        if not info["strip"]:
+            assert info["strip_cols_max"] == 0, info
+            continue
+        bm, bn, bk = info["BM"], info["BN"], info["BK"]
+        nt = 64 * info["waves"][0] * info["waves"][1]
+        scm = info["strip_cols_max"]
+        assert scm in (1, 2, 4), info
+        widths.add(scm)
+        rows = -(-bm // 16)
+        for sc in range(2, 6):
+            M, N, K = 16 * bm - 3, 16 * bn + sc, 33
+            d = g.sgemm_f32_variant_describe(v, M, N, K, K + 1, N + 3, N + 2, num_cus=cus)
+            if sc <= scm and rows * bk // 4 <= nt:
+                assert d["strip_cols"] == sc and d["strip_rows"] == rows, (info["name"], sc, d)
+                assert d["tiles"][1] == 16, d
+            else:
+                assert d["strip_cols"] == 0 and d["tiles"][1] == 17, (info["name"], sc, d)
+    assert widths >= {2, 4}, widths
+    for (M, N, K) in [(1024, 1026, 1024), (1024, 1027, 1024), (1024, 1028, 1024),
+                      (1023, 1027, 1027)]:
+        d = g.sgemm_f32_plan_describe(M, N, K, num_cus=cus)
+        assert d["strip_cols"] == N % d["BN"] and d["strip_rows"] > 0, d
+        assert d["tiles"][1] == N // d["BN"], d
+
+
 def test_variant_describe_strip_forms():
     """A forced variant's plan, as sgemm_f32_variant runs it: the column strip spread over
     the tiles of each row where one K-group's threads cover a tile's share of the rows,

@@ -1,10 +1,11 @@
-"""The column strip through the C ABI: when N leaves one column past the last whole tile
-column, the tiles also compute that column, on the vector ALUs between their MFMAs: spread
-over the tiles of each row (each tile a few of the row's strip rows, from its A panels in
-LDS), or, when the tile columns are too few for that, by the last tile column from the A
-operands it reads for the MFMAs. Checked against the oracle (exact on small integers,
-within the normalised tolerance on floats) with NaN-poisoned row padding and guard bands
-around C, for every strip-capable variant forced (both forms), for the automatic plan, and
+"""The column strip through the C ABI: when N leaves one to four columns past the last whole
+tile column, the tiles also compute those columns, on the vector ALUs between their MFMAs:
+spread over the tiles of each row (each tile a few of the row's strip rows, from its A
+panels in LDS; up to the variant's strip_cols_max columns), or, for one column when the
+tile columns are too few for that, by the last tile column from the A operands it reads for
+the MFMAs. Checked against the oracle (exact on small integers, within the normalised
+tolerance on floats) with NaN-poisoned row padding and guard bands around C, for every
+strip-capable variant forced (both forms, every strip width), for the automatic plan, and
 for run-to-run determinism."""
 import numpy as np
 import pytest
@@ -119,6 +120,57 @@ def test_strip_forced_both_forms(gpu):
             run_kernel(f"v{v}", M, N, K, dA, lda, dB, ldb, c)
             gpu.cuda.synchronize()
             _check(A, B, c.result(), "int", (name, M, N, K, form))
+
+
+def test_strip_forced_wide(gpu):
+    """Every strip-capable variant forced on shapes whose N leaves two, three or four
+    columns (up to the variant's strip_cols_max): the spread form takes them all, as
+    variant_describe reports; exact on integers with padded leading dimensions and guard
+    bands, K below, at and past the panel depth."""
+    cus = gpu.cuda.get_device_properties(0).multi_processor_count
+    for v in strip_variants():
+        info = g.sgemm_f32_variant_info(v)
+        name, bm, bn = info["name"], info["BM"], info["BN"]
+        for sc in range(2, info["strip_cols_max"] + 1):
+            for (M, N, K) in [((cus // 16) * bm - 3, 16 * bn + sc, 33),
+                              ((cus // 17) * bm, 17 * bn + sc, 72 + sc)]:
+                lda, ldb, ldc = K + 1, N + 3, N + 2
+                d = g.sgemm_f32_variant_describe(v, M, N, K, lda, ldb, ldc)
+                assert d["strip_cols"] == sc and d["strip_rows"] > 0, (name, M, N, K, d)
+                rng = np.random.default_rng(M + 3 * N + 7 * K + sc)
+                A = wl.draw(rng, (M, K), "int")
+                B = wl.draw(rng, (K, N), "int")
+                _, dA, _ = device_matrix(A, lda)
+                _, dB, _ = device_matrix(B, ldb)
+                c = GuardedC(M, N, ldc)
+                print(f"[strip] {name} {M}x{N}x{K} {sc} columns rows={d['strip_rows']}",
+                      flush=True)
+                run_kernel(f"v{v}", M, N, K, dA, lda, dB, ldb, c)
+                gpu.cuda.synchronize()
+                _check(A, B, c.result(), "int", (name, M, N, K, sc))
+
+
+@pytest.mark.parametrize("M,N,K", [(1024, 1026, 1024), (1024, 1027, 1024), (1023, 1028, 1027),
+                                   (2048, 2050, 2048), (512, 514, 4096)])
+def test_plan_wide_strip(gpu, M, N, K):
+    """The automatic plan where N leaves two to four columns past the tile columns: it puts
+    them in a spread strip, and the result matches the oracle (floats, normalised
+    tolerance; sampled rows at the larger size)."""
+    plan = g.sgemm_f32_plan_describe(M, N, K)
+    print(f"[strip] plan {M}x{N}x{K} {plan}", flush=True)
+    assert plan["strip_cols"] == N % plan["BN"] and plan["strip_rows"] > 0, plan
+    rng = np.random.default_rng(M * 31 + N * 7 + K)
+    A = wl.draw(rng, (M, K), "uniform")
+    B = wl.draw(rng, (K, N), "uniform")
+    _, dA, lda = device_matrix(A)
+    _, dB, ldb = device_matrix(B)
+    c = GuardedC(M, N, N + 1)
+    run_kernel("auto", M, N, K, dA, lda, dB, ldb, c)
+    gpu.cuda.synchronize()
+    C = c.result()
+    rows = None if M * N * K <= 2 ** 31 else np.unique(np.r_[0:8, M - 8:M, 1000:1010])
+    rep = oracle.check(A, B, C, rows=rows) if rows is not None else oracle.check(A, B, C)
+    assert rep["n_nonfinite"] == 0 and rep["max_err"] <= TOL, rep
 
 
 @pytest.mark.parametrize("kind", ["int", "float"])
