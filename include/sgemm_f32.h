@@ -57,9 +57,9 @@ typedef enum {
  * The hot path: the LDS-tiled, register-tiled matrix-core kernel ("SGEMM: 2D Register
  * Tiling Visualizer", "Why 2D Register Tiling Dominates", carried onto the FP32 MFMA
  * instructions), with tiles zero-filled past the edges of ragged shapes. The tile shape
- * is chosen per (M, N, K) and compute-unit count; when N leaves one column past the last
- * whole tile column, the tiles of that last column may also compute it, on the vector ALUs
- * beside their MFMAs, instead of a nearly empty column of tiles. Any 4-byte aligned
+ * is chosen per (M, N, K) and compute-unit count; when N leaves one to four columns past
+ * the last whole tile column, the tiles may also compute them, on the vector ALUs beside
+ * their MFMAs, instead of a nearly empty column of tiles. Any 4-byte aligned
  * pointers and any leading dimensions work. Leading dimensions so large that 256 rows of A or C (or 32
  * rows of B) exceed 2^31 bytes return SGEMM_ETOO_LARGE.
  */
@@ -269,12 +269,14 @@ const char *sgemm_f32_variant_name(int variant);
  * bytes including the NUL): name, tile (BM, BN, BK), waves along M and N, K-groups,
  * threads, the MFMA instruction shape ("32x32x2" or "16x16x4"), resident workgroups per
  * CU, direct loads, whether the automatic plan may pick it, whether it has a stream-K
- * form, the plan's cost-model parameters (rate, overhead, solo) for it, the kernel family
+ * form, the plan's cost-model parameters (rate, overhead, solo, and the launch's latency in
+ * microseconds, "latency_us") for it, the kernel family
  * ("mfma": the LDS-double-buffered template; "regpanel": the one-wave-per-SIMD kernel;
  * "persist": the persistent kernel), whether split-K may use it, whether it runs one
  * workgroup per CU over the tiles ("persistent"), whether it only takes whole tiles
- * ("whole_tiles"), whether the tiles of its last tile column can also compute one
- * column of N past it, on the vector ALUs ("strip"), and the LDS stages per K-group of the
+ * ("whole_tiles"), whether its tiles can also compute columns of N past the last whole
+ * tile column, on the vector ALUs ("strip"), and how many at most ("strip_cols_max": 1, 2
+ * or 4; more than one only spread over the tiles of each row), the LDS stages per K-group of the
  * template kernel ("lds_stages": 2, or 3 where each panel's loads are issued two panels
  * ahead; "Shared Memory Tiling", "What tiling does not fix"). Host-only, no GPU needed. Returns SGEMM_OK, or
  * SGEMM_EINVAL_ARG for a bad index or a buffer too small.
@@ -288,8 +290,8 @@ const char *sgemm_f32_status_string(int status);
  * Writes a one-line JSON description of the plan sgemm_f32 would run for these
  * arguments into buf (at most buflen bytes including the NUL): variant, tile shape,
  * waves, grid, workgroups resident per CU, whether panels load straight into LDS, the
- * operand bytes the tiles request, and the column strip: "strip_cols" (the column past
- * the last whole tile column that the tiles also compute, 0 or 1), "strip_rows" (the
+ * operand bytes the tiles request, and the column strip: "strip_cols" (the columns past
+ * the last whole tile column that the tiles also compute, 0 to 4), "strip_rows" (the
  * strip rows each tile of a row computes when they are spread over the row's tiles; 0
  * when the last tile column computes them all), "strip_tiles" (how many tiles compute
  * some) and "edge_launches" (0-2: the right and bottom edges a whole-tile variant leaves to
