@@ -126,6 +126,12 @@ struct GemmArgs {
     int strip_n0;
     int strip_cols;
     int strip_rows;
+    // Row strip (plain kernels only; never with a column strip): when rstrip > 0, the tiles
+    // cover rows [0, M - rstrip) (tiles_m whole tile rows), and the rstrip (at most
+    // STRIP_COLS_MAX) rows past them are computed on the vector ALUs by the tiles of each
+    // tile column: tile row t computes columns [t c, (t + 1) c) of its tile column's share
+    // of them, c = strip_rows.
+    int rstrip;
 };
 
 // Most columns a strip may hold: a remainder of N past the last whole tile column of up to
@@ -133,11 +139,12 @@ struct GemmArgs {
 // spread form computes it).
 constexpr int kStripCols = 4;
 
-// Strip columns loaded per panel by the kernel's strip modes: 1 the last tile column's
-// (one column), 2, 3 and 4 the spread form's one, two and four columns; 0 none.
+// Strip columns (or rows) loaded per panel by the kernel's strip modes: 1 the last tile
+// column's (one column); 2, 3 and 4 the spread column strip's one, two and four columns;
+// 5, 6 and 7 the row strip's one, two and four rows; 0 none.
 __host__ __device__ constexpr int strip_mode_cols(int smode)
 {
-    return smode == 3 ? 2 : smode == 4 ? 4 : smode >= 1 ? 1 : 0;
+    return smode == 3 || smode == 6 ? 2 : smode == 4 || smode == 7 ? 4 : smode >= 1 ? 1 : 0;
 }
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const float *base, int64_t bytes)
@@ -434,13 +441,18 @@ struct MfmaTile {
 // and the grid has one workgroup per item. With SK the grid is sk.tiles_dp workgroups of
 // one tile each followed by sk.G stream-K workgroups, each walking the segments of its
 // range of K-panel units (streamk.hpp): whole tiles go to C, partial ones to its two
-// workspace slots.
+// workspace slots. FORM (a strip mode of strip_mode_cols) selects the strip the kernel
+// computes: each strip form is a kernel of its own, so that no form's registers or code
+// weigh on the others (the plain tiles' kernel, FORM 0, holds none).
 template <int BM, int BN, int BK, int WGM, int WGN, int KACC, int KG, bool DL, bool SK = false,
-          int MB = 32, int NSTG = 2>
+          int MB = 32, int NSTG = 2, int FORM = 0>
 __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
 {
     static_assert(NSTG == 2 || (NSTG == 3 && DL), "two LDS stages, or three with direct loads");
     using T = MfmaTile<BM, BN, BK, WGM, WGN, KACC, KG, MB, NSTG>;
+    static_assert(FORM == 0 || (!SK && DL && T::STRIP_OK &&
+                                strip_mode_cols(FORM) <= T::STRIP_COLS_MAX),
+                  "a strip form the tile can hold");
     using S = MfmaShape<MB>;
     typedef typename S::acc_t acc_t;
     constexpr int NT = T::kGroupThreads, WM = T::WM, WN = T::WN, RB = T::RB, CI = T::CI,
@@ -735,7 +747,6 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
     // reads and 4 RB FMAs per k-group in the last column, so the plan uses it wherever a
     // K-group's threads cover a tile's share of the rows and few rounds of tiles make
     // that cheaper than the last-column form (strip_form_rows).
-    constexpr bool CAN_STRIP = !SK && DL && T::STRIP_OK;
     constexpr int SCM = T::STRIP_COLS_MAX > 0 ? T::STRIP_COLS_MAX : 1;   // columns per stage
     float *const strip_lds = lds_all + T::STAGES;
     float *const strip_red = strip_lds + NSTG * KG * SCM * T::STRIP_STAGE;
@@ -770,6 +781,34 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
             }
         }
     };
+    // Row strip: the strip rows' A values of a panel go to the same LDS columns (row j of
+    // stage s of group kg at strip_lds + ((s KG + kg) SCM + j) STRIP_STAGE, value k at + k),
+    // one load per row by the group's first wave, lane k loading value k; values past the
+    // K range and rows past rstrip read zeros. The resource spans the strip rows from the
+    // panel's first k; lanes past the K range are masked by offset, since the range also
+    // covers the next row's start.
+    int r_kvalid = 0;
+    auto set_rstrip_panel = [&](int k0) __attribute__((always_inline)) {
+        r_kvalid = min(lK - k0, BK);
+        const int64_t ea = int64_t(M - p.rstrip) * lda + lkb + k0;
+        const uint32_t na =
+            r_kvalid > 0 ? uint32_t((p.rstrip - 1) * lda + r_kvalid) * 4u : 0u;
+        rss = make_rsrc32(p.A + ea, na);
+    };
+    auto rstrip_load = [&](int stage, auto sc_tag) __attribute__((always_inline)) {
+        constexpr int SC = decltype(sc_tag)::value;
+        if (wave_u == 0) {
+#pragma unroll
+            for (int j = 0; j < SC; ++j) {
+                const uint32_t off = j < p.rstrip && lane < r_kvalid
+                                         ? (uint32_t(j) * uint32_t(lda) + uint32_t(lane)) * 4u
+                                         : kOob;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rss, (lds_ptr)(strip_lds + ((stage * KG + kg) * SCM + j) * T::STRIP_STAGE),
+                    4, off, 0, 0, 0);
+            }
+        }
+    };
     // The empty asm after the products keeps them at this step: left alone, the compiler
     // gathers the products of a whole panel at its end, with all their operands live.
     auto strip_fma = [&](const f32x4 (&av)[RB]) __attribute__((always_inline)) {
@@ -798,6 +837,21 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
 #pragma unroll
         for (int j = 0; j < SCM; ++j) sp_acc[j] = 0.0f;
     };
+    // Row strip, mirrored: thread tid of a K-group owns chunk c = tid % CPR (four values of
+    // k) of column slot tid / CPR of the tile's share; per panel it reads that column's four
+    // B values from the B panel in LDS (four 4-byte reads, BN floats apart, the same chunk
+    // swizzle for all four) and each strip row's four A values (16-byte reads), and adds
+    // four products per row. Slots past the share, or columns past the tile, read column 0
+    // and are never stored.
+    auto set_rspread_item = [&]() __attribute__((always_inline)) {
+        const int q = tid / CPR, c = tid % CPR;
+        const int col = (lm0 / BM) * p.strip_rows + q;
+        const int lc = q < p.strip_rows && col < BN ? col : 0;
+        sp_aoff = 4 * c * BN + 4 * ((lc >> 2) ^ b_swizzle<MB>(4 * c)) + (lc & 3);
+        sp_boff = 4 * c;
+#pragma unroll
+        for (int j = 0; j < SCM; ++j) sp_acc[j] = 0.0f;
+    };
 
     // NEXT (next_tag 1 or 2): a next panel follows, whose step 0 this one reads after its
     // barrier; 2 (NextTail): that next panel is its group's last, which may hold the end of
@@ -822,8 +876,9 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
         constexpr int SMODE = decltype(strip_tag)::value;
         constexpr bool STRIP = SMODE != 0;          // the panel loads strip values
         constexpr bool COLS = SMODE == 1;           // last tile column: the whole strip
-        constexpr bool SPREAD = SMODE >= 2;         // a share of the strip's rows
-        constexpr int SC = strip_mode_cols(SMODE);  // strip columns loaded per panel
+        constexpr bool SPREAD = SMODE >= 2 && SMODE <= 4;   // a share of the strip's rows
+        constexpr bool ROWS = SMODE >= 5;           // row strip: a share of its columns
+        constexpr int SC = strip_mode_cols(SMODE);  // strip columns (rows) loaded per panel
         constexpr bool NEXT = decltype(next_tag)::value != 0;
         constexpr bool TAIL_NEXT = decltype(next_tag)::value == 2;
         constexpr bool LOADS = NSTG == 2 ? NEXT : decltype(next_tag)::value == 1;
@@ -865,13 +920,19 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
             constexpr int n_sload = (STRIP && LOADS && t == 0) ? SC : 0;
             constexpr bool s_rd = COLS && s == 0;
             constexpr bool s_fma = COLS && s == 2;
-            constexpr int n_sprd = SPREAD && t == 0 ? 1 + SC : 0;
-            if constexpr (n_sload > 0)
-                strip_load(NSTG == 2 ? cur_stage ^ 1 : load_stage, std::integral_constant<int, SC>{});
+            constexpr int n_sprd = SPREAD && t == 0 ? 1 + SC : ROWS && t == 0 ? 4 + SC : 0;
+            if constexpr (n_sload > 0) {
+                if constexpr (ROWS)
+                    rstrip_load(NSTG == 2 ? cur_stage ^ 1 : load_stage,
+                                std::integral_constant<int, SC>{});
+                else
+                    strip_load(NSTG == 2 ? cur_stage ^ 1 : load_stage,
+                               std::integral_constant<int, SC>{});
+            }
             if constexpr (s_fma) strip_fma(a[kb & 1]);
             if constexpr (s_rd)
                 sbv = *reinterpret_cast<const f32x4 *>(Ss + 4 * (S::H * kb + hi));
-            if constexpr (SPREAD && t == 3) {
+            if constexpr ((SPREAD || ROWS) && t == 3) {
 #pragma unroll
                 for (int j = 0; j < SC; ++j) {
 #pragma unroll
@@ -880,7 +941,13 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
                 }
             }
             if constexpr (n_sprd > 0) {
-                sp_a = *reinterpret_cast<const f32x4 *>(As + sp_aoff);
+                if constexpr (ROWS) {
+                    // sp_a: the column's four B values; sp_b[j]: strip row j's four A values
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sp_a[e] = Bs[sp_aoff + e * BN];
+                } else {
+                    sp_a = *reinterpret_cast<const f32x4 *>(As + sp_aoff);
+                }
 #pragma unroll
                 for (int j = 0; j < SC; ++j)
                     sp_b[j] = *reinterpret_cast<const f32x4 *>(Ss + j * T::STRIP_STAGE + sp_boff);
@@ -1138,13 +1205,21 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
             constexpr bool STRIP = SMODE != 0;
             constexpr int SC = strip_mode_cols(SMODE);
             using ScTag = std::integral_constant<int, SC>;
+            constexpr bool ROWS = SMODE >= 5;
             auto setp = [&](int k0) __attribute__((always_inline)) {
                 set_panel(k0);
-                if constexpr (STRIP) set_strip_panel(k0);
+                if constexpr (ROWS) set_rstrip_panel(k0);
+                else if constexpr (STRIP) set_strip_panel(k0);
+            };
+            // the first loads of a panel: the strip's with the operands'
+            auto sload = [&](int stage) __attribute__((always_inline)) {
+                if constexpr (ROWS) rstrip_load(stage, ScTag{});
+                else if constexpr (STRIP) strip_load(stage, ScTag{});
             };
             set_item();
-            if constexpr (STRIP) set_strip_item();
-            if constexpr (SMODE >= 2) set_spread_item();
+            if constexpr (STRIP && !ROWS) set_strip_item();
+            if constexpr (SMODE >= 2 && !ROWS) set_spread_item();
+            if constexpr (ROWS) set_rspread_item();
             // rounds of panels of this group; a group whose last panel lies past the K range
             // loads only zeros for it
             auto group_rounds = [&]() { return ((lK + BK - 1) / BK + KG - 1) / KG; };
@@ -1152,7 +1227,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
             if constexpr (DL) {
 #pragma unroll
                 for (int l = 0; l < NL; ++l) load_direct(smem, l);
-                if constexpr (STRIP) strip_load(0, ScTag{});
+                sload(0);
                 if constexpr (NSTG == 3) {
                     if (group_rounds() > 1) {
                         // the second panel's loads too, left in flight (the first panel is
@@ -1160,7 +1235,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
                         setp((KG + kg) * BK);
 #pragma unroll
                         for (int l = 0; l < NL; ++l) load_direct(smem + SSTRIDE, l);
-                        if constexpr (STRIP) strip_load(1, ScTag{});
+                        sload(1);
                         wait_vmcnt_split<NL + SC, NL>(wave_u == 0);
                     } else {
                         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1265,7 +1340,23 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
                 for (int j = 0; j < SC; ++j) strip_red[(j * KG + kg) * NT + tid] = sp_acc[j];
             }
             finish();
-            if constexpr (SMODE >= 2) {
+            if constexpr (ROWS) {
+                // each column's chunk sums, K-group by K-group, in ascending order of both,
+                // for each of the strip's rows
+                if constexpr (KG == 1) __syncthreads();
+                const int q = threadIdx.x;
+                const int col = (lm0 / BM) * p.strip_rows + q;
+                if (q < p.strip_rows && col < BN && ln0 + col < N) {
+                    for (int j = 0; j < SC && j < p.rstrip; ++j) {
+                        float v = 0.0f;
+                        for (int g = 0; g < KG; ++g)
+                            for (int c = 0; c < CPR; ++c)
+                                v += strip_red[(j * KG + g) * NT + q * CPR + c];
+                        p.C[int64_t(M - p.rstrip + j) * ldc + ln0 + col] = v;
+                    }
+                }
+            }
+            if constexpr (SMODE >= 2 && !ROWS) {
                 // each row's chunk sums, K-group by K-group, in ascending order of both, for
                 // each of the strip's columns
                 if constexpr (KG == 1) __syncthreads();
@@ -1300,21 +1391,15 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void k_sgemm_mfma(GemmArgs p)
             }
         };
         using NoStrip = std::integral_constant<int, 0>;
-        if constexpr (CAN_STRIP) {
-            // the host gives strip_cols > 1 only with the spread form, and at most
-            // STRIP_COLS_MAX of them
-            if (p.strip_cols == 1 && p.strip_rows > 0)
-                run_item(std::integral_constant<int, 2>{});
-            else if (p.strip_cols == 1 && ln0 + BN == p.strip_n0)
+        // the host launches the kernel of the plan's strip form (strip_kernel_mode); in the
+        // last-column form only the last tile column computes the strip
+        if constexpr (FORM == 1) {
+            if (ln0 + BN == p.strip_n0)
                 run_item(std::integral_constant<int, 1>{});
-            else if (T::STRIP_COLS_MAX >= 2 && p.strip_cols == 2 && p.strip_rows > 0)
-                run_item(std::integral_constant<int, T::STRIP_COLS_MAX >= 2 ? 3 : 0>{});
-            else if (T::STRIP_COLS_MAX >= 4 && p.strip_cols > 2 && p.strip_rows > 0)
-                run_item(std::integral_constant<int, T::STRIP_COLS_MAX >= 4 ? 4 : 0>{});
             else
                 run_item(NoStrip{});
         } else {
-            run_item(NoStrip{});
+            run_item(std::integral_constant<int, FORM>{});
         }
         {   // every K-group stores its own units of the tile
             if (!to_workspace) {

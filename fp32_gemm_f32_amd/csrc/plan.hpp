@@ -151,10 +151,12 @@ inline double strip_spread_share(const Variant &v, const Operands &o, int cus)
     return per_cu >= v.wg_per_cu ? share / v.wg_per_cu : share;
 }
 
-// Busiest-CU estimate for variant v with tn tile columns, in multiply-adds at rate 1.
-inline double tiles_cost(const Variant &v, const Operands &o, int cus, int64_t tn)
+// Busiest-CU estimate for variant v with tn tile columns (and tm tile rows; by default
+// every row of M in a tile), in multiply-adds at rate 1.
+inline double tiles_cost(const Variant &v, const Operands &o, int cus, int64_t tn,
+                         int64_t tm = -1)
 {
-    const int64_t tm = (int64_t(o.M) + v.BM - 1) / v.BM;
+    if (tm < 0) tm = (int64_t(o.M) + v.BM - 1) / v.BM;
     // the busiest CU runs ceil(tiles / CUs) tiles; each is BM*BN*K multiply-adds at the
     // variant's measured relative rate plus the variant's per-tile overhead
     int64_t per_cu = (tm * tn * o.splits + cus - 1) / cus;
@@ -193,18 +195,71 @@ inline double strip_cost(const Variant &v, const Operands &o, int cus)
     return tiles_cost(v, o, cus, o.N / v.BN) * (1.0 + share);
 }
 
+// Row strip, the column strip's spread form mirrored: the rows of M past the last whole
+// tile row computed by the tiles of each tile column, tile row t taking columns
+// [t c, (t + 1) c) of its tile column's share, c = ceil(BN / whole tile rows), if one
+// K-group's threads hold a (column, 16-byte chunk of a panel row) pair each; else 0.
+inline int rstrip_share_cols(const Variant &v, const Operands &o)
+{
+    const int tm = o.M / v.BM;
+    if (tm <= 0) return 0;
+    const int cols = (v.BN + tm - 1) / tm;
+    return cols * (v.BK / 4) <= 64 * v.wgm * v.wgn ? cols : 0;
+}
+
+// Rows variant v could leave to a row strip for o: M mod BM when that is 1 to the
+// variant's strip_cols_max and M holds at least one whole tile row, else 0.
+inline int rstrip_eligible(const Variant &v, const Operands &o)
+{
+    if (!v.strip || o.splits != 1 || o.M <= v.BM) return 0;
+    const int r = o.M % v.BM;
+    if (r < 1 || r > v.strip_cols_max || r > kStripColsMax) return 0;
+    return rstrip_share_cols(v, o) > 0 ? r : 0;
+}
+
+// The row strip's share of a tile's time. Per panel every thread reads four B values of
+// one column, BN floats apart in LDS: with 64-float rows the lanes of one column hit one
+// bank, so the reads serialise over the panel's BK / 4 chunks, and the share grows with BK
+// rather than shrinking (measured at steady state against the same tiles without the rows:
+// 1025 x 1024 x 1024, 64 x 64 x 64 tiles 11.8 %, 64 x 64 x 32 tiles 5.7 %; two rows 14.5 and
+// 7.7 %, four 19.1 and 15.3 %). Halved where another workgroup's MFMAs cover it.
+constexpr double kRowStripShare = 0.10;
+inline double rstrip_cost(const Variant &v, const Operands &o, int cus)
+{
+    const int64_t tm = o.M / v.BM, tn = (int64_t(o.N) + v.BN - 1) / v.BN;
+    const int64_t per_cu = (tm * tn + cus - 1) / cus;
+    const int sc = strip_load_cols(rstrip_eligible(v, o));
+    double share = kRowStripShare * v.BK / 64.0 * (3.0 + sc) / 4.0;
+    if (per_cu >= v.wg_per_cu) share /= v.wg_per_cu;
+    return tiles_cost(v, o, cus, tn, tm) * (1.0 + share);
+}
+
+// Rows variant v leaves to a row strip for o: those of rstrip_eligible when the strip is
+// priced below a last row of masked tiles and below a column strip, else 0.
+inline int rstrip_rows(const Variant &v, const Operands &o, int cus)
+{
+    const int r = rstrip_eligible(v, o);
+    if (r == 0) return 0;
+    const double c = rstrip_cost(v, o, cus);
+    if (!(c < tiles_cost(v, o, cus, (int64_t(o.N) + v.BN - 1) / v.BN))) return 0;
+    if (strip_eligible(v, o) > 0 && !(c < strip_cost(v, o, cus))) return 0;
+    return r;
+}
+
 // Columns variant v leaves to the strip for o: those of strip_eligible when the strip is
-// priced below a last column of masked tiles, else 0.
+// priced below a last column of masked tiles and the plan takes no row strip, else 0.
 inline int strip_cols(const Variant &v, const Operands &o, int cus)
 {
     const int r = strip_eligible(v, o);
     if (r == 0) return 0;
     const int64_t tn_all = (int64_t(o.N) + v.BN - 1) / v.BN;
-    return strip_cost(v, o, cus) < tiles_cost(v, o, cus, tn_all) ? r : 0;
+    if (!(strip_cost(v, o, cus) < tiles_cost(v, o, cus, tn_all))) return 0;
+    return rstrip_rows(v, o, cus) > 0 ? 0 : r;
 }
 
 inline double variant_cost(const Variant &v, const Operands &o, int cus)
 {
+    if (rstrip_rows(v, o, cus) > 0) return rstrip_cost(v, o, cus);
     if (strip_cols(v, o, cus) > 0) return strip_cost(v, o, cus);
     return tiles_cost(v, o, cus, (int64_t(o.N) + v.BN - 1) / v.BN);
 }

@@ -72,7 +72,32 @@ struct VariantEntry {
     bool persistent = false;       // one workgroup per CU walks the tiles (kernel_persist.hpp)
     MfmaKernel kern_ktail = nullptr;   // its form for a K that is not a multiple of BK
     int stages = 2;                    // LDS stages per K-group (the template kernel)
+    // the plain kernel's strip forms, indexed by strip_kernel_mode (1-7; null where the
+    // tile cannot hold the form)
+    MfmaKernel kern_strip[8] = {};
 };
+
+// The strip form a plain launch computes (k_sgemm_mfma's SMODE): 0 none; 1 one column in
+// the last tile column; 2-4 one, two or four (three) columns spread over the tile rows;
+// 5-7 one, two or four (three) rows spread over the tile columns.
+int strip_kernel_mode(const GemmArgs &p)
+{
+    if (p.rstrip > 0) return p.rstrip == 1 ? 5 : p.rstrip == 2 ? 6 : 7;
+    if (p.strip_cols > 0)
+        return p.strip_rows == 0 ? 1 : p.strip_cols == 1 ? 2 : p.strip_cols == 2 ? 3 : 4;
+    return 0;
+}
+
+template <int BM, int BN, int BK, int WGM, int WGN, int KACC, int KG, bool DL, int MB, int NSTG,
+          int SMODE>
+constexpr MfmaKernel strip_kernel()
+{
+    using Tile = MfmaTile<BM, BN, BK, WGM, WGN, KACC, KG, MB, NSTG>;
+    if constexpr (DL && Tile::STRIP_OK && strip_mode_cols(SMODE) <= Tile::STRIP_COLS_MAX)
+        return &k_sgemm_mfma<BM, BN, BK, WGM, WGN, KACC, KG, DL, false, MB, NSTG, SMODE>;
+    else
+        return nullptr;
+}
 
 // PLANNED variants also get a stream-K form and its fixup kernel; the others are never
 // planned and are instantiated in their plain form only.
@@ -97,6 +122,13 @@ constexpr VariantEntry entry(const char *name, int wg_per_cu, double rate, doubl
     e.v.sk_price = sk_price;
     e.v.latency = latency;
     e.stages = NSTG;
+    e.kern_strip[1] = strip_kernel<BM, BN, BK, WGM, WGN, KACC, KG, DL, MB, NSTG, 1>();
+    e.kern_strip[2] = strip_kernel<BM, BN, BK, WGM, WGN, KACC, KG, DL, MB, NSTG, 2>();
+    e.kern_strip[3] = strip_kernel<BM, BN, BK, WGM, WGN, KACC, KG, DL, MB, NSTG, 3>();
+    e.kern_strip[4] = strip_kernel<BM, BN, BK, WGM, WGN, KACC, KG, DL, MB, NSTG, 4>();
+    e.kern_strip[5] = strip_kernel<BM, BN, BK, WGM, WGN, KACC, KG, DL, MB, NSTG, 5>();
+    e.kern_strip[6] = strip_kernel<BM, BN, BK, WGM, WGN, KACC, KG, DL, MB, NSTG, 6>();
+    e.kern_strip[7] = strip_kernel<BM, BN, BK, WGM, WGN, KACC, KG, DL, MB, NSTG, 7>();
     return e;
 }
 
@@ -257,15 +289,17 @@ GemmArgs plain_args(const VariantEntry &e, const Operands &o, const float *A, co
     p.b_bytes = span_elems(o.K, o.N, o.ldb) * 4;
     p.c_bytes = span_elems(o.M, o.N, o.ldc) * 4;
     p.M = o.M; p.N = o.N; p.K = o.K; p.lda = o.lda; p.ldb = o.ldb; p.ldc = o.ldc;
-    const int r = cus > 0 ? strip_cols(e.v, o, cus) : 0;
-    p.tiles_m = (o.M + e.v.BM - 1) / e.v.BM;
+    const int rr = cus > 0 ? rstrip_rows(e.v, o, cus) : 0;
+    const int r = cus > 0 && rr == 0 ? strip_cols(e.v, o, cus) : 0;
+    p.tiles_m = rr > 0 ? o.M / e.v.BM : (o.M + e.v.BM - 1) / e.v.BM;
     p.tiles_n = (o.N - r + e.v.BN - 1) / e.v.BN;
     p.splits = 1;
     p.k_chunk = o.K;
     p.c_split_stride = 0;
     p.strip_n0 = o.N - r;
     p.strip_cols = r;
-    p.strip_rows = r > 0 ? strip_form_rows(e.v, o, cus) : 0;
+    p.strip_rows = rr > 0 ? rstrip_share_cols(e.v, o) : r > 0 ? strip_form_rows(e.v, o, cus) : 0;
+    p.rstrip = rr;
     return p;
 }
 
@@ -380,7 +414,10 @@ int run_variant(int vi, const Operands &o, const float *A, const float *B, float
     const GemmArgs p = plain_args(e, o, A, B, C, cus);
     const int64_t grid = int64_t(p.tiles_m) * p.tiles_n;
     if (grid > INT32_MAX) return SGEMM_ETOO_LARGE;
-    return launch(e.kern, dim3(unsigned(grid)), dim3(e.threads), stream, p);
+    const int mode = strip_kernel_mode(p);
+    const MfmaKernel kern = mode ? e.kern_strip[mode] : e.kern;
+    if (!kern) return SGEMM_ELAUNCH;   // the plan gave a strip form the tile lacks
+    return launch(kern, dim3(unsigned(grid)), dim3(e.threads), stream, p);
 }
 
 // Split-K geometry: K is cut into `splits` ranges of whole BK panels (the last may be
@@ -718,6 +755,7 @@ extern "C" int sgemm_f32_streamk_describe(int M, int N, int K, int variant, int 
     }
     // a plain plan may leave a thin remainder of N to the last tile column (strip_cols)
     const int strip = sk || kVariants[vi].persistent ? 0 : strip_cols(v, o, cus);
+    const int rstrip = sk || kVariants[vi].persistent ? 0 : rstrip_rows(v, o, cus);
     // walk every stream-K range with the kernels' own functions: each unit must belong to
     // exactly one range, each shared tile's partial slots must be distinct and written by
     // the segment that the fixup reads them for
@@ -768,7 +806,7 @@ extern "C" int sgemm_f32_streamk_describe(int M, int N, int K, int variant, int 
                            "\"partition_ok\": %s, \"strip_cols\": %d, "
                            "\"plain_cost_us\": %.2f, \"streamk_cost_us\": %.2f}",
                            vi, v.name, sk ? "true" : "false", v.BM, v.BN, v.BK, cus, g.G,
-                           (long long)(int64_t((M + v.BM - 1) / v.BM) *
+                           (long long)(int64_t((M - rstrip + v.BM - 1) / v.BM) *
                                        ((N - strip + v.BN - 1) / v.BN)),
                            sk ? g.tiles_dp : 0, sk ? g.tiles_sk : 0, g.panels,
                            (long long)(sk ? g.iters : 0), (long long)shared,
@@ -916,17 +954,20 @@ int describe_plan(int vi, const Operands &o, int cus, char *buf, int buflen)
     const Variant &v = kVariants[vi].v;
     const bool pers = kVariants[vi].persistent;
     const int strip = pers ? 0 : strip_cols(v, o, cus);
+    const int rstrip = pers ? 0 : rstrip_rows(v, o, cus);
+    const int rcols = rstrip ? rstrip_share_cols(v, o) : 0;
     // a whole-tile variant's kernel covers the whole tiles; the edges run as launches of
     // their own, planned for their shapes
     const Operands w = pers ? whole_part(v, o) : o;
     const int edges = pers ? int(w.M < M) + int(w.N < N) : 0;
-    const int64_t tm = (int64_t(w.M) + v.BM - 1) / v.BM,
+    const int64_t tm = (int64_t(w.M) - rstrip + v.BM - 1) / v.BM,
                   tn = (int64_t(w.N) - strip + v.BN - 1) / v.BN;
     // workgroups computing rows of the strip: every tile column holding some of its rows
     // (spread), or the last tile column
     const int srows = strip ? strip_form_rows(v, o, cus) : 0;
     const int64_t strip_tiles =
-        !strip ? 0 : srows ? tm * std::min<int64_t>(tn, (v.BM + srows - 1) / srows) : tm;
+        rstrip ? tn * std::min<int64_t>(tm, (v.BN + rcols - 1) / rcols)
+        : !strip ? 0 : srows ? tm * std::min<int64_t>(tn, (v.BM + srows - 1) / srows) : tm;
     // one workgroup per tile, or for the persistent variant one per CU over its tiles
     const int64_t grid = pers ? std::min<int64_t>(tm * tn, cus) : tm * tn;
     // operand bytes the tiles request: every A row panel once per tile column and every
@@ -937,12 +978,13 @@ int describe_plan(int vi, const Operands &o, int cus, char *buf, int buflen)
                            "\"BK\": %d, \"waves\": [%d, %d], \"threads\": %d, \"grid\": %lld, "
                            "\"tiles\": [%lld, %lld], \"cus\": %d, \"wg_per_cu\": %d, "
                            "\"direct_loads\": %s, \"tile_request_bytes\": %lld, "
-                           "\"strip_cols\": %d, \"strip_rows\": %d, \"strip_tiles\": %lld, "
+                           "\"strip_cols\": %d, \"strip_rows\": %d, \"row_strip\": %d, "
+                           "\"row_strip_cols\": %d, \"strip_tiles\": %lld, "
                            "\"edge_launches\": %d}",
                            vi, v.name, v.BM, v.BN, v.BK, v.wgm, v.wgn, kVariants[vi].threads,
                            (long long)grid, (long long)tm, (long long)tn, cus, v.wg_per_cu,
                            v.direct ? "true" : "false", (long long)tile_bytes, strip,
-                           srows, (long long)strip_tiles, edges);
+                           srows, rstrip, rcols, (long long)strip_tiles, edges);
     if (n < 0 || n >= buflen) return SGEMM_EINVAL_ARG;
     return vi;
 }

@@ -58,8 +58,9 @@ typedef enum {
  * Tiling Visualizer", "Why 2D Register Tiling Dominates", carried onto the FP32 MFMA
  * instructions), with tiles zero-filled past the edges of ragged shapes. The tile shape
  * is chosen per (M, N, K) and compute-unit count; when N leaves one to four columns past
- * the last whole tile column, the tiles may also compute them, on the vector ALUs beside
- * their MFMAs, instead of a nearly empty column of tiles. Any 4-byte aligned
+ * the last whole tile column (or M as many rows past the last tile row), the tiles may also
+ * compute them, on the vector ALUs beside their MFMAs, instead of a nearly empty column (or
+ * row) of tiles. Any 4-byte aligned
  * pointers and any leading dimensions work. Leading dimensions so large that 256 rows of A or C (or 32
  * rows of B) exceed 2^31 bytes return SGEMM_ETOO_LARGE.
  */
@@ -291,7 +292,9 @@ const char *sgemm_f32_status_string(int status);
  * arguments into buf (at most buflen bytes including the NUL): variant, tile shape,
  * waves, grid, workgroups resident per CU, whether panels load straight into LDS, the
  * operand bytes the tiles request, and the column strip: "strip_cols" (the columns past
- * the last whole tile column that the tiles also compute, 0 to 4), "strip_rows" (the
+ * the last whole tile column that the tiles also compute, 0 to 4), "row_strip" and
+ * "row_strip_cols" (the rows past the last whole tile row that the tiles of each tile
+ * column compute instead, 0 to 4, and the columns each tile takes of them), "strip_rows" (the
  * strip rows each tile of a row computes when they are spread over the row's tiles; 0
  * when the last tile column computes them all), "strip_tiles" (how many tiles compute
  * some) and "edge_launches" (0-2: the right and bottom edges a whole-tile variant leaves to

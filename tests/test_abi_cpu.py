@@ -430,6 +430,35 @@ def test_variant_describe_wide_strips():
         assert d["tiles"][1] == N // d["BN"], d
 
 
+def test_variant_describe_row_strips():
+    """One to four rows of M past the last whole tile row: every strip-capable variant takes
+    up to its strip_cols_max of them as a row strip (each tile row computing a share of its
+    tile column's columns) where that share's threads fit a K-group and the strip saves a
+    round of tiles; never together with a column strip. The plan gives 1025..1028 x 1024 x
+    1024 a row strip and keeps 1029 off it."""
+    cus = 256
+    for v in range(len(g.variant_names())):
+        info = g.sgemm_f32_variant_info(v)
+        if not info["strip"]:
+            continue
+        bm, bn, bk = info["BM"], info["BN"], info["BK"]
+        nt = 64 * info["waves"][0] * info["waves"][1]
+        cols = -(-bn // 16)
+        for rr in range(1, 6):
+            M, N, K = 16 * bm + rr, 16 * bn - 3, 33
+            d = g.sgemm_f32_variant_describe(v, M, N, K, K + 3, N + 1, N + 2, num_cus=cus)
+            if rr <= info["strip_cols_max"] and cols * bk // 4 <= nt:
+                assert d["row_strip"] == rr and d["row_strip_cols"] == cols, (info["name"], d)
+                assert d["tiles"] == [16, 16] and d["strip_cols"] == 0, d
+            else:
+                assert d["row_strip"] == 0 and d["tiles"][0] == 17, (info["name"], rr, d)
+    for M in (1025, 1026, 1027, 1028):
+        d = g.sgemm_f32_plan_describe(M, 1024, 1024, num_cus=cus)
+        assert d["row_strip"] == M - 1024 and d["tiles"][0] == 16 and d["strip_cols"] == 0, d
+    d = g.sgemm_f32_plan_describe(1029, 1024, 1024, num_cus=cus)
+    assert d["row_strip"] == 0, d
+
+
 def test_variant_describe_strip_forms():
     """A forced variant's plan, as sgemm_f32_variant runs it: the column strip spread over
     the tiles of each row where one K-group's threads cover a tile's share of the rows,

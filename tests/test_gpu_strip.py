@@ -150,6 +150,61 @@ def test_strip_forced_wide(gpu):
                 _check(A, B, c.result(), "int", (name, M, N, K, sc))
 
 
+def test_row_strip_forced(gpu):
+    """Every strip-capable variant forced on shapes whose M leaves one to strip_cols_max
+    rows past the last whole tile row: the tiles of each tile column compute those rows
+    (each tile row a share of the columns), as variant_describe reports; exact on
+    integers with padded leading dimensions, guard bands and a ragged, masked last tile
+    column."""
+    cus = gpu.cuda.get_device_properties(0).multi_processor_count
+    for v in strip_variants():
+        info = g.sgemm_f32_variant_info(v)
+        name, bm, bn = info["name"], info["BM"], info["BN"]
+        for rr in range(1, info["strip_cols_max"] + 1):
+            for (M, N, K) in [(16 * bm + rr, (cus // 16) * bn - 3, 33),
+                              (17 * bm + rr, (cus // 17) * bn, 72 + rr)]:
+                lda, ldb, ldc = K + 3, N + 1, N + 2
+                d = g.sgemm_f32_variant_describe(v, M, N, K, lda, ldb, ldc)
+                assert d["row_strip"] == rr and d["strip_cols"] == 0, (name, M, N, K, d)
+                assert d["tiles"][0] == M // bm, d
+                rng = np.random.default_rng(7 * M + N + 3 * K)
+                A = wl.draw(rng, (M, K), "int")
+                B = wl.draw(rng, (K, N), "int")
+                _, dA, _ = device_matrix(A, lda)
+                _, dB, _ = device_matrix(B, ldb)
+                c = GuardedC(M, N, ldc)
+                print(f"[strip] {name} {M}x{N}x{K} {rr} strip rows, "
+                      f"{d['row_strip_cols']} columns per tile", flush=True)
+                run_kernel(f"v{v}", M, N, K, dA, lda, dB, ldb, c)
+                gpu.cuda.synchronize()
+                _check(A, B, c.result(), "int", (name, M, N, K, rr))
+
+
+@pytest.mark.parametrize("M,N,K", [(1025, 1024, 1024), (1028, 1024, 1027), (2049, 2048, 2048),
+                                   (513, 512, 4096), (1026, 11934, 230)])
+def test_plan_row_strip(gpu, M, N, K):
+    """The automatic plan where M leaves one to four rows past the tile rows: a row strip,
+    matching the oracle (floats, normalised tolerance; sampled rows, the strip's included,
+    at the larger sizes)."""
+    plan = g.sgemm_f32_plan_describe(M, N, K)
+    print(f"[strip] plan {M}x{N}x{K} {plan}", flush=True)
+    assert plan["row_strip"] == M % plan["BM"] and plan["row_strip_cols"] > 0, plan
+    rng = np.random.default_rng(M * 13 + N * 5 + K)
+    A = wl.draw(rng, (M, K), "uniform")
+    B = wl.draw(rng, (K, N), "uniform")
+    _, dA, lda = device_matrix(A)
+    _, dB, ldb = device_matrix(B)
+    c = GuardedC(M, N, N + 1)
+    run_kernel("auto", M, N, K, dA, lda, dB, ldb, c)
+    gpu.cuda.synchronize()
+    C = c.result()
+    if M * N * K <= 2 ** 31:
+        rep = oracle.check(A, B, C)
+    else:
+        rep = oracle.check(A, B, C, rows=np.unique(np.r_[0:4, 1000:1004, M - 12:M]))
+    assert rep["n_nonfinite"] == 0 and rep["max_err"] <= TOL, rep
+
+
 @pytest.mark.parametrize("M,N,K", [(1024, 1026, 1024), (1024, 1027, 1024), (1023, 1028, 1027),
                                    (2048, 2050, 2048), (512, 514, 4096)])
 def test_plan_wide_strip(gpu, M, N, K):
